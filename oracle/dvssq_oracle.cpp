@@ -1,0 +1,673 @@
+// DV-SSQ oracle: a plain, slow, fp64 CPU implementation of the quantized
+// linear layer described on the "Spark-X2.5-4B-Hadamard-GSQ" and
+// "MiniCPM5-2B-Hadamard-GSQ" model cards.
+//
+// TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+// loads this file; only the tests, the smoke check and the benchmark's
+// CPU-baseline leg do.  It shares no code, header or constant table with the
+// GPU path.
+//
+// What it computes, in the cards' order:
+//   1. salience ranking of the rows of W by L2 norm; the top 1/8 form the
+//      INT8 tier            (Spark card, Architectural Pillars 1, Tier A)
+//   2. rotation W_rot = W . H_K, H_K = diag(H_b, ..., H_b), H_b the normalized
+//      Sylvester Walsh-Hadamard matrix
+//                            (Spark card, Tier B equation; MiniCPM card,
+//                             Mathematical Foundations 1)
+//   3. INT8 rows: per-row absmax/127 scale, clip(round(w/s), -128, 127)
+//                            (Spark card, Tier A equation)
+//   4. INT4 rows: groups of G = 64 along the input dimension,
+//      s_g = max|w|/7.0, clip(round(w/s_g), -8, 7)
+//                            (MiniCPM card, Mathematical Foundations 2)
+//   5. residual R = W_rot - W_hat and its rank-r truncated SVD, split as
+//      A = U_r sqrt(S_r), B = sqrt(S_r) V_r^T, stored in bf16
+//                            (MiniCPM card, Mathematical Foundations 2;
+//                             Spark card, Tier C)
+//   6. forward Y = (X H) W_hat^T + ((X H) B^T) A^T
+//                            (MiniCPM card, Mathematical Foundations 2,
+//                             runtime equation)
+//
+// Readings where the cards are silent (all listed in the design notes):
+// rows (output features) carry the INT8 tier; INT8 rows are rotated too;
+// scales are stored as fp32 (INT8) and bf16 (INT4) and the codes are computed
+// against the stored scale; rounding is to nearest, ties to even; an all-zero
+// group or row gets scale 0 and codes 0; the residual covers all rows; the
+// fused gate+up layer quantizes each projection (segment) separately.
+//
+// Packed blob (every sub-buffer starts on a 256-byte boundary), rows ordered
+// INT4 tier first, then INT8 tier; inside a tier segment 0's rows then
+// segment 1's, each in ascending original index:
+//   idx  int32 [N]           packed row -> original output column
+//   q4   uint8 [N4][K/2]     byte j: code k=2j in the low nibble, 2j+1 high;
+//                            nibble = q + 8
+//   s4   bf16  [N4][K/64]
+//   q8   int8  [N8][K]
+//   s8   fp32  [N8]
+//   U    bf16  [N][r]        A's row for each packed row
+//   V    bf16  [n_seg*r][K]  B of segment s in rows s*r .. s*r+r-1
+
+#include <algorithm>
+#include <cfenv>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <numeric>
+#include <thread>
+#include <vector>
+
+namespace {
+
+constexpr int kGroup = 64;        // INT4 group size G
+constexpr int kParts = 16;        // fixed work partition (results independent of thread count)
+
+int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// ---------------------------------------------------------------- number types
+
+// fp64 -> bf16, nearest with ties to even, straight from fp64.
+uint16_t bf16_from_double(double v) {
+  if (std::isnan(v)) return 0x7FC0;
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  const double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  int e = 0;
+  std::frexp(a, &e);                      // a = f * 2^e, f in [0.5, 1)
+  const int q = std::max(e - 8, -133);    // quantum: 8 significant bits, or 2^-133
+  const double m = std::nearbyint(std::ldexp(a, -q));
+  const float f = static_cast<float>(std::ldexp(m, q));   // exact, or inf on overflow
+  uint32_t bits;
+  std::memcpy(&bits, &f, 4);
+  return static_cast<uint16_t>(sign | (bits >> 16));
+}
+
+double double_from_bf16(uint16_t h) {
+  const uint32_t bits = static_cast<uint32_t>(h) << 16;
+  float f;
+  std::memcpy(&f, &bits, 4);
+  return f;
+}
+
+// ---------------------------------------------------------------- Hadamard
+
+// In-place unnormalized Walsh-Hadamard butterflies on n = 2^k values, then the
+// 1/sqrt(n) normalization.  Result: x <- H_n x with H_n[i][j] =
+// (-1)^popcount(i & j) / sqrt(n) (Sylvester construction, natural order).
+void fwht_block(double *x, int n) {
+  for (int len = 1; len < n; len <<= 1)
+    for (int i = 0; i < n; i += 2 * len)
+      for (int j = i; j < i + len; ++j) {
+        const double a = x[j], b = x[j + len];
+        x[j] = a + b;
+        x[j + len] = a - b;
+      }
+  const double sc = 1.0 / std::sqrt(static_cast<double>(n));
+  for (int i = 0; i < n; ++i) x[i] *= sc;
+}
+
+void fwht_rows(double *X, int64_t rows, int64_t K, int b) {
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t c = 0; c < K; c += b) fwht_block(X + i * K + c, b);
+}
+
+// ---------------------------------------------------------------- quantizers
+
+// Tier A: one fp32 scale per row, s = max|w| / 127 (the card leaves s_salient
+// open; a per-row absmax scale is the reading taken).
+void quant_int8_row(const double *w, int64_t K, int8_t *q, float *s_out) {
+  double amax = 0.0;
+  for (int64_t k = 0; k < K; ++k) amax = std::max(amax, std::fabs(w[k]));
+  const float s = static_cast<float>(amax / 127.0);
+  *s_out = s;
+  for (int64_t k = 0; k < K; ++k) {
+    if (s == 0.0f) { q[k] = 0; continue; }
+    double v = std::nearbyint(w[k] / static_cast<double>(s));
+    v = std::min(127.0, std::max(-128.0, v));
+    q[k] = static_cast<int8_t>(v);
+  }
+}
+
+// Tier B: groups of 64 consecutive inputs, s_g = max|w| / 7.0 stored as bf16,
+// q = clip(round(w / s_g), -8, 7).
+void quant_int4_row(const double *w, int64_t K, int8_t *q, uint16_t *s_out) {
+  for (int64_t g = 0; g < K / kGroup; ++g) {
+    const double *wg = w + g * kGroup;
+    double amax = 0.0;
+    for (int j = 0; j < kGroup; ++j) amax = std::max(amax, std::fabs(wg[j]));
+    const uint16_t sb = bf16_from_double(amax / 7.0);
+    s_out[g] = sb;
+    const double s = double_from_bf16(sb);
+    for (int j = 0; j < kGroup; ++j) {
+      if (s == 0.0) { q[g * kGroup + j] = 0; continue; }
+      double v = std::nearbyint(wg[j] / s);
+      v = std::min(7.0, std::max(-8.0, v));
+      q[g * kGroup + j] = static_cast<int8_t>(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- small dense helpers
+
+template <class F>
+void parallel_parts(int64_t n, int nthreads, F fn) {
+  // Splits [0, n) into kParts fixed ranges; threads only choose who runs which.
+  std::vector<std::pair<int64_t, int64_t>> ranges;
+  for (int p = 0; p < kParts; ++p) ranges.emplace_back(n * p / kParts, n * (p + 1) / kParts);
+  nthreads = std::max(1, std::min(nthreads, kParts));
+  std::vector<std::thread> th;
+  for (int t = 0; t < nthreads; ++t)
+    th.emplace_back([&, t] {
+      for (int p = t; p < kParts; p += nthreads) fn(p, ranges[p].first, ranges[p].second);
+    });
+  for (auto &x : th) x.join();
+}
+
+int default_threads() {
+  unsigned h = std::thread::hardware_concurrency();
+  return static_cast<int>(std::max(1u, std::min(h, 16u)));
+}
+
+// C (n x l) = A (n x k, row-major) * B (k x l, row-major)
+void matmul(const double *A, const double *B, double *C, int64_t n, int64_t k, int64_t l) {
+  parallel_parts(n, default_threads(), [&](int, int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i) {
+      double *c = C + i * l;
+      for (int64_t j = 0; j < l; ++j) c[j] = 0.0;
+      for (int64_t kk = 0; kk < k; ++kk) {
+        const double a = A[i * k + kk];
+        const double *b = B + kk * l;
+        for (int64_t j = 0; j < l; ++j) c[j] += a * b[j];
+      }
+    }
+  });
+}
+
+// C (k x l) = A^T * B with A (n x k), B (n x l), both row-major.
+void matmul_tn(const double *A, const double *B, double *C, int64_t n, int64_t k, int64_t l) {
+  std::vector<std::vector<double>> part(kParts, std::vector<double>(k * l, 0.0));
+  parallel_parts(n, default_threads(), [&](int p, int64_t lo, int64_t hi) {
+    double *acc = part[p].data();
+    for (int64_t i = lo; i < hi; ++i)
+      for (int64_t kk = 0; kk < k; ++kk) {
+        const double a = A[i * k + kk];
+        if (a == 0.0) continue;
+        const double *b = B + i * l;
+        double *c = acc + kk * l;
+        for (int64_t j = 0; j < l; ++j) c[j] += a * b[j];
+      }
+  });
+  for (int64_t e = 0; e < k * l; ++e) {
+    double s = 0.0;
+    for (int p = 0; p < kParts; ++p) s += part[p][e];
+    C[e] = s;
+  }
+}
+
+// Orthonormalize the l columns of Y (n x l, row-major) by modified Gram-Schmidt,
+// applied twice.  Columns that vanish (rank deficiency) become zero.
+void orth_columns(double *Y, int64_t n, int64_t l) {
+  std::vector<double> norm0(l);
+  for (int64_t j = 0; j < l; ++j) {
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += Y[i * l + j] * Y[i * l + j];
+    norm0[j] = std::sqrt(s);
+  }
+  for (int pass = 0; pass < 2; ++pass)
+    for (int64_t j = 0; j < l; ++j) {
+      for (int64_t p = 0; p < j; ++p) {
+        double d = 0.0;
+        for (int64_t i = 0; i < n; ++i) d += Y[i * l + p] * Y[i * l + j];
+        for (int64_t i = 0; i < n; ++i) Y[i * l + j] -= d * Y[i * l + p];
+      }
+      double s = 0.0;
+      for (int64_t i = 0; i < n; ++i) s += Y[i * l + j] * Y[i * l + j];
+      s = std::sqrt(s);
+      const bool dead = !(s > 1e-13 * norm0[j]) || s == 0.0;
+      for (int64_t i = 0; i < n; ++i) Y[i * l + j] = dead ? 0.0 : Y[i * l + j] / s;
+    }
+}
+
+// One-sided (Hestenes) Jacobi SVD of A (rows x cols, row-major).
+// Output: U (rows x cols), S (cols), V (cols x cols), all sorted by S
+// descending; for each j the largest-magnitude entry of V[:, j] is positive.
+// Returns the number of sweeps taken.
+int svd_jacobi(const double *A, int64_t rows, int64_t cols, double *U, double *S, double *V,
+               double tol, int max_sweeps) {
+  // Column-major working copies.
+  std::vector<double> G(rows * cols), J(cols * cols, 0.0);
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t j = 0; j < cols; ++j) G[j * rows + i] = A[i * cols + j];
+  for (int64_t j = 0; j < cols; ++j) J[j * cols + j] = 1.0;
+  int sweep = 0;
+  for (; sweep < max_sweeps; ++sweep) {
+    bool rotated = false;
+    for (int64_t p = 0; p < cols - 1; ++p)
+      for (int64_t q = p + 1; q < cols; ++q) {
+        double *gp = &G[p * rows], *gq = &G[q * rows];
+        double alpha = 0.0, beta = 0.0, gamma = 0.0;
+        for (int64_t i = 0; i < rows; ++i) {
+          alpha += gp[i] * gp[i];
+          beta += gq[i] * gq[i];
+          gamma += gp[i] * gq[i];
+        }
+        if (alpha == 0.0 || beta == 0.0) continue;
+        if (std::fabs(gamma) <= tol * std::sqrt(alpha * beta)) continue;
+        rotated = true;
+        const double zeta = (beta - alpha) / (2.0 * gamma);
+        const double t = (zeta >= 0 ? 1.0 : -1.0) / (std::fabs(zeta) + std::sqrt(1.0 + zeta * zeta));
+        const double c = 1.0 / std::sqrt(1.0 + t * t), s = c * t;
+        for (int64_t i = 0; i < rows; ++i) {
+          const double a = gp[i], b = gq[i];
+          gp[i] = c * a - s * b;
+          gq[i] = s * a + c * b;
+        }
+        double *jp = &J[p * cols], *jq = &J[q * cols];
+        for (int64_t i = 0; i < cols; ++i) {
+          const double a = jp[i], b = jq[i];
+          jp[i] = c * a - s * b;
+          jq[i] = s * a + c * b;
+        }
+      }
+    if (!rotated) { ++sweep; break; }
+  }
+  std::vector<double> sig(cols);
+  for (int64_t j = 0; j < cols; ++j) {
+    double s = 0.0;
+    for (int64_t i = 0; i < rows; ++i) s += G[j * rows + i] * G[j * rows + i];
+    sig[j] = std::sqrt(s);
+  }
+  std::vector<int64_t> ord(cols);
+  std::iota(ord.begin(), ord.end(), 0);
+  std::stable_sort(ord.begin(), ord.end(), [&](int64_t a, int64_t b) { return sig[a] > sig[b]; });
+  for (int64_t jj = 0; jj < cols; ++jj) {
+    const int64_t j = ord[jj];
+    // sign: largest-magnitude entry of the right singular vector positive
+    int64_t arg = 0;
+    for (int64_t i = 1; i < cols; ++i)
+      if (std::fabs(J[j * cols + i]) > std::fabs(J[j * cols + arg])) arg = i;
+    const double sg = J[j * cols + arg] < 0 ? -1.0 : 1.0;
+    S[jj] = sig[j];
+    for (int64_t i = 0; i < cols; ++i) V[i * cols + jj] = sg * J[j * cols + i];
+    for (int64_t i = 0; i < rows; ++i)
+      U[i * cols + jj] = sig[j] > 0 ? sg * G[j * rows + i] / sig[j] : 0.0;
+  }
+  return sweep;
+}
+
+// Rank-r factors of R (n x k): A (n x r) = U_r sqrt(S_r), B (r x k) = sqrt(S_r) V_r^T.
+// full != 0: exact thin SVD of R by one-sided Jacobi.
+// full == 0: randomized subspace iteration from the sketch Omega (k x l),
+// power_iters rounds of Q = orth(R orth(R^T Q)), then Jacobi on the small
+// projection Q^T R.
+int svd_lowrank(const double *R, int64_t n, int64_t k, int r, const double *omega, int l,
+                int power_iters, int full, double *A, double *B, double *S) {
+  if (full) {
+    std::vector<double> U(n * k), Sv(k), V(k * k);
+    // thin SVD needs rows >= cols; for a wide R factor its transpose
+    if (n >= k) {
+      svd_jacobi(R, n, k, U.data(), Sv.data(), V.data(), 1e-15, 80);
+      for (int j = 0; j < r; ++j) {
+        const double sq = std::sqrt(Sv[j]);
+        S[j] = Sv[j];
+        for (int64_t i = 0; i < n; ++i) A[i * r + j] = U[i * k + j] * sq;
+        for (int64_t i = 0; i < k; ++i) B[j * k + i] = V[i * k + j] * sq;
+      }
+    } else {
+      std::vector<double> Rt(k * n), U2(k * n), S2(n), V2(n * n);
+      for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < k; ++j) Rt[j * n + i] = R[i * k + j];
+      svd_jacobi(Rt.data(), k, n, U2.data(), S2.data(), V2.data(), 1e-15, 80);
+      // R = V2 S2 U2^T: left vectors V2, right vectors U2.
+      for (int j = 0; j < r; ++j) {
+        int64_t arg = 0;  // re-apply the sign rule to the right vectors of R
+        for (int64_t i = 1; i < k; ++i)
+          if (std::fabs(U2[i * n + j]) > std::fabs(U2[arg * n + j])) arg = i;
+        const double sg = U2[arg * n + j] < 0 ? -1.0 : 1.0;
+        const double sq = std::sqrt(S2[j]);
+        S[j] = S2[j];
+        for (int64_t i = 0; i < n; ++i) A[i * r + j] = sg * V2[i * n + j] * sq;
+        for (int64_t i = 0; i < k; ++i) B[j * k + i] = sg * U2[i * n + j] * sq;
+      }
+    }
+    return 0;
+  }
+  if (l < r) return -1;
+  std::vector<double> Q(n * l), Z(k * l);
+  matmul(R, omega, Q.data(), n, k, l);
+  orth_columns(Q.data(), n, l);
+  for (int it = 0; it < power_iters; ++it) {
+    matmul_tn(R, Q.data(), Z.data(), n, k, l);  // Z = R^T Q
+    orth_columns(Z.data(), k, l);
+    matmul(R, Z.data(), Q.data(), n, k, l);     // Q = R Z
+    orth_columns(Q.data(), n, l);
+  }
+  // Bt = R^T Q  (k x l), i.e. the transpose of the projection Q^T R.
+  std::vector<double> Bt(k * l);
+  matmul_tn(R, Q.data(), Bt.data(), n, k, l);
+  std::vector<double> Ub(k * l), Sb(l), Vb(l * l);
+  svd_jacobi(Bt.data(), k, l, Ub.data(), Sb.data(), Vb.data(), 1e-15, 80);
+  // Q^T R = Vb Sb Ub^T, so R ~= (Q Vb) Sb Ub^T: right vectors Ub (sign rule
+  // applies to these), left vectors Q Vb.
+  for (int j = 0; j < r; ++j) {
+    int64_t arg = 0;
+    for (int64_t i = 1; i < k; ++i)
+      if (std::fabs(Ub[i * l + j]) > std::fabs(Ub[arg * l + j])) arg = i;
+    const double sg = Ub[arg * l + j] < 0 ? -1.0 : 1.0;
+    const double sq = std::sqrt(Sb[j]);
+    S[j] = Sb[j];
+    for (int64_t i = 0; i < k; ++i) B[j * k + i] = sg * Ub[i * l + j] * sq;
+    for (int64_t i = 0; i < n; ++i) {
+      double u = 0.0;
+      for (int p = 0; p < l; ++p) u += Q[i * l + p] * Vb[p * l + j];
+      A[i * r + j] = sg * u * sq;
+    }
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------- layout
+
+struct Layout {
+  int64_t N4, N8, off_idx, off_q4, off_s4, off_q8, off_s8, off_U, off_V, blob_bytes, algo_bytes;
+};
+
+bool make_layout(int N, int K, int r, int n_seg, Layout *L) {
+  if (N <= 0 || K <= 0 || r < 1 || r > 64 || n_seg < 1) return false;
+  if (K % kGroup != 0 || N % (8 * n_seg) != 0) return false;
+  const int64_t n8 = static_cast<int64_t>(N / n_seg / 8) * n_seg;
+  const int64_t n4 = N - n8;
+  const int64_t sz[7] = {4LL * N, n4 * (K / 2), n4 * (K / kGroup) * 2, n8 * K, n8 * 4,
+                         2LL * N * r, 2LL * n_seg * r * K};
+  int64_t off[7], cur = 0, algo = 0;
+  for (int i = 0; i < 7; ++i) {
+    off[i] = cur;
+    cur = align256(cur + sz[i]);
+    algo += sz[i];
+  }
+  *L = Layout{n4, n8, off[0], off[1], off[2], off[3], off[4], off[5], off[6], cur, algo};
+  return true;
+}
+
+struct Packed {
+  Layout L;
+  int N, K, r, n_seg;
+  const uint8_t *blob;
+  const int32_t *idx() const { return reinterpret_cast<const int32_t *>(blob + L.off_idx); }
+  const uint8_t *q4() const { return blob + L.off_q4; }
+  const uint16_t *s4() const { return reinterpret_cast<const uint16_t *>(blob + L.off_s4); }
+  const int8_t *q8() const { return reinterpret_cast<const int8_t *>(blob + L.off_q8); }
+  const float *s8() const { return reinterpret_cast<const float *>(blob + L.off_s8); }
+  const uint16_t *U() const { return reinterpret_cast<const uint16_t *>(blob + L.off_U); }
+  const uint16_t *V() const { return reinterpret_cast<const uint16_t *>(blob + L.off_V); }
+
+  // Dequantized rotated row p (packed order): q * s.
+  void row(int64_t p, double *w) const {
+    if (p < L.N4) {
+      const uint8_t *c = q4() + p * (K / 2);
+      const uint16_t *s = s4() + p * (K / kGroup);
+      for (int64_t k = 0; k < K; ++k) {
+        const int nib = (k & 1) ? (c[k >> 1] >> 4) : (c[k >> 1] & 0xF);
+        w[k] = static_cast<double>(nib - 8) * double_from_bf16(s[k / kGroup]);
+      }
+    } else {
+      const int64_t j = p - L.N4;
+      const int8_t *c = q8() + j * K;
+      const double s = s8()[j];
+      for (int64_t k = 0; k < K; ++k) w[k] = static_cast<double>(c[k]) * s;
+    }
+  }
+};
+
+// The layer's forward on the packed values, for the output columns listed in
+// `cols` (all of them when cols == nullptr), in fp64:
+//   x_rot = x H_K;  t = x_rot V^T;  y[:, idx[p]] = x_rot W_hat[p]^T + t[:, seg(p) r ..] U[p]^T
+void forward(const Packed &P, int b, const uint16_t *x, int M, const int32_t *cols, int ncols,
+             double *y, int nthreads) {
+  const int64_t K = P.K, N = P.N, r = P.r, nsr = static_cast<int64_t>(P.n_seg) * r;
+  const int64_t Ns = N / P.n_seg;
+  std::vector<double> xr(static_cast<size_t>(M) * K);
+  for (int64_t i = 0; i < static_cast<int64_t>(M) * K; ++i) xr[i] = double_from_bf16(x[i]);
+  fwht_rows(xr.data(), M, K, b);
+  std::vector<double> t(static_cast<size_t>(M) * nsr, 0.0);
+  for (int m = 0; m < M; ++m)
+    for (int64_t i = 0; i < nsr; ++i) {
+      double s = 0.0;
+      for (int64_t k = 0; k < K; ++k) s += xr[m * K + k] * double_from_bf16(P.V()[i * K + k]);
+      t[m * nsr + i] = s;
+    }
+  // which packed rows to evaluate, and where each result goes
+  std::vector<int64_t> prow, ocol;
+  if (cols == nullptr) {
+    for (int64_t p = 0; p < N; ++p) { prow.push_back(p); ocol.push_back(P.idx()[p]); }
+  } else {
+    std::vector<int64_t> inv(N, -1);
+    for (int64_t p = 0; p < N; ++p) inv[P.idx()[p]] = p;
+    for (int c = 0; c < ncols; ++c) { prow.push_back(inv[cols[c]]); ocol.push_back(c); }
+  }
+  const int64_t ystride = cols ? ncols : N;
+  parallel_parts(static_cast<int64_t>(prow.size()), nthreads, [&](int, int64_t lo, int64_t hi) {
+    std::vector<double> w(K);
+    for (int64_t e = lo; e < hi; ++e) {
+      const int64_t p = prow[e];
+      P.row(p, w.data());
+      const int64_t seg = P.idx()[p] / Ns;
+      for (int m = 0; m < M; ++m) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) s += xr[m * K + k] * w[k];
+        for (int64_t i = 0; i < r; ++i)
+          s += t[m * nsr + seg * r + i] * double_from_bf16(P.U()[p * r + i]);
+        y[m * ystride + ocol[e]] = s;
+      }
+    }
+  });
+}
+
+}  // namespace
+
+// ============================================================== C ABI (ctypes)
+
+extern "C" {
+
+uint16_t orc_bf16_from_double(double v) { return bf16_from_double(v); }
+double orc_bf16_to_double(uint16_t h) { return double_from_bf16(h); }
+
+// out[11] = N4, N8, off_idx, off_q4, off_s4, off_q8, off_s8, off_U, off_V, blob_bytes, algo_bytes
+int orc_layout(int N, int K, int r, int n_seg, int64_t *out) {
+  Layout L;
+  if (!out || !make_layout(N, K, r, n_seg, &L)) return -1;
+  const int64_t v[11] = {L.N4, L.N8, L.off_idx, L.off_q4, L.off_s4, L.off_q8, L.off_s8,
+                         L.off_U, L.off_V, L.blob_bytes, L.algo_bytes};
+  std::memcpy(out, v, sizeof v);
+  return 0;
+}
+
+int orc_fwht_rows(double *X, int64_t rows, int64_t K, int b) {
+  if (!X || !pow2(b) || K % b != 0) return -1;
+  fwht_rows(X, rows, K, b);
+  return 0;
+}
+
+// Salience S_n = sum_k W[n,k]^2 (ascending k) and the ranking: order[0..N) is
+// the row indices sorted by S descending, ties to the lower index.
+int orc_rank_rows(const double *W, int64_t N, int64_t K, double *S, int32_t *order) {
+  if (!W || !S || !order) return -1;
+  for (int64_t n = 0; n < N; ++n) {
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k) s += W[n * K + k] * W[n * K + k];
+    S[n] = s;
+  }
+  std::vector<int32_t> o(N);
+  std::iota(o.begin(), o.end(), 0);
+  std::stable_sort(o.begin(), o.end(), [&](int32_t a, int32_t b) { return S[a] > S[b]; });
+  std::copy(o.begin(), o.end(), order);
+  return 0;
+}
+
+int orc_quant_int8_row(const double *w, int64_t K, int8_t *q, float *s) {
+  if (!w || !q || !s) return -1;
+  quant_int8_row(w, K, q, s);
+  return 0;
+}
+
+int orc_quant_int4_row(const double *w, int64_t K, int8_t *q, uint16_t *s) {
+  if (!w || !q || !s || K % kGroup != 0) return -1;
+  quant_int4_row(w, K, q, s);
+  return 0;
+}
+
+int orc_svd_jacobi(const double *A, int64_t rows, int64_t cols, double *U, double *S, double *V) {
+  if (!A || !U || !S || !V || rows < cols) return -1;
+  return svd_jacobi(A, rows, cols, U, S, V, 1e-15, 80);
+}
+
+int orc_svd_lowrank(const double *R, int64_t n, int64_t k, int r, const double *omega, int l,
+                    int power_iters, int full, double *A, double *B, double *S) {
+  if (!R || !A || !B || !S || r < 1 || r > std::min(n, k)) return -1;
+  if (!full && (!omega || l < r || l > std::min(n, k))) return -1;
+  return svd_lowrank(R, n, k, r, omega, l, power_iters, full, A, B, S);
+}
+
+// Quantize a bf16 weight matrix W [N][K] (segment s = rows s*N/n_seg ..) into
+// a packed blob of orc_layout's blob_bytes.  omega: n_seg consecutive K x l
+// sketches (unused when full_svd).  diag (optional, n_seg x 4): ||R||_F,
+// ||R - A B||_F with fp64 factors, the same with the stored bf16 factors, and
+// sigma_{r+1} estimate (0 if unavailable).
+int orc_quantize(const uint16_t *W, int N, int K, int r, int b, int n_seg, const double *omega,
+                 int l, int power_iters, int full_svd, uint8_t *blob, double *diag) {
+  Layout L;
+  if (!W || !blob || !pow2(b) || K % b != 0 || !make_layout(N, K, r, n_seg, &L)) return -1;
+  const int64_t Ns = N / n_seg, n8s = Ns / 8, n4s = Ns - n8s;
+  if (r > std::min<int64_t>(Ns, K)) return -1;
+  std::memset(blob, 0, L.blob_bytes);
+  int32_t *idx = reinterpret_cast<int32_t *>(blob + L.off_idx);
+  uint8_t *q4 = blob + L.off_q4;
+  uint16_t *s4 = reinterpret_cast<uint16_t *>(blob + L.off_s4);
+  int8_t *q8 = reinterpret_cast<int8_t *>(blob + L.off_q8);
+  float *s8 = reinterpret_cast<float *>(blob + L.off_s8);
+  uint16_t *Ub = reinterpret_cast<uint16_t *>(blob + L.off_U);
+  uint16_t *Vb = reinterpret_cast<uint16_t *>(blob + L.off_V);
+
+  for (int s = 0; s < n_seg; ++s) {
+    std::vector<double> Wd(Ns * K);
+    for (int64_t i = 0; i < Ns * K; ++i) Wd[i] = double_from_bf16(W[s * Ns * K + i]);
+    // 1. salience on the unrotated weights
+    std::vector<double> S(Ns);
+    std::vector<int32_t> order(Ns);
+    orc_rank_rows(Wd.data(), Ns, K, S.data(), order.data());
+    std::vector<char> salient(Ns, 0);
+    for (int64_t i = 0; i < n8s; ++i) salient[order[i]] = 1;
+    // 2. rotate
+    fwht_rows(Wd.data(), Ns, K, b);
+    // packed positions: INT4 rows of segment s then INT8 rows, ascending
+    std::vector<int64_t> pos(Ns);
+    int64_t c4 = s * n4s, c8 = L.N4 + s * n8s;
+    for (int64_t n = 0; n < Ns; ++n) pos[n] = salient[n] ? c8++ : c4++;
+    // 3/4. tiers, and the residual R = W_rot - W_hat
+    std::vector<double> R(Ns * K);
+    std::vector<int8_t> q(K);
+    for (int64_t n = 0; n < Ns; ++n) {
+      const double *w = &Wd[n * K];
+      const int64_t p = pos[n];
+      idx[p] = static_cast<int32_t>(s * Ns + n);
+      if (salient[n]) {
+        const int64_t j = p - L.N4;
+        quant_int8_row(w, K, q8 + j * K, s8 + j);
+        for (int64_t k = 0; k < K; ++k)
+          R[n * K + k] = w[k] - static_cast<double>(q8[j * K + k]) * static_cast<double>(s8[j]);
+      } else {
+        uint16_t *sg = s4 + p * (K / kGroup);
+        quant_int4_row(w, K, q.data(), sg);
+        uint8_t *c = q4 + p * (K / 2);
+        for (int64_t k = 0; k < K; k += 2)
+          c[k / 2] = static_cast<uint8_t>(((q[k] + 8) & 0xF) | (((q[k + 1] + 8) & 0xF) << 4));
+        for (int64_t k = 0; k < K; ++k)
+          R[n * K + k] = w[k] - static_cast<double>(q[k]) * double_from_bf16(sg[k / kGroup]);
+      }
+    }
+    // 5. truncated SVD of the residual
+    std::vector<double> A(Ns * r), B(static_cast<int64_t>(r) * K), sig(r);
+    const double *om = omega ? omega + static_cast<int64_t>(s) * K * l : nullptr;
+    if (svd_lowrank(R.data(), Ns, K, r, om, l, power_iters, full_svd, A.data(), B.data(), sig.data()))
+      return -1;
+    for (int64_t n = 0; n < Ns; ++n)
+      for (int i = 0; i < r; ++i) Ub[pos[n] * r + i] = bf16_from_double(A[n * r + i]);
+    for (int i = 0; i < r; ++i)
+      for (int64_t k = 0; k < K; ++k)
+        Vb[(static_cast<int64_t>(s) * r + i) * K + k] = bf16_from_double(B[i * K + k]);
+    if (diag) {
+      double fr = 0, f64 = 0, fbf = 0;
+      for (int64_t n = 0; n < Ns; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+          double ab = 0, abq = 0;
+          for (int i = 0; i < r; ++i) {
+            ab += A[n * r + i] * B[i * K + k];
+            abq += double_from_bf16(Ub[pos[n] * r + i]) *
+                   double_from_bf16(Vb[(static_cast<int64_t>(s) * r + i) * K + k]);
+          }
+          const double e = R[n * K + k];
+          fr += e * e;
+          f64 += (e - ab) * (e - ab);
+          fbf += (e - abq) * (e - abq);
+        }
+      diag[s * 4 + 0] = std::sqrt(fr);
+      diag[s * 4 + 1] = std::sqrt(f64);
+      diag[s * 4 + 2] = std::sqrt(fbf);
+      diag[s * 4 + 3] = 0.0;
+    }
+  }
+  return 0;
+}
+
+// Decode a blob: idx [N], dequantized rotated rows What [N][K] (packed order),
+// U [N][r], V [n_seg*r][K] as fp64.  Any output pointer may be null.
+int orc_unpack(const uint8_t *blob, int N, int K, int r, int n_seg, int32_t *idx, double *What,
+               double *U, double *V) {
+  Layout L;
+  if (!blob || !make_layout(N, K, r, n_seg, &L)) return -1;
+  Packed P{L, N, K, r, n_seg, blob};
+  if (idx) std::memcpy(idx, P.idx(), 4LL * N);
+  if (What)
+    for (int64_t p = 0; p < N; ++p) P.row(p, What + p * K);
+  if (U)
+    for (int64_t i = 0; i < static_cast<int64_t>(N) * r; ++i) U[i] = double_from_bf16(P.U()[i]);
+  if (V)
+    for (int64_t i = 0; i < static_cast<int64_t>(n_seg) * r * K; ++i)
+      V[i] = double_from_bf16(P.V()[i]);
+  return 0;
+}
+
+// y [M][N] (original column order) of the layer for bf16 x [M][K].
+int orc_forward(const uint8_t *blob, int N, int K, int r, int b, int n_seg, const uint16_t *x,
+                int M, double *y, int nthreads) {
+  Layout L;
+  if (!blob || !x || !y || !pow2(b) || K % b != 0 || M < 0 || !make_layout(N, K, r, n_seg, &L))
+    return -1;
+  Packed P{L, N, K, r, n_seg, blob};
+  forward(P, b, x, M, nullptr, 0, y, nthreads > 0 ? nthreads : default_threads());
+  return 0;
+}
+
+// y [M][ncols]: the same forward restricted to original output columns cols[].
+int orc_forward_cols(const uint8_t *blob, int N, int K, int r, int b, int n_seg,
+                     const uint16_t *x, int M, const int32_t *cols, int ncols, double *y,
+                     int nthreads) {
+  Layout L;
+  if (!blob || !x || !y || !cols || !pow2(b) || K % b != 0 || M < 0 ||
+      !make_layout(N, K, r, n_seg, &L))
+    return -1;
+  for (int c = 0; c < ncols; ++c)
+    if (cols[c] < 0 || cols[c] >= N) return -1;
+  Packed P{L, N, K, r, n_seg, blob};
+  forward(P, b, x, M, cols, ncols, y, nthreads > 0 ? nthreads : default_threads());
+  return 0;
+}
+
+// Rotate bf16 activations: xr [M][K] = x H_K in fp64.
+int orc_rotate_x(const uint16_t *x, int M, int K, int b, double *xr) {
+  if (!x || !xr || !pow2(b) || K % b != 0) return -1;
+  for (int64_t i = 0; i < static_cast<int64_t>(M) * K; ++i) xr[i] = double_from_bf16(x[i]);
+  fwht_rows(xr, M, K, b);
+  return 0;
+}
+
+}  // extern "C"
