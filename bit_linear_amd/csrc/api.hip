@@ -1,0 +1,272 @@
+// Host side of the C ABI declared in include/dvssq.h: argument validation,
+// packed-layout arithmetic and kernel dispatch.  Every check runs before the
+// first HIP call, so each error path is reachable without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include "dvssq_internal.h"
+
+namespace dvssq {
+int prologue_rows_per_wg(int block);
+}
+
+using namespace dvssq;
+
+namespace {
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_shape(int32_t N, int32_t K, int32_t r, int32_t block, int32_t n_seg, int32_t M_max) {
+  if (N <= 0 || K <= 0 || r < 1 || r > 64 || M_max < 1) return DVSSQ_EINVAL;
+  if (n_seg != 1 && n_seg != 2) return DVSSQ_EINVAL;
+  if (n_seg * r > 64) return DVSSQ_EINVAL;
+  if (K % DVSSQ_GROUP != 0 || N % (8 * n_seg) != 0) return DVSSQ_EINVAL;
+  if (block <= 0 || K % block != 0) return DVSSQ_EINVAL;
+  if (!is_pow2(block) || block < 64 || block > 2048) return DVSSQ_EUNSUPPORTED;
+  if (static_cast<int64_t>(N) * K > (int64_t(1) << 40)) return DVSSQ_EINVAL;
+  return DVSSQ_OK;
+}
+
+// Re-derives the layout from its shape fields and compares: rejects a layout
+// that did not come from dvssq_pack_info (or was edited).
+int check_layout(const dvssq_layout *L) {
+  if (L == nullptr) return DVSSQ_EINVAL;
+  dvssq_layout ref;
+  const int rc = dvssq_pack_info(L->N, L->K, L->r, L->block, L->n_seg, L->M_max, &ref);
+  if (rc != DVSSQ_OK) return rc;
+  if (memcmp(&ref, L, sizeof ref) != 0) return DVSSQ_EINVAL;
+  return DVSSQ_OK;
+}
+
+int check_call(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M,
+               void *ws, int32_t M_limit) {
+  int rc = check_layout(L);
+  if (rc != DVSSQ_OK) return rc;
+  if (!blob || !x || !y || !ws) return DVSSQ_EINVAL;
+  if (M < 1 || M > L->M_max) return DVSSQ_EINVAL;
+  if (M > M_limit) return DVSSQ_EUNSUPPORTED;
+  if (!aligned(blob, 256) || !aligned(ws, 256) || !aligned(x, 16) || !aligned(y, 16)) return DVSSQ_EINVAL;
+  const size_t xb = static_cast<size_t>(M) * L->K * 2, yb = static_cast<size_t>(M) * L->N * 2;
+  if (overlap(x, xb, y, yb) || overlap(y, yb, blob, L->blob_bytes) || overlap(y, yb, ws, L->ws_bytes) ||
+      overlap(x, xb, ws, L->ws_bytes))
+    return DVSSQ_EINVAL;
+  return DVSSQ_OK;
+}
+
+struct Blob {
+  const uint8_t *b;
+  const dvssq_layout *L;
+  const int32_t *idx() const { return reinterpret_cast<const int32_t *>(b + L->off_idx); }
+  const uint8_t *q4() const { return b + L->off_q4; }
+  const uint16_t *s4() const { return reinterpret_cast<const uint16_t *>(b + L->off_s4); }
+  const int8_t *q8() const { return reinterpret_cast<const int8_t *>(b + L->off_q8); }
+  const float *s8() const { return reinterpret_cast<const float *>(b + L->off_s8); }
+  const uint16_t *U() const { return reinterpret_cast<const uint16_t *>(b + L->off_U); }
+  const uint16_t *V() const { return reinterpret_cast<const uint16_t *>(b + L->off_V); }
+};
+
+float inv_sqrt_block(int block) {
+  // 1/sqrt(b) rounded once to fp32: b = 2^e
+  int e = 0;
+  while ((1 << e) < block) ++e;
+  double v = 1.0;
+  for (int i = 0; i < e / 2; ++i) v *= 0.5;
+  if (e % 2) v *= 0.70710678118654752440;
+  return static_cast<float>(v);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dvssq_pack_info(int32_t N, int32_t K, int32_t r, int32_t block, int32_t n_seg, int32_t M_max,
+                    dvssq_layout *out) {
+  if (out == nullptr) return DVSSQ_EINVAL;
+  const int rc = check_shape(N, K, r, block, n_seg, M_max);
+  if (rc != DVSSQ_OK) return rc;
+  dvssq_layout L;
+  memset(&L, 0, sizeof L);
+  L.N = N;
+  L.K = K;
+  L.r = r;
+  L.block = block;
+  L.group = DVSSQ_GROUP;
+  L.n_seg = n_seg;
+  L.n_int8 = N / n_seg / 8 * n_seg;
+  L.n_int4 = N - L.n_int8;
+  L.M_max = M_max;
+  const int64_t n4 = L.n_int4, n8 = L.n_int8;
+  const int64_t sz[7] = {4LL * N,
+                         n4 * (K / 2),
+                         n4 * (K / DVSSQ_GROUP) * 2,
+                         n8 * K,
+                         n8 * 4,
+                         2LL * N * r,
+                         2LL * n_seg * r * K};
+  int64_t *offs[7] = {&L.off_idx, &L.off_q4, &L.off_s4, &L.off_q8, &L.off_s8, &L.off_U, &L.off_V};
+  int64_t cur = 0, algo = 0;
+  for (int i = 0; i < 7; ++i) {
+    *offs[i] = cur;
+    cur = align256(cur + sz[i]);
+    algo += sz[i];
+  }
+  L.blob_bytes = cur;
+  L.algo_bytes = algo;
+  L.ws_bytes = ws_layout(L).total;
+  *out = L;
+  return DVSSQ_OK;
+}
+
+int dvssq_fwht(const void *x, void *xrot, int32_t M, int32_t K, int32_t block, void *stream) {
+  if (!x || !xrot || M < 0 || K <= 0) return DVSSQ_EINVAL;
+  if (block <= 0 || K % block != 0) return DVSSQ_EINVAL;
+  if (!is_pow2(block) || block < 64 || block > 2048) return DVSSQ_EUNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(xrot, 16)) return DVSSQ_EINVAL;
+  if (x != xrot && overlap(x, static_cast<size_t>(M) * K * 2, xrot, static_cast<size_t>(M) * K * 2))
+    return DVSSQ_EINVAL;
+  if (M == 0) return DVSSQ_OK;
+  PrologueArgs a{};
+  a.x = static_cast<const uint16_t *>(x);
+  a.xr = static_cast<uint16_t *>(xrot);
+  a.M = M;
+  a.K = K;
+  a.blocks_per_wg = 1;
+  a.rotate = 1;
+  a.scale = inv_sqrt_block(block);
+  const hipError_t e = launch_prologue(a, block, prologue_rows_per_wg(block), K / block,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
+}
+
+int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M,
+                        void *ws, uint32_t flags, void *stream) {
+  int rc = check_call(L, blob, x, y, M, ws, DVSSQ_DECODE_MAX_M);
+  if (rc != DVSSQ_OK) return rc;
+  if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
+  const WsLayout W = ws_layout(*L);
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  const Blob B{static_cast<const uint8_t *>(blob), L};
+  const int nsp = nsr_pad_of(L->n_seg, L->r);
+  const int n4t = (L->n_int4 + 31) / 32, n8t = (L->n_int8 + 31) / 32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  PrologueArgs p{};
+  p.x = static_cast<const uint16_t *>(x);
+  p.xr = reinterpret_cast<uint16_t *>(wsb + W.d_xr);
+  p.xs = reinterpret_cast<float *>(wsb + W.d_xs);
+  p.V = B.V();
+  p.tp = reinterpret_cast<float *>(wsb + W.d_tp);
+  p.cnt_zero = reinterpret_cast<int *>(wsb + W.d_cnt);
+  p.n_cnt = n4t + n8t;
+  p.M = M;
+  p.K = L->K;
+  p.nsr = L->n_seg * L->r;
+  p.nsr_pad = nsp;
+  p.tp_rows = kDecodeRows;
+  p.blocks_per_wg = 1;
+  p.permuted = 1;
+  p.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
+  p.scale = inv_sqrt_block(L->block);
+  hipError_t e = launch_prologue(p, L->block, prologue_rows_per_wg(L->block), L->K / L->block, s);
+  if (e != hipSuccess) return DVSSQ_EHIP;
+
+  DecodeArgs d{};
+  d.q4 = B.q4();
+  d.s4 = B.s4();
+  d.q8 = B.q8();
+  d.s8 = B.s8();
+  d.U = B.U();
+  d.idx = B.idx();
+  d.xr = p.xr;
+  d.xs = p.xs;
+  d.tp = p.tp;
+  d.part = reinterpret_cast<float *>(wsb + W.d_part);
+  d.cnt = p.cnt_zero;
+  d.y = static_cast<uint16_t *>(y);
+  d.N = L->N;
+  d.K = L->K;
+  d.r = L->r;
+  d.n_seg = L->n_seg;
+  d.n4 = L->n_int4;
+  d.n8 = L->n_int8;
+  d.M = M;
+  d.block = L->block;
+  d.nsr = p.nsr;
+  d.nsr_pad = nsp;
+  d.nchunk = (L->K + kChunk - 1) / kChunk;
+  d.n4_tiles = n4t;
+  d.n8_tiles = n8t;
+  e = launch_decode(d, s);
+  return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
+}
+
+int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M,
+                         void *ws, uint32_t flags, void *stream) {
+  int rc = check_call(L, blob, x, y, M, ws, L ? L->M_max : 0);
+  if (rc != DVSSQ_OK) return rc;
+  if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
+  const WsLayout W = ws_layout(*L);
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  const Blob B{static_cast<const uint8_t *>(blob), L};
+  const int nsp = nsr_pad_of(L->n_seg, L->r);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  PrologueArgs p{};
+  p.x = static_cast<const uint16_t *>(x);
+  p.xr = reinterpret_cast<uint16_t *>(wsb + W.p_xr);
+  p.V = B.V();
+  p.tp = reinterpret_cast<float *>(wsb + W.p_t);
+  p.M = M;
+  p.K = L->K;
+  p.nsr = L->n_seg * L->r;
+  p.nsr_pad = nsp;
+  p.tp_rows = L->M_max;
+  p.blocks_per_wg = L->K / L->block;
+  p.permuted = 0;
+  p.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
+  p.scale = inv_sqrt_block(L->block);
+  hipError_t e = launch_prologue(p, L->block, prologue_rows_per_wg(L->block), 1, s);
+  if (e != hipSuccess) return DVSSQ_EHIP;
+
+  PrefillArgs f{};
+  f.q4 = B.q4();
+  f.s4 = B.s4();
+  f.q8 = B.q8();
+  f.s8 = B.s8();
+  f.U = B.U();
+  f.idx = B.idx();
+  f.xr = p.xr;
+  f.t = p.tp;
+  f.y = static_cast<uint16_t *>(y);
+  f.N = L->N;
+  f.K = L->K;
+  f.r = L->r;
+  f.n_seg = L->n_seg;
+  f.n4 = L->n_int4;
+  f.n8 = L->n_int8;
+  f.M = M;
+  f.nsr = p.nsr;
+  f.nsr_pad = nsp;
+  f.n4_tiles = (L->n_int4 + 127) / 128;
+  f.n8_tiles = (L->n_int8 + 127) / 128;
+  f.m_tiles = (M + 127) / 128;
+  e = launch_prefill(f, s);
+  return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
+}
+
+const char *dvssq_status_str(int status) {
+  switch (status) {
+    case DVSSQ_OK: return "ok";
+    case DVSSQ_EINVAL: return "invalid argument";
+    case DVSSQ_EUNSUPPORTED: return "unsupported configuration";
+    case DVSSQ_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

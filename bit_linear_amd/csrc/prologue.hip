@@ -1,0 +1,230 @@
+// Activation side of the DV-SSQ layer: x_rot = x H_K, the decode group sums of
+// x_rot, and t = x_rot V^T.
+//
+// Rotation: MiniCPM5-2B-Hadamard-GSQ model card, Mathematical Foundations 1
+// (X' = X H, Sylvester H) and Spark-X2.5-4B-Hadamard-GSQ model card, Tier B
+// equation (block-diagonal H_K).  t: MiniCPM card, Mathematical Foundations 2,
+// runtime equation (the X B^T factor).
+//
+// One workgroup = 4 wavefronts handles MT activation rows and a run of
+// Hadamard blocks.  Each row of a block is rotated by one wavefront with the
+// fast Walsh-Hadamard transform: V = block/64 consecutive values per lane,
+// log2(V) butterfly stages inside the lane's registers, then 6 stages across
+// lanes (xor 1..32).  The bf16-rounded block is staged in LDS, copied out in
+// the order the consumer wants, and multiplied by V^T on the matrix cores
+// (32x32x16 bf16 MFMA), accumulating t over the workgroup's blocks.
+#include "dvssq_internal.h"
+
+namespace dvssq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int VPL>  // values per lane = block / 64
+__device__ __forceinline__ void load_row(const uint16_t *src, float (&v)[VPL]) {
+  if constexpr (VPL >= 8) {
+#pragma unroll
+    for (int q = 0; q < VPL / 8; ++q) {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(src + 8 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * q + 2 * e] = __uint_as_float(w[e] << 16);
+        v[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    }
+  } else if constexpr (VPL == 4) {
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
+    v[0] = __uint_as_float(w[0] << 16);
+    v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+    v[2] = __uint_as_float(w[1] << 16);
+    v[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) v[j] = bf16_to_f32(src[j]);
+  }
+}
+
+template <int VPL>
+__device__ __forceinline__ void fwht_wave(float (&v)[VPL], int lane) {
+#pragma unroll
+  for (int s = 1; s < VPL; s <<= 1)
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (!(j & s)) {
+        const float a = v[j], b = v[j + s];
+        v[j] = a + b;
+        v[j + s] = a - b;
+      }
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const bool upper = (lane & s) != 0;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const float p = __shfl_xor(v[j], s, 64);
+      v[j] = upper ? (p - v[j]) : (v[j] + p);
+    }
+  }
+}
+
+template <int VPL, int MT>
+__global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
+  constexpr int B = 64 * VPL;
+  constexpr int LDSR = B + 8;  // padded LDS row (bf16 elements)
+  extern __shared__ __align__(16) uint16_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * MT;
+  const int nblk = a.K / B;
+  const int b0 = blockIdx.y * a.blocks_per_wg;
+  const int b1 = min(nblk, b0 + a.blocks_per_wg);
+  const int mrows = min(MT, a.M - m0);
+  const bool want_t = a.nsr > 0;
+  const int n_it = (a.nsr_pad + 31) / 32;
+
+  if (a.cnt_zero != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = tid; i < a.n_cnt; i += kThreads) a.cnt_zero[i] = 0;
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[it][e] = 0.0f;
+
+  for (int blk = b0; blk < b1; ++blk) {
+    const int kb = blk * B;
+    // 1. rotate each row of this block (one wavefront per row), stage bf16 in LDS
+    for (int ml = wave; ml < MT; ml += 4) {
+      uint16_t *row = lds + ml * LDSR + lane * VPL;
+      if (ml < mrows) {
+        float v[VPL];
+        load_row<VPL>(a.x + static_cast<int64_t>(m0 + ml) * a.K + kb + lane * VPL, v);
+        if (a.rotate) {
+          fwht_wave<VPL>(v, lane);
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) v[j] *= a.scale;
+        }
+#pragma unroll
+        for (int j = 0; j < VPL; j += 2) {
+          if constexpr (VPL >= 2) {
+            *reinterpret_cast<uint32_t *>(row + j) = pack_bf16x2(v[j], v[j + 1]);
+          } else {
+            row[j] = f32_to_bf16(v[j]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) row[j] = 0;
+      }
+    }
+    __syncthreads();
+    // 2. copy out in runs of 8 (decode order 0,4,1,5,2,6,3,7 when permuted), and group sums
+    constexpr int RUNS = B / 8;
+    for (int e = tid; e < MT * RUNS; e += kThreads) {
+      const int ml = e / RUNS, run = e % RUNS;
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(lds + ml * LDSR + run * 8);
+      float gsum = 0.0f;
+      if (a.xs != nullptr) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          gsum += __uint_as_float(w[q] << 16) + __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+      if (ml < mrows) {
+        u32x4 o = w;
+        if (a.permuted) {
+          // natural halves: w[q] = (e_{2q}, e_{2q+1});  want (e0,e4),(e1,e5),(e2,e6),(e3,e7)
+          const uint32_t lo = 0xFFFFu;
+          o[0] = (w[0] & lo) | (w[2] << 16);
+          o[1] = (w[0] >> 16) | (w[2] & ~lo);
+          o[2] = (w[1] & lo) | (w[3] << 16);
+          o[3] = (w[1] >> 16) | (w[3] & ~lo);
+        }
+        *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) = o;
+      }
+      if (a.xs != nullptr) {
+        // 8 consecutive runs form one group of 64; they sit in 8 consecutive lanes
+        gsum += __shfl_xor(gsum, 1, 64);
+        gsum += __shfl_xor(gsum, 2, 64);
+        gsum += __shfl_xor(gsum, 4, 64);
+        if ((run & 7) == 0 && ml < mrows)
+          a.xs[static_cast<int64_t>((kb + run * 8) / kGroup) * kDecodeRows + m0 + ml] = gsum;
+      }
+    }
+    // 3. t += x_rot(block) V(block)^T on the matrix cores; K-steps of 16 split over the waves
+    if (want_t) {
+      const int arow = lane & 31, half = lane >> 5;
+      for (int s = wave; s < B / 16; s += 4) {
+        u32x4 av = {0u, 0u, 0u, 0u};
+        if (arow < MT) av = *reinterpret_cast<const u32x4 *>(lds + arow * LDSR + 16 * s + 8 * half);
+        for (int it = 0; it < n_it; ++it) {
+          const int i = 32 * it + arow;
+          u32x4 bv = {0u, 0u, 0u, 0u};
+          if (i < a.nsr)
+            bv = *reinterpret_cast<const u32x4 *>(a.V + static_cast<int64_t>(i) * a.K + kb + 16 * s + 8 * half);
+          if (it == 0) acc[0] = mfma32x32x16(av, bv, acc[0]);
+          else acc[1] = mfma32x32x16(av, bv, acc[1]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (!want_t) return;
+  // 4. reduce the four waves' partial t and write it out
+  float *red = reinterpret_cast<float *>(lds);  // [4 waves][2 it][32 m][32 i]
+  {
+    const int col = lane & 31, half = lane >> 5;
+    for (int it = 0; it < n_it; ++it)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 8 * (v / 4) + 4 * half + (v % 4);
+        red[((wave * 2 + it) * 32 + m) * 32 + col] = acc[it][v];
+      }
+  }
+  __syncthreads();
+  for (int e = tid; e < mrows * a.nsr_pad; e += kThreads) {
+    const int ml = e / a.nsr_pad, i = e % a.nsr_pad;
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s += red[((w * 2 + i / 32) * 32 + ml) * 32 + (i % 32)];
+    a.tp[(static_cast<int64_t>(blockIdx.y) * a.tp_rows + m0 + ml) * a.nsr_pad + i] = s;
+  }
+}
+
+template <int VPL, int MT>
+hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
+  constexpr int B = 64 * VPL;
+  const size_t lds_rows = static_cast<size_t>(MT) * (B + 8) * 2;
+  const size_t lds_red = 4 * 2 * 32 * 32 * 4;
+  const size_t lds = lds_rows > lds_red ? lds_rows : lds_red;
+  if (lds > 65536) {
+    static bool attr_set = false;
+    if (!attr_set) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prologue_kernel<VPL, MT>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+  }
+  dim3 grid((a.M + MT - 1) / MT, n_wg_blocks);
+  hipLaunchKernelGGL((prologue_kernel<VPL, MT>), grid, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const PrologueArgs &a, int block, int /*m_rows_per_wg*/,
+                           int n_wg_blocks, hipStream_t s) {
+  switch (block) {
+    case 64: return launch_vpl<1, 32>(a, n_wg_blocks, s);
+    case 128: return launch_vpl<2, 32>(a, n_wg_blocks, s);
+    case 256: return launch_vpl<4, 32>(a, n_wg_blocks, s);
+    case 512: return launch_vpl<8, 32>(a, n_wg_blocks, s);
+    case 1024: return launch_vpl<16, 32>(a, n_wg_blocks, s);
+    case 2048: return launch_vpl<32, 16>(a, n_wg_blocks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int prologue_rows_per_wg(int block) { return block == 2048 ? 16 : 32; }
+
+}  // namespace dvssq

@@ -1,0 +1,153 @@
+"""C-ABI contract tests that need no GPU: symbols, layout arithmetic and every
+error path (all argument checks run before the first HIP call)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import bit_linear_amd as dv
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dvssq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dvssq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(dv.EXPORTS)
+    lib = C.CDLL(dv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_layout_struct_size_matches_header():
+    # 10 int32 + 10 int64 fields, no padding
+    assert C.sizeof(dv.Layout) == 10 * 4 + 10 * 8
+
+
+@pytest.mark.parametrize("N,K,r,block,n_seg", [
+    (512, 256, 4, 256, 1), (10240, 2560, 16, 256, 1), (2560, 10240, 16, 256, 1),
+    (20480, 2560, 24, 256, 2), (6144, 2048, 16, 2048, 1), (2048, 6144, 32, 2048, 1),
+    (520, 192, 1, 64, 1), (48, 128, 64, 128, 1),
+])
+def test_pack_info_matches_oracle_layout(N, K, r, block, n_seg):
+    L = dv.pack_info(N, K, r, block, n_seg, M_max=4096)
+    ref = oracle.layout(N, K, r, n_seg)
+    assert L.n_int4 == ref["N4"] and L.n_int8 == ref["N8"]
+    for k in ("off_idx", "off_q4", "off_s4", "off_q8", "off_s8", "off_U", "off_V",
+              "blob_bytes", "algo_bytes"):
+        assert getattr(L, k) == ref[k], k
+    assert (L.N, L.K, L.r, L.block, L.group, L.n_seg, L.M_max) == (N, K, r, block, 64, n_seg, 4096)
+    assert L.ws_bytes > 0 and L.ws_bytes % 256 == 0
+
+
+def test_algo_bytes_of_workloads():
+    # packed sizes of the benchmark layers (bytes of the layer itself, no padding)
+    assert dv.pack_info(512, 256, 4, 256).algo_bytes == 85_760
+    assert dv.pack_info(10240, 2560, 16, 256).algo_bytes == 15_918_080
+    assert dv.pack_info(2560, 10240, 16, 256).algo_bytes == 15_883_520
+    assert dv.pack_info(20480, 2560, 24, 256, 2).algo_bytes == 32_245_760
+    assert dv.pack_info(6144, 2048, 16, 2048).algo_bytes == 7_711_744
+    assert dv.pack_info(2048, 6144, 16, 2048).algo_bytes == 7_693_312
+
+
+def rc_pack(*args):
+    out = dv.Layout()
+    return dv.lib().dvssq_pack_info(*args, C.byref(out))
+
+
+@pytest.mark.parametrize("args,code", [
+    ((512, 256, 4, 256, 1, 32), dv.DVSSQ_OK),
+    ((0, 256, 4, 256, 1, 32), dv.DVSSQ_EINVAL),        # N <= 0
+    ((516, 256, 4, 256, 1, 32), dv.DVSSQ_EINVAL),      # N % 8
+    ((520, 256, 4, 256, 2, 32), dv.DVSSQ_EINVAL),      # N % 16 with two segments
+    ((512, 200, 4, 256, 1, 32), dv.DVSSQ_EINVAL),      # K % 64
+    ((512, 320, 4, 256, 1, 32), dv.DVSSQ_EINVAL),      # K % block
+    ((512, 256, 0, 256, 1, 32), dv.DVSSQ_EINVAL),      # r < 1
+    ((512, 256, 65, 256, 1, 32), dv.DVSSQ_EINVAL),     # r > 64
+    ((512, 256, 33, 256, 2, 32), dv.DVSSQ_EINVAL),     # n_seg * r > 64
+    ((512, 256, 4, 256, 3, 32), dv.DVSSQ_EINVAL),      # n_seg
+    ((512, 256, 4, 256, 1, 0), dv.DVSSQ_EINVAL),       # M_max
+    ((512, 256, 4, 32, 1, 32), dv.DVSSQ_EUNSUPPORTED),   # block below 64
+    ((512, 8192, 4, 4096, 1, 32), dv.DVSSQ_EUNSUPPORTED),  # block above 2048
+    ((512, 384, 4, 192, 1, 32), dv.DVSSQ_EUNSUPPORTED),    # not a power of two
+])
+def test_pack_info_errors(args, code):
+    assert rc_pack(*args) == code
+
+
+def test_pack_info_null_out():
+    assert dv.lib().dvssq_pack_info(512, 256, 4, 256, 1, 32, None) == dv.DVSSQ_EINVAL
+
+
+# Fake, never-dereferenced device addresses: every call below fails validation
+# before any HIP call, so they run without a GPU.
+BLOB, X, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def call(fn, L, blob=BLOB, x=X, y=Y, M=1, ws=WS, flags=0):
+    f = getattr(dv.lib(), fn)
+    return f(C.byref(L) if L is not None else None, blob, x, y, M, ws, flags, None)
+
+
+@pytest.mark.parametrize("fn", ["dvssq_linear_decode", "dvssq_linear_prefill"])
+def test_linear_error_paths(fn):
+    L = dv.pack_info(512, 256, 4, 256, 1, M_max=64)
+    E = dv.DVSSQ_EINVAL
+    assert call(fn, None) == E
+    assert call(fn, L, blob=None) == E
+    assert call(fn, L, x=None) == E
+    assert call(fn, L, y=None) == E
+    assert call(fn, L, ws=None) == E
+    assert call(fn, L, M=0) == E
+    assert call(fn, L, M=65) == E                         # above M_max
+    assert call(fn, L, blob=BLOB + 16) == E               # blob not 256-aligned
+    assert call(fn, L, ws=WS + 128) == E                  # ws not 256-aligned
+    assert call(fn, L, x=X + 2) == E                      # x not 16-aligned
+    assert call(fn, L, y=Y + 8) == E                      # y not 16-aligned
+    assert call(fn, L, y=X + 256) == E                    # y overlaps x
+    assert call(fn, L, y=WS + 1024) == E                  # y overlaps ws
+    assert call(fn, L, flags=2) == E                      # unknown flag
+    bad = dv.pack_info(512, 256, 4, 256, 1, M_max=64)
+    bad.off_V += 256                                      # edited layout
+    assert call(fn, bad) == E
+    bad2 = dv.pack_info(512, 256, 4, 256, 1, M_max=64)
+    bad2.K = 300
+    assert call(fn, bad2) == E
+
+
+def test_decode_rejects_large_m():
+    L = dv.pack_info(512, 256, 4, 256, 1, M_max=64)
+    assert call("dvssq_linear_decode", L, M=33) == dv.DVSSQ_EUNSUPPORTED
+
+
+def test_fwht_error_paths():
+    f = dv.lib().dvssq_fwht
+    assert f(None, Y, 4, 256, 256, None) == dv.DVSSQ_EINVAL
+    assert f(X, None, 4, 256, 256, None) == dv.DVSSQ_EINVAL
+    assert f(X, Y, -1, 256, 256, None) == dv.DVSSQ_EINVAL
+    assert f(X, Y, 4, 320, 256, None) == dv.DVSSQ_EINVAL       # K % block
+    assert f(X, Y, 4, 256, 32, None) == dv.DVSSQ_EUNSUPPORTED
+    assert f(X, Y, 4, 96 * 4, 96, None) == dv.DVSSQ_EUNSUPPORTED
+    assert f(X + 2, Y, 4, 256, 256, None) == dv.DVSSQ_EINVAL
+    assert f(X, X + 512, 4, 256, 256, None) == dv.DVSSQ_EINVAL  # partial overlap
+    assert f(X, Y, 0, 256, 256, None) == dv.DVSSQ_OK            # M = 0: nothing to do
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, 7):
+        assert isinstance(dv.status_str(code), str) and dv.status_str(code)
+    assert dv.status_str(dv.DVSSQ_EINVAL) != dv.status_str(dv.DVSSQ_EHIP)
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(dv.DvssqError) as ei:
+        dv.pack_info(516, 256, 4, 256)
+    assert ei.value.code == dv.DVSSQ_EINVAL

@@ -1,0 +1,201 @@
+"""GPU parity: every call goes through the C ABI (libdvssq.so) and is compared
+with the fp64 oracle on the same seeded inputs and the same packed blob.
+
+Bar: max|y_gpu - y_ref| / max|y_ref| <= 5e-3 (bf16 activations, fp32
+accumulation); bit-exact for the blob round trip and for repeated calls.
+"""
+import numpy as np
+import pytest
+
+import cases
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import bit_linear_amd as dv  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def gpu_layer(name, M_max):
+    lay, blob = cases.quantized(name)
+    return lay, blob, dv.Linear(blob, lay.N, lay.K, lay.r, lay.block, lay.n_seg, M_max=M_max, device=DEV)
+
+
+def run(lin, x_bits, path, flags=0):
+    x = cases.to_device_bf16(x_bits, DEV)
+    y = lin.forward(x, flags=flags, path=path)
+    torch.cuda.synchronize()
+    return cases.from_device_bf16(y)
+
+
+# ------------------------------------------------------------------ rotation
+
+@pytest.mark.parametrize("b", [64, 128, 256, 512, 1024, 2048])
+@pytest.mark.parametrize("M", [1, 5, 37])
+def test_fwht_parity(b, M):
+    K = b * (3 if b <= 512 else 2)
+    x_bits = synth.activations_bf16(7, f"fwht{b}", M, K)
+    ref = oracle.rotate_x(x_bits, b)
+    x = cases.to_device_bf16(x_bits, DEV)
+    out = torch.empty_like(x)
+    dv.fwht(x, out, M, K, b)
+    torch.cuda.synchronize()
+    got = cases.from_device_bf16(out)
+    err = np.abs(got - ref)
+    assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+    same = got == synth.bf16_bits_to_f64(synth.to_bf16_bits(ref))
+    assert same.mean() >= 0.99
+    # in place
+    dv.fwht(x, x, M, K, b)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cases.from_device_bf16(x), got)
+
+
+def test_fwht_exact_special_cases():
+    b, K = 256, 512
+    x = np.zeros((3, K))
+    x[0, 3] = 1.0                 # one-hot -> +-1/16 everywhere in its block
+    x[1, 256:] = 1.0              # constant block -> 16 e_0
+    x[2, 100] = -2.0
+    bits = synth.to_bf16_bits(x)
+    d = cases.to_device_bf16(bits, DEV)
+    out = torch.empty_like(d)
+    dv.fwht(d, out, 3, K, b)
+    torch.cuda.synchronize()
+    got = cases.from_device_bf16(out)
+    np.testing.assert_array_equal(got, oracle.rotate_x(bits, b))
+    np.testing.assert_array_equal(np.abs(got[0, :256]), np.full(256, 1 / 16))
+    assert got[1, 256] == 16 and not got[1, 257:].any() and not got[1, :256].any()
+
+
+# ------------------------------------------------------------------ decode
+
+DECODE_CASES = [
+    ("tiny", 1), ("tiny", 4), ("tiny", 3), ("tiny", 8), ("tiny", 9), ("tiny", 16), ("tiny", 17),
+    ("tiny", 32),
+    ("spark_up", 1), ("spark_up", 4), ("spark_up", 16),
+    ("spark_down", 1), ("spark_down", 8), ("spark_down", 32),
+    ("minicpm_gate", 1), ("minicpm_up", 1), ("minicpm_down", 1),
+    ("minicpm_gate_r32", 1), ("minicpm_down_r32", 1),
+    ("spark_gateup", 1), ("spark_gateup", 4),
+    ("ragged_b64_r1", 1), ("ragged_b64_r1", 7), ("b128_r64", 32), ("seg2_b512_r32", 5),
+    ("b1024_tail", 3), ("b2048_ragged", 17), ("b2048_ragged", 32), ("seg2_small", 2),
+]
+
+
+@pytest.mark.parametrize("name,M", DECODE_CASES, ids=[f"{n}-M{m}" for n, m in DECODE_CASES])
+def test_decode_parity(name, M):
+    lay, blob, lin = gpu_layer(name, 32)
+    x_bits = cases.activations(name, 32)[:M]
+    y = run(lin, x_bits, "decode")
+    ref = oracle.forward(blob, lay.N, lay.K, lay.r, lay.block, lay.n_seg, x_bits)
+    err = cases.rel_err(y, ref)
+    print(f"{name} M={M} decode rel_err={err:.3e}")
+    assert err <= cases.TOL
+
+
+# ------------------------------------------------------------------ prefill
+
+PREFILL_CASES = [
+    ("tiny", 1), ("tiny", 4), ("tiny", 33), ("tiny", 130), ("tiny", 257),
+    ("ragged_b64_r1", 45), ("b128_r64", 200), ("seg2_b512_r32", 129), ("b1024_tail", 64),
+    ("b2048_ragged", 100), ("seg2_small", 77), ("spark_up", 40),
+]
+
+
+@pytest.mark.parametrize("name,M", PREFILL_CASES, ids=[f"{n}-M{m}" for n, m in PREFILL_CASES])
+def test_prefill_parity(name, M):
+    lay, blob, lin = gpu_layer(name, M)
+    x_bits = cases.activations(name, M)
+    y = run(lin, x_bits, "prefill")
+    ref = oracle.forward(blob, lay.N, lay.K, lay.r, lay.block, lay.n_seg, x_bits)
+    err = cases.rel_err(y, ref)
+    print(f"{name} M={M} prefill rel_err={err:.3e}")
+    assert err <= cases.TOL
+
+
+FULL_PREFILL = [("spark_gateup", 512), ("spark_gateup", 2048), ("minicpm_gate", 4096),
+                ("minicpm_up", 4096), ("minicpm_down", 4096), ("minicpm_down_r32", 4096)]
+
+
+@pytest.mark.parametrize("name,M", FULL_PREFILL, ids=[f"{n}-M{m}" for n, m in FULL_PREFILL])
+def test_prefill_full_size_sampled(name, M):
+    """Full-size prefill, checked on sampled output columns (all tokens)."""
+    lay, blob, lin = gpu_layer(name, M)
+    x_bits = cases.activations(name, M)
+    y = run(lin, x_bits, "prefill")
+    cols = cases.sample_columns(lay, blob)
+    ref = oracle.forward_cols(blob, lay.N, lay.K, lay.r, lay.block, lay.n_seg, x_bits, cols)
+    err = cases.rel_err(y[:, cols], ref)
+    print(f"{name} M={M} prefill sampled({cols.size} cols) rel_err={err:.3e}")
+    assert err <= cases.TOL
+
+
+# ------------------------------------------------------------------ special inputs and properties
+
+@pytest.mark.parametrize("path,M", [("decode", 5), ("prefill", 70)])
+def test_zero_input_gives_zero(path, M):
+    lay, blob, lin = gpu_layer("tiny", max(M, 32))
+    y = run(lin, np.zeros((M, lay.K), dtype=np.uint16), path)
+    assert not y.any()
+
+
+@pytest.mark.parametrize("path,M", [("decode", 6), ("prefill", 40)])
+def test_prerotated_input_flag(path, M):
+    lay, blob, lin = gpu_layer("spark_down" if path == "decode" else "tiny", max(M, 32))
+    x_bits = cases.activations(lay.name, M)
+    xr_bits = synth.to_bf16_bits(oracle.rotate_x(x_bits, lay.block))
+    y = run(lin, xr_bits, path, flags=dv.DVSSQ_X_ROTATED)
+    idx, What, U, V = oracle.unpack(blob, lay.N, lay.K, lay.r, lay.n_seg)
+    xr = synth.bf16_bits_to_f64(xr_bits)
+    ref = np.zeros((M, lay.N))
+    Ns = lay.N // lay.n_seg
+    t = xr @ V.T
+    for s in range(lay.n_seg):
+        rows = np.nonzero(idx // Ns == s)[0]
+        ref[:, idx[rows]] = xr @ What[rows].T + t[:, s * lay.r:(s + 1) * lay.r] @ U[rows].T
+    assert cases.rel_err(y, ref) <= cases.TOL
+
+
+def test_blob_roundtrip_bit_exact():
+    lay, blob, lin = gpu_layer("spark_up", 32)
+    back = lin.blob.cpu().numpy()
+    np.testing.assert_array_equal(back, blob)
+
+
+@pytest.mark.parametrize("path,name,M", [("decode", "spark_down", 8), ("prefill", "tiny", 130)])
+def test_repeat_calls_are_bit_identical(path, name, M):
+    lay, blob, lin = gpu_layer(name, max(M, 32))
+    x = cases.to_device_bf16(cases.activations(name, M), DEV)
+    first = lin.forward(x, path=path).clone()
+    for _ in range(20):
+        again = lin.forward(x, path=path)
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+
+
+def test_decode_and_prefill_share_workspace():
+    lay, blob, lin = gpu_layer("tiny", 64)
+    x_bits = cases.activations("tiny", 64)
+    ref = oracle.forward(blob, lay.N, lay.K, lay.r, lay.block, lay.n_seg, x_bits)
+    x = cases.to_device_bf16(x_bits, DEV)
+    yd = lin.forward(x[:3], path="decode")
+    yp = lin.forward(x, path="prefill")
+    yd2 = lin.forward(x[:32], path="decode")
+    torch.cuda.synchronize()
+    assert cases.rel_err(cases.from_device_bf16(yd), ref[:3]) <= cases.TOL
+    assert cases.rel_err(cases.from_device_bf16(yp), ref) <= cases.TOL
+    assert cases.rel_err(cases.from_device_bf16(yd2), ref[:32]) <= cases.TOL
+
+
+def test_decode_matches_prefill():
+    lay, blob, lin = gpu_layer("spark_up", 32)
+    x = cases.to_device_bf16(cases.activations("spark_up", 16), DEV)
+    yd = cases.from_device_bf16(lin.forward(x, path="decode"))
+    yp = cases.from_device_bf16(lin.forward(x, path="prefill"))
+    assert cases.rel_err(yd, yp) <= cases.TOL
