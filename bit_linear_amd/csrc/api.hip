@@ -4,11 +4,10 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "dvssq_internal.h"
+#include <atomic>
+#include <chrono>
 
-namespace dvssq {
-int prologue_rows_per_wg(int block);
-}
+#include "dvssq_internal.h"
 
 using namespace dvssq;
 
@@ -69,6 +68,38 @@ struct Blob {
   const uint16_t *U() const { return reinterpret_cast<const uint16_t *>(b + L->off_U); }
   const uint16_t *V() const { return reinterpret_cast<const uint16_t *>(b + L->off_V); }
 };
+
+// Generation stamps for the decode kernel's producer flags: a process-wide
+// counter started from a clock- and address-derived 64-bit value, so a stamp
+// left in a workspace by an earlier call or process is never mistaken for the
+// current one.
+uint64_t next_generation() {
+  static std::atomic<uint64_t> counter{[] {
+    uint64_t z = static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count());
+    z ^= reinterpret_cast<uintptr_t>(&counter) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }()};
+  uint64_t g;
+  do g = counter.fetch_add(1, std::memory_order_relaxed); while (g == 0);
+  return g;
+}
+
+// Split-K factor of the decode kernel: the smallest S (dividing K/64, at most
+// kMaxSplit) that gives >= 160 consumer workgroups while the LDS copy of the
+// rotated activations (M rows x K/S inputs, f16) stays within 96 KB.
+int decode_split(int K, int groups, int M) {
+  const int nchunk = K / DVSSQ_GROUP;
+  int best = 1;
+  for (int S = 1; S <= kMaxSplit && S <= nchunk; ++S) {
+    if (nchunk % S) continue;
+    const int64_t lds = static_cast<int64_t>(M) * (K / S + 8) * 2;
+    best = S;
+    if (lds <= 96 * 1024 && static_cast<int64_t>(groups) * S >= 160) return S;
+  }
+  return best;
+}
 
 float inv_sqrt_block(int block) {
   // 1/sqrt(b) rounded once to fp32: b = 2^e
@@ -137,9 +168,9 @@ int dvssq_fwht(const void *x, void *xrot, int32_t M, int32_t K, int32_t block, v
   a.K = K;
   a.blocks_per_wg = 1;
   a.rotate = 1;
-  a.scale = inv_sqrt_block(block);
-  const hipError_t e = launch_prologue(a, block, prologue_rows_per_wg(block), K / block,
-                                       static_cast<hipStream_t>(stream));
+  a.out_f16 = 0;
+  a.hscale = inv_sqrt_block(block);
+  const hipError_t e = launch_prologue(a, block, K / block, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
@@ -148,46 +179,27 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   int rc = check_call(L, blob, x, y, M, ws, DVSSQ_DECODE_MAX_M);
   if (rc != DVSSQ_OK) return rc;
   if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
+  if (L->K % decode_unit(L->block) != 0) return DVSSQ_EUNSUPPORTED;
   const WsLayout W = ws_layout(*L);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   const Blob B{static_cast<const uint8_t *>(blob), L};
-  const int nsp = nsr_pad_of(L->n_seg, L->r);
-  const int n4t = (L->n_int4 + 31) / 32, n8t = (L->n_int8 + 31) / 32;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  PrologueArgs p{};
-  p.x = static_cast<const uint16_t *>(x);
-  p.xr = reinterpret_cast<uint16_t *>(wsb + W.d_xr);
-  p.xs = reinterpret_cast<float *>(wsb + W.d_xs);
-  p.V = B.V();
-  p.tp = reinterpret_cast<float *>(wsb + W.d_tp);
-  p.cnt_zero = reinterpret_cast<int *>(wsb + W.d_cnt);
-  p.n_cnt = n4t + n8t;
-  p.M = M;
-  p.K = L->K;
-  p.nsr = L->n_seg * L->r;
-  p.nsr_pad = nsp;
-  p.tp_rows = kDecodeRows;
-  p.blocks_per_wg = 1;
-  p.permuted = 1;
-  p.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
-  p.scale = inv_sqrt_block(L->block);
-  hipError_t e = launch_prologue(p, L->block, prologue_rows_per_wg(L->block), L->K / L->block, s);
-  if (e != hipSuccess) return DVSSQ_EHIP;
-
   DecodeArgs d{};
   d.q4 = B.q4();
   d.s4 = B.s4();
   d.q8 = B.q8();
   d.s8 = B.s8();
   d.U = B.U();
+  d.V = B.V();
   d.idx = B.idx();
-  d.xr = p.xr;
-  d.xs = p.xs;
-  d.tp = p.tp;
+  d.x = static_cast<const uint16_t *>(x);
+  d.xq = reinterpret_cast<uint16_t *>(wsb + W.d_xq);
+  d.sc = reinterpret_cast<float *>(wsb + W.d_sc);
+  d.tp = reinterpret_cast<float *>(wsb + W.d_tp);
+  d.flag = reinterpret_cast<uint64_t *>(wsb + W.d_flag);
+  d.cnt = reinterpret_cast<int *>(wsb + W.d_cnt);
   d.part = reinterpret_cast<float *>(wsb + W.d_part);
-  d.cnt = p.cnt_zero;
   d.y = static_cast<uint16_t *>(y);
+  d.gen = next_generation();
   d.N = L->N;
   d.K = L->K;
   d.r = L->r;
@@ -196,12 +208,17 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.n8 = L->n_int8;
   d.M = M;
   d.block = L->block;
-  d.nsr = p.nsr;
-  d.nsr_pad = nsp;
-  d.nchunk = (L->K + kChunk - 1) / kChunk;
-  d.n4_tiles = n4t;
-  d.n8_tiles = n8t;
-  e = launch_decode(d, s);
+  d.unit = decode_unit(L->block);
+  d.nunit = L->K / d.unit;
+  d.nsr = L->n_seg * L->r;
+  d.nsr_pad = nsr_pad_of(L->n_seg, L->r);
+  d.g4 = decode_groups(L->n_int4);
+  d.g8 = decode_groups(L->n_int8);
+  d.S = decode_split(L->K, d.g4 + d.g8, M);
+  d.KW = L->K / d.S;
+  d.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
+  d.hscale = inv_sqrt_block(L->block);
+  const hipError_t e = launch_decode(d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
@@ -219,18 +236,18 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   PrologueArgs p{};
   p.x = static_cast<const uint16_t *>(x);
   p.xr = reinterpret_cast<uint16_t *>(wsb + W.p_xr);
+  p.sc = reinterpret_cast<float *>(wsb + W.p_sc);
   p.V = B.V();
-  p.tp = reinterpret_cast<float *>(wsb + W.p_t);
+  p.t = reinterpret_cast<float *>(wsb + W.p_t);
   p.M = M;
   p.K = L->K;
   p.nsr = L->n_seg * L->r;
   p.nsr_pad = nsp;
-  p.tp_rows = L->M_max;
   p.blocks_per_wg = L->K / L->block;
-  p.permuted = 0;
   p.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
-  p.scale = inv_sqrt_block(L->block);
-  hipError_t e = launch_prologue(p, L->block, prologue_rows_per_wg(L->block), 1, s);
+  p.out_f16 = 1;
+  p.hscale = inv_sqrt_block(L->block);
+  hipError_t e = launch_prologue(p, L->block, 1, s);
   if (e != hipSuccess) return DVSSQ_EHIP;
 
   PrefillArgs f{};
@@ -241,7 +258,8 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   f.U = B.U();
   f.idx = B.idx();
   f.xr = p.xr;
-  f.t = p.tp;
+  f.sc = p.sc;
+  f.t = p.t;
   f.y = static_cast<uint16_t *>(y);
   f.N = L->N;
   f.K = L->K;

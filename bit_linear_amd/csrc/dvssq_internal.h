@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/dvssq.h"
 
 namespace dvssq {
@@ -40,42 +42,107 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------------ f16 operands
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
+}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pk_fma(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, a),
+                                                                __builtin_bit_cast(f16x2, b),
+                                                                __builtin_bit_cast(f16x2, c)));
+}
+__device__ __forceinline__ uint32_t pk_add(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) + __builtin_bit_cast(f16x2, b));
+}
+// 8 INT4 codes (one dword, natural order) -> 8 exact f16 (n - 8) s, slots k+0,4,1,5,2,6,3,7.
+// Each nibble pair is moved to bits 6-9 of the two halves; or-ed with 0x4C00
+// that is the f16 value 16 + n.  With s = m 2^E (m < 256), -24 s = -3m 2^(E+3)
+// has at most 10 significant bits and (n - 8) s at most 11, so the fused
+// fma(16 + n, s, -24 s) returns (n - 8) s exactly.
+__device__ __forceinline__ u32x4 int4_to_f16(uint32_t w, uint32_t s2, uint32_t c24) {
+  const uint32_t m = 0x03C003C0u, o = 0x4C004C00u;
+  u32x4 r;
+  r[0] = pk_fma(((w << 6) & m) | o, s2, c24);
+  r[1] = pk_fma(((w << 2) & m) | o, s2, c24);
+  r[2] = pk_fma(((w >> 2) & m) | o, s2, c24);
+  r[3] = pk_fma(((w >> 6) & m) | o, s2, c24);
+  return r;
+}
+
+// 8 INT8 codes (k+0..3 in lo, k+4..7 in hi) -> 8 exact f16 q, slots k+0,4,1,5,2,6,3,7
+__device__ __forceinline__ u32x4 int8_to_f16(uint32_t lo, uint32_t hi) {
+  const uint32_t m1152 = 0xE480E480u;  // f16 -1152 twice
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t sel = 0x0C000C00u | ((4u + i) << 16) | static_cast<uint32_t>(i);
+    r[i] = pk_add(__builtin_amdgcn_perm(hi, lo, sel) ^ 0x64806480u, m1152);
+  }
+  return r;
+}
+
 // ------------------------------------------------------------------ workspace
 // Byte offsets inside the caller's workspace.  Decode and prefill regions
 // overlap (one call at a time per workspace).
+constexpr int kMaxSplit = 16;   // largest decode split-K factor
+
 struct WsLayout {
   // decode
-  int64_t d_xr;    // bf16 [32][K], rotated x, each 8-input run stored in the order 0,4,1,5,2,6,3,7
-  int64_t d_xs;    // fp32 [K/64][32] group sums of the bf16 rotated x
-  int64_t d_tp;    // fp32 [K/block][32][nsr_pad] per-block partial t = x_rot V^T
-  int64_t d_part;  // fp32 [nchunk][32][N] split-K partial outputs
-  int64_t d_cnt;   // int32 [n_tiles] arrivals per 32-row tile
+  int64_t d_xq;    // f16 [32][K]: rotated x scaled by 2^-e per (row, unit), runs of 8 in order 0,4,1,5,2,6,3,7
+  int64_t d_sc;    // fp32 [nunit][32]: 2^e of each (unit, row)
+  int64_t d_tp;    // fp32 [nunit][32][nsr_pad]: partial t = x_rot V^T of each unit
+  int64_t d_flag;  // u64 [nunit]: generation stamp written by the unit's producer
+  int64_t d_cnt;   // int32 [groups]: split-K arrivals per 64-row group
+  int64_t d_part;  // fp32 [kMaxSplit][32][N]: split-K partial outputs
   int64_t d_end;
   // prefill
-  int64_t p_xr;    // bf16 [M_max][K] rotated x, natural order
+  int64_t p_xr;    // f16 [M_max][K] rotated x scaled by 2^-e per row (or bf16 for dvssq_fwht)
+  int64_t p_sc;    // fp32 [M_max] 2^e per row
   int64_t p_t;     // fp32 [M_max][nsr_pad] t = x_rot V^T
   int64_t p_end;
   int64_t total;
 };
 
 inline int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
-inline int nsr_pad_of(int n_seg, int r) { return (n_seg * r + 15) / 16 * 16; }
-inline int decode_tiles(int n4, int n8) { return (n4 + 31) / 32 + (n8 + 31) / 32; }
+inline int nsr_pad_of(int n_seg, int r) { return (n_seg * r + 31) / 32 * 32; }
+inline int decode_unit(int block) { return block > 256 ? block : 256; }
+inline int decode_groups(int n) { return (n + 63) / 64; }
 
 inline WsLayout ws_layout(const dvssq_layout &L) {
   WsLayout w{};
   const int64_t K = L.K, N = L.N;
   const int nsp = nsr_pad_of(L.n_seg, L.r);
-  const int64_t nchunk = (K + kChunk - 1) / kChunk;
+  const int64_t nunit = K / decode_unit(L.block);
   int64_t cur = 0;
-  w.d_xr = cur;   cur = align256(cur + 2 * kDecodeRows * K);
-  w.d_xs = cur;   cur = align256(cur + 4 * (K / kGroup) * kDecodeRows);
-  w.d_tp = cur;   cur = align256(cur + 4 * (K / L.block) * kDecodeRows * nsp);
-  w.d_part = cur; cur = align256(cur + 4 * nchunk * kDecodeRows * N);
-  w.d_cnt = cur;  cur = align256(cur + 4 * decode_tiles(L.n_int4, L.n_int8));
+  w.d_xq = cur;   cur = align256(cur + 2 * kDecodeRows * K);
+  w.d_sc = cur;   cur = align256(cur + 4 * nunit * kDecodeRows);
+  w.d_tp = cur;   cur = align256(cur + 4 * nunit * kDecodeRows * nsp);
+  w.d_flag = cur; cur = align256(cur + 8 * nunit);
+  w.d_cnt = cur;  cur = align256(cur + 4 * (decode_groups(L.n_int4) + decode_groups(L.n_int8)));
+  w.d_part = cur; cur = align256(cur + 4 * int64_t(kMaxSplit) * kDecodeRows * N);
   w.d_end = cur;
   cur = 0;
   w.p_xr = cur;   cur = align256(cur + 2 * static_cast<int64_t>(L.M_max) * K);
+  w.p_sc = cur;   cur = align256(cur + 4 * static_cast<int64_t>(L.M_max));
   w.p_t = cur;    cur = align256(cur + 4 * static_cast<int64_t>(L.M_max) * nsp);
   w.p_end = cur;
   w.total = w.d_end > w.p_end ? w.d_end : w.p_end;
@@ -85,34 +152,38 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
 // ------------------------------------------------------------------ kernel arguments
 struct PrologueArgs {
   const uint16_t *x;   // bf16 [M][K]
-  uint16_t *xr;        // bf16 [rows][K] output (permuted or natural order)
-  float *xs;           // fp32 [K/64][32] group sums (decode) or null
+  uint16_t *xr;        // [M][K]: bf16 natural order, or f16 scaled, runs of 8 in order 0,4,1,5,2,6,3,7
+  float *sc;           // fp32 [M] 2^e per row (f16 output) or null
   const uint16_t *V;   // bf16 [nsr][K] or null (no t)
-  float *tp;           // fp32 [n_out][tp_rows][nsr_pad]: partial or full t
-  int *cnt_zero;       // int32 counters to clear (decode) or null
-  int n_cnt;
+  float *t;            // fp32 [M][nsr_pad] or null
   int M, K, nsr, nsr_pad;
-  int tp_rows;         // row stride count of tp (32 for decode, M_max for prefill)
   int blocks_per_wg;   // Hadamard blocks handled (and t-accumulated) by one workgroup
-  int permuted;        // 1: decode order of each 8-input run
-  int rotate;          // 0: x is already rotated (copy + sums + t only)
-  float scale;         // 1/sqrt(block)
+  int rotate;          // 0: x is already rotated (copy + t only)
+  int out_f16;         // 1: f16 scaled permuted output and sc; 0: bf16 natural
+  float hscale;        // 1/sqrt(block)
 };
 
 struct DecodeArgs {
+  // packed layer
   const uint8_t *q4;
   const uint16_t *s4;
   const int8_t *q8;
   const float *s8;
   const uint16_t *U;
+  const uint16_t *V;
   const int32_t *idx;
-  const uint16_t *xr;  // bf16 [32][K] permuted
-  const float *xs;     // fp32 [K/64][32]
-  const float *tp;     // fp32 [K/block][32][nsr_pad]
-  float *part;         // fp32 [nchunk][32][N]
-  int *cnt;            // int32 [n_tiles]
+  const uint16_t *x;   // bf16 [M][K]
+  // workspace
+  uint16_t *xq;        // f16 [32][K]
+  float *sc;           // fp32 [nunit][32]
+  float *tp;           // fp32 [nunit][32][nsr_pad]
+  uint64_t *flag;      // [nunit]
+  int *cnt;            // [g4 + g8]
+  float *part;         // fp32 [S][32][N]
   uint16_t *y;         // bf16 [M][N]
-  int N, K, r, n_seg, n4, n8, M, block, nsr, nsr_pad, nchunk, n4_tiles, n8_tiles;
+  uint64_t gen;        // generation stamp of this call
+  int N, K, r, n_seg, n4, n8, M, block, unit, nunit, nsr, nsr_pad, S, KW, g4, g8, rotate;
+  float hscale;        // 1/sqrt(block)
 };
 
 struct PrefillArgs {
@@ -122,7 +193,8 @@ struct PrefillArgs {
   const float *s8;
   const uint16_t *U;
   const int32_t *idx;
-  const uint16_t *xr;  // bf16 [M][K] natural
+  const uint16_t *xr;  // f16 [M][K] scaled per row, runs of 8 in order 0,4,1,5,2,6,3,7
+  const float *sc;     // fp32 [M] 2^e per row
   const float *t;      // fp32 [M][nsr_pad]
   uint16_t *y;         // bf16 [M][N]
   int N, K, r, n_seg, n4, n8, M, nsr, nsr_pad;
@@ -130,9 +202,9 @@ struct PrefillArgs {
 };
 
 // launchers (return hipError_t of the launch)
-hipError_t launch_prologue(const PrologueArgs &a, int block, int m_rows_per_wg, int n_wg_blocks,
-                           hipStream_t s);
+hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+size_t decode_lds_bytes(int M, int unit, int KW, int nsr_pad);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
 }  // namespace dvssq

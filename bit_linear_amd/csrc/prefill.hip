@@ -1,11 +1,13 @@
 // Prefill path (large M) of y = (x H) W_hat^T + ((x H) V^T) U^T
 // (MiniCPM5-2B-Hadamard-GSQ model card, Mathematical Foundations 2, runtime
-// equation).  A tiled GEMM on the bf16 matrix cores: x_rot tiles (bf16, from
-// the prologue) and weight tiles dequantized into LDS as bf16 -- INT4 rows as
-// (n - 8) * s_g (same card, INT4 equation), INT8 rows as the exact code q with
-// the fp32 row scale applied to the accumulator afterwards (Spark-X2.5-4B-
-// Hadamard-GSQ model card, Tier A).  The low-rank term is one more K-slab:
-// t (bf16) times the U rows of the tile.
+// equation).  A tiled GEMM on the f16 matrix cores: x_rot tiles (f16, scaled
+// by a power of two per row, from the prologue) and weight tiles dequantized
+// into LDS as exact f16 values -- INT4 rows as (n - 8) s_g (same card, INT4
+// equation), INT8 rows as the code q, whose fp32 row scale (Spark-X2.5-4B-
+// Hadamard-GSQ model card, Tier A) is applied to the accumulator afterwards.
+// Both operands hold each run of 8 inputs in the order 0,4,1,5,2,6,3,7, which
+// leaves the K-reduction unchanged.  The epilogue undoes the row scale, then
+// adds the low-rank term as one bf16 MFMA slab of t (bf16) times the U rows.
 #include "dvssq_internal.h"
 
 namespace dvssq {
@@ -13,42 +15,10 @@ namespace dvssq {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;          // padded LDS row, bf16 elements
+constexpr int LDK = BK + 8;          // padded LDS row, f16 elements
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
-// 32 INT4 codes (16 bytes, natural order) and scale s -> 32 bf16 (n - 8) * s, natural order
-__device__ __forceinline__ void dequant_int4(u32x4 w, float s, u32x4 (&out)[4]) {
-  const float ns8 = -8.0f * s;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t lo = w[d] & 0x0F0F0F0Fu;          // codes k = 8d + 0, 2, 4, 6
-    const uint32_t hi = (w[d] >> 4) & 0x0F0F0F0Fu;   // codes k = 8d + 1, 3, 5, 7
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = fmaf(static_cast<float>((lo >> (8 * i)) & 0xFFu), s, ns8);
-      const float b = fmaf(static_cast<float>((hi >> (8 * i)) & 0xFFu), s, ns8);
-      o[i] = pack_bf16x2(a, b);
-    }
-    out[d] = o;
-  }
-}
-
-// 16 INT8 codes -> 16 bf16 (exact), natural order
-__device__ __forceinline__ void int8_exact(u32x4 w, u32x4 (&out)[2]) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t v = w[d];
-    const float f0 = static_cast<float>(static_cast<int8_t>(v & 0xFFu));
-    const float f1 = static_cast<float>(static_cast<int8_t>((v >> 8) & 0xFFu));
-    const float f2 = static_cast<float>(static_cast<int8_t>((v >> 16) & 0xFFu));
-    const float f3 = static_cast<float>(static_cast<int8_t>(v >> 24));
-    out[d / 2][(d % 2) * 2] = pack_bf16x2(f0, f1);
-    out[d / 2][(d % 2) * 2 + 1] = pack_bf16x2(f2, f3);
-  }
-}
 
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
@@ -56,7 +26,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   uint16_t *Bs = lds + 2 * BM * LDK;        // [2][BN][LDK]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n_ntiles = a.n4_tiles + a.n8_tiles;
   const int ntile = blockIdx.x / a.m_tiles, mtile = blockIdx.x % a.m_tiles;
   const bool t8 = ntile >= a.n4_tiles;
   const int rows = t8 ? a.n8 : a.n4;
@@ -64,7 +33,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int m0 = mtile * BM;
   const int KG = a.K / kGroup;
   const int nk = KG;
-  (void)n_ntiles;
 
   // global -> register staging assignment
   const int a_row = tid >> 3, a_seg = tid & 7;         // A: rows a_row + 32 i, 16-byte segment a_seg
@@ -72,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const bool b_ok = p0l + b_row < rows;
 
   u32x4 ra[4], rb[2];
-  float rs = 0.0f;
+  uint32_t rs = 0;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
 
   auto gload = [&](int kt) {
@@ -84,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     }
     if (!t8) {
       rb[0] = b_ok ? ld16(a.q4 + static_cast<int64_t>(p0l + b_row) * (a.K / 2) + k0 / 2 + 16 * b_half) : z4;
-      rs = b_ok ? bf16_to_f32(a.s4[static_cast<int64_t>(p0l + b_row) * KG + kt]) : 0.0f;
+      rs = b_ok ? a.s4[static_cast<int64_t>(p0l + b_row) * KG + kt] : 0u;
     } else {
       const int8_t *src = a.q8 + static_cast<int64_t>(p0l + b_row) * a.K + k0 + 32 * b_half;
       rb[0] = b_ok ? ld16(src) : z4;
@@ -98,18 +66,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(as + (a_row + 32 * i) * LDK + 8 * a_seg) = ra[i];
     uint16_t *dst = bs + b_row * LDK + 32 * b_half;
     if (!t8) {
-      u32x4 o[4];
-      dequant_int4(rb[0], rs, o);
+      const float s = bf16_to_f32(rs);
+      const uint32_t s2 = pack_f16x2(s, s), c24 = pack_f16x2(-24.0f * s, -24.0f * s);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4 *>(dst + 8 * d) = o[d];
+      for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4 *>(dst + 8 * d) = int4_to_f16(rb[0][d], s2, c24);
     } else {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        u32x4 o[2];
-        int8_exact(rb[s], o);
-        *reinterpret_cast<u32x4 *>(dst + 16 * s) = o[0];
-        *reinterpret_cast<u32x4 *>(dst + 16 * s + 8) = o[1];
-      }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          *reinterpret_cast<u32x4 *>(dst + 16 * h + 8 * e) = int8_to_f16(rb[h][2 * e], rb[h][2 * e + 1]);
     }
   };
 
@@ -140,25 +106,31 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16_f16(af[i], bf[j], acc[i][j]);
     }
     if (kt + 1 < nk) sstore(cur ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: INT8 row scale, low-rank slab, bf16 scatter through idx
+  // ---- epilogue: row scale 2^e, INT8 row scale, low-rank slab, bf16 scatter through idx
+  float rsc[2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + 64 * wm + 32 * i + 8 * (v / 4) + 4 * fh + (v % 4);
+      rsc[i][v] = (m < a.M) ? a.sc[m] : 0.0f;
+    }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int pl = p0l + 64 * wn + 32 * j + fr;
     const bool ok = pl < rows;
     const int p = (t8 ? a.n4 : 0) + pl;
-    if (t8) {
-      const float s8 = ok ? a.s8[pl] : 0.0f;
+    const float s8 = (t8 && ok) ? a.s8[pl] : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] *= s8;
-    }
+      for (int v = 0; v < 16; ++v) acc[i][j][v] *= rsc[i][v] * s8;
     const int seg = ok ? a.idx[p] / (a.N / a.n_seg) : 0;
     for (int js = 0; js < a.nsr_pad / 16; ++js) {
       u32x4 bv;
@@ -214,8 +186,5 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
-
-int prefill_tile_m() { return BM; }
-int prefill_tile_n() { return BN; }
 
 }  // namespace dvssq

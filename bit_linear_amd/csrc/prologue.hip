@@ -1,5 +1,5 @@
-// Activation side of the DV-SSQ layer: x_rot = x H_K, the decode group sums of
-// x_rot, and t = x_rot V^T.
+// Activation side of the DV-SSQ layer for dvssq_fwht and the prefill path:
+// x_rot = x H_K and t = x_rot V^T.
 //
 // Rotation: MiniCPM5-2B-Hadamard-GSQ model card, Mathematical Foundations 1
 // (X' = X H, Sylvester H) and Spark-X2.5-4B-Hadamard-GSQ model card, Tier B
@@ -8,11 +8,15 @@
 //
 // One workgroup = 4 wavefronts handles MT activation rows and a run of
 // Hadamard blocks.  Each row of a block is rotated by one wavefront with the
-// fast Walsh-Hadamard transform: V = block/64 consecutive values per lane,
-// log2(V) butterfly stages inside the lane's registers, then 6 stages across
-// lanes (xor 1..32).  The bf16-rounded block is staged in LDS, copied out in
-// the order the consumer wants, and multiplied by V^T on the matrix cores
-// (32x32x16 bf16 MFMA), accumulating t over the workgroup's blocks.
+// fast Walsh-Hadamard transform: VPL = block/64 consecutive values per lane,
+// log2(VPL) butterfly stages in registers, then the stages across lanes (xor
+// 1..32).  The fp32 block is staged in LDS and copied out either as bf16 in
+// natural order (dvssq_fwht), or -- for the prefill GEMM -- as f16 scaled by
+// a power of two per row and stored in runs of 8 in the order 0,4,1,5,2,6,3,7
+// (the order the weight decoder produces).  The row's exponent comes from the
+// bound max|x H| <= sqrt(block) max|x|, so the scaled values stay below 2^15.
+// t is accumulated on the matrix cores (32x32x16 bf16 MFMA) over the
+// workgroup's blocks.
 #include "dvssq_internal.h"
 
 namespace dvssq {
@@ -70,8 +74,10 @@ __device__ __forceinline__ void fwht_wave(float (&v)[VPL], int lane) {
 template <int VPL, int MT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   constexpr int B = 64 * VPL;
-  constexpr int LDSR = B + 8;  // padded LDS row (bf16 elements)
-  extern __shared__ __align__(16) uint16_t lds[];
+  constexpr int LDR = B + 4;  // padded LDS row (fp32)
+  constexpr int LOG2_SQRT_B = (__builtin_ctz(B) + 1) / 2;
+  extern __shared__ __align__(16) float lds[];
+  __shared__ int rowexp[MT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.x * MT;
   const int nblk = a.K / B;
@@ -81,8 +87,28 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   const bool want_t = a.nsr > 0;
   const int n_it = (a.nsr_pad + 31) / 32;
 
-  if (a.cnt_zero != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = tid; i < a.n_cnt; i += kThreads) a.cnt_zero[i] = 0;
+  // 0. per-row power-of-two scale (f16 output only)
+  if (a.out_f16) {
+    for (int ml = wave; ml < MT; ml += 4) {
+      float mx = 0.0f;
+      if (ml < mrows)
+        for (int blk = b0; blk < b1; ++blk) {
+          float v[VPL];
+          load_row<VPL>(a.x + static_cast<int64_t>(m0 + ml) * a.K + blk * B + lane * VPL, v);
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) mx = fmaxf(mx, fabsf(v[j]));
+        }
+#pragma unroll
+      for (int s = 1; s < 64; s <<= 1) mx = fmaxf(mx, __shfl_xor(mx, s, 64));
+      int e = 0;
+      if (mx > 0.0f && mx <= 3.0e38f) e = max(-120, min(120, ilogbf(mx) + (a.rotate ? LOG2_SQRT_B : 0) + 1 - 15));
+      if (lane == 0) {
+        rowexp[ml] = e;
+        if (ml < mrows) a.sc[m0 + ml] = ldexpf(1.0f, e);
+      }
+    }
+    __syncthreads();
+  }
 
   f32x16 acc[2];
 #pragma unroll
@@ -92,69 +118,53 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
 
   for (int blk = b0; blk < b1; ++blk) {
     const int kb = blk * B;
-    // 1. rotate each row of this block (one wavefront per row), stage bf16 in LDS
+    // 1. rotate each row of this block (one wavefront per row), stage fp32 in LDS
     for (int ml = wave; ml < MT; ml += 4) {
-      uint16_t *row = lds + ml * LDSR + lane * VPL;
+      float *row = lds + ml * LDR + lane * VPL;
       if (ml < mrows) {
         float v[VPL];
         load_row<VPL>(a.x + static_cast<int64_t>(m0 + ml) * a.K + kb + lane * VPL, v);
         if (a.rotate) {
           fwht_wave<VPL>(v, lane);
 #pragma unroll
-          for (int j = 0; j < VPL; ++j) v[j] *= a.scale;
+          for (int j = 0; j < VPL; ++j) v[j] *= a.hscale;
         }
 #pragma unroll
-        for (int j = 0; j < VPL; j += 2) {
-          if constexpr (VPL >= 2) {
-            *reinterpret_cast<uint32_t *>(row + j) = pack_bf16x2(v[j], v[j + 1]);
-          } else {
-            row[j] = f32_to_bf16(v[j]);
-          }
-        }
+        for (int j = 0; j < VPL; ++j) row[j] = v[j];
       } else {
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) row[j] = 0;
+        for (int j = 0; j < VPL; ++j) row[j] = 0.0f;
       }
     }
     __syncthreads();
-    // 2. copy out in runs of 8 (decode order 0,4,1,5,2,6,3,7 when permuted), and group sums
+    // 2. copy out in runs of 8
     constexpr int RUNS = B / 8;
-    for (int e = tid; e < MT * RUNS; e += kThreads) {
+    for (int e = tid; e < mrows * RUNS; e += kThreads) {
       const int ml = e / RUNS, run = e % RUNS;
-      const u32x4 w = *reinterpret_cast<const u32x4 *>(lds + ml * LDSR + run * 8);
-      float gsum = 0.0f;
-      if (a.xs != nullptr) {
+      const float *w = lds + ml * LDR + run * 8;
+      u32x4 o;
+      if (a.out_f16) {
+        const float d = ldexpf(1.0f, -rowexp[ml]);
+        o[0] = pack_f16x2(w[0] * d, w[4] * d);
+        o[1] = pack_f16x2(w[1] * d, w[5] * d);
+        o[2] = pack_f16x2(w[2] * d, w[6] * d);
+        o[3] = pack_f16x2(w[3] * d, w[7] * d);
+      } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          gsum += __uint_as_float(w[q] << 16) + __uint_as_float(w[q] & 0xFFFF0000u);
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
       }
-      if (ml < mrows) {
-        u32x4 o = w;
-        if (a.permuted) {
-          // natural halves: w[q] = (e_{2q}, e_{2q+1});  want (e0,e4),(e1,e5),(e2,e6),(e3,e7)
-          const uint32_t lo = 0xFFFFu;
-          o[0] = (w[0] & lo) | (w[2] << 16);
-          o[1] = (w[0] >> 16) | (w[2] & ~lo);
-          o[2] = (w[1] & lo) | (w[3] << 16);
-          o[3] = (w[1] >> 16) | (w[3] & ~lo);
-        }
-        *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) = o;
-      }
-      if (a.xs != nullptr) {
-        // 8 consecutive runs form one group of 64; they sit in 8 consecutive lanes
-        gsum += __shfl_xor(gsum, 1, 64);
-        gsum += __shfl_xor(gsum, 2, 64);
-        gsum += __shfl_xor(gsum, 4, 64);
-        if ((run & 7) == 0 && ml < mrows)
-          a.xs[static_cast<int64_t>((kb + run * 8) / kGroup) * kDecodeRows + m0 + ml] = gsum;
-      }
+      *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) = o;
     }
     // 3. t += x_rot(block) V(block)^T on the matrix cores; K-steps of 16 split over the waves
     if (want_t) {
       const int arow = lane & 31, half = lane >> 5;
       for (int s = wave; s < B / 16; s += 4) {
         u32x4 av = {0u, 0u, 0u, 0u};
-        if (arow < MT) av = *reinterpret_cast<const u32x4 *>(lds + arow * LDSR + 16 * s + 8 * half);
+        if (arow < MT) {
+          const float *w = lds + arow * LDR + 16 * s + 8 * half;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) av[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
+        }
         for (int it = 0; it < n_it; ++it) {
           const int i = 32 * it + arow;
           u32x4 bv = {0u, 0u, 0u, 0u};
@@ -169,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   }
   if (!want_t) return;
   // 4. reduce the four waves' partial t and write it out
-  float *red = reinterpret_cast<float *>(lds);  // [4 waves][2 it][32 m][32 i]
+  float *red = lds;  // [4 waves][2 it][32 m][32 i]
   {
     const int col = lane & 31, half = lane >> 5;
     for (int it = 0; it < n_it; ++it)
@@ -185,14 +195,14 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) s += red[((w * 2 + i / 32) * 32 + ml) * 32 + (i % 32)];
-    a.tp[(static_cast<int64_t>(blockIdx.y) * a.tp_rows + m0 + ml) * a.nsr_pad + i] = s;
+    a.t[static_cast<int64_t>(m0 + ml) * a.nsr_pad + i] = s;
   }
 }
 
 template <int VPL, int MT>
 hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
   constexpr int B = 64 * VPL;
-  const size_t lds_rows = static_cast<size_t>(MT) * (B + 8) * 2;
+  const size_t lds_rows = static_cast<size_t>(MT) * (B + 4) * 4;
   const size_t lds_red = 4 * 2 * 32 * 32 * 4;
   const size_t lds = lds_rows > lds_red ? lds_rows : lds_red;
   if (lds > 65536) {
@@ -212,19 +222,16 @@ hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_prologue(const PrologueArgs &a, int block, int /*m_rows_per_wg*/,
-                           int n_wg_blocks, hipStream_t s) {
+hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hipStream_t s) {
   switch (block) {
     case 64: return launch_vpl<1, 32>(a, n_wg_blocks, s);
     case 128: return launch_vpl<2, 32>(a, n_wg_blocks, s);
     case 256: return launch_vpl<4, 32>(a, n_wg_blocks, s);
     case 512: return launch_vpl<8, 32>(a, n_wg_blocks, s);
-    case 1024: return launch_vpl<16, 32>(a, n_wg_blocks, s);
+    case 1024: return launch_vpl<16, 16>(a, n_wg_blocks, s);
     case 2048: return launch_vpl<32, 16>(a, n_wg_blocks, s);
     default: return hipErrorInvalidValue;
   }
 }
-
-int prologue_rows_per_wg(int block) { return block == 2048 ? 16 : 32; }
 
 }  // namespace dvssq

@@ -104,12 +104,18 @@ int dvssq_pack_info(int32_t N, int32_t K, int32_t r, int32_t block, int32_t n_se
 int dvssq_fwht(const void *x, void *xrot, int32_t M, int32_t K, int32_t block, void *stream);
 
 /*
- * Decode forward (memory-bound GEMV path), 1 <= M <= min(32, L->M_max).
+ * Decode forward (memory-bound GEMV path), 1 <= M <= min(32, L->M_max), one
+ * kernel launch.  Needs K to be a multiple of max(block, 256)
+ * (DVSSQ_EUNSUPPORTED otherwise).
  * L: from dvssq_pack_info.  blob: device, L->blob_bytes, 256-byte aligned.
  * x: device bf16 [M][K] (x.H when flags has DVSSQ_X_ROTATED).  y: device bf16
  * [M][N] in original column order; y must not overlap x, blob or ws.
  * ws: device workspace of L->ws_bytes, 256-byte aligned, contents need no
  * initialization; one ws must not be used by two calls in flight at once.
+ * The rotated activations are held in f16 with a power-of-two scale per row
+ * and per max(block, 256) inputs (no overflow for finite fp32 values), the
+ * weights as exact f16 values; accumulation is fp32.  Decode needs the INT4
+ * scales s4 to lie in [2^-14, 63] for exact f16 weights.
  * x and y must be 16-byte aligned.  Accumulation is fp32; y is rounded once to
  * bf16 (nearest-even).
  */
@@ -117,10 +123,12 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
                         int32_t M, void *ws, uint32_t flags, void *stream);
 
 /*
- * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max.  Same arguments and
- * ownership rules as dvssq_linear_decode.  The rotated activations, the
- * dequantized weights and t = (x H) V^T are rounded to bf16 before the matrix
- * cores; accumulation is fp32.
+ * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: two kernel launches
+ * (rotation + t, then the GEMM).  Same arguments and ownership rules as
+ * dvssq_linear_decode.  The rotated activations are held in f16 with one
+ * power-of-two scale per row, the weights as exact f16 values (same s4 range
+ * as decode), t = (x H) V^T in bf16 for the low-rank product; accumulation is
+ * fp32.
  */
 int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x, void *y,
                          int32_t M, void *ws, uint32_t flags, void *stream);

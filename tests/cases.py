@@ -29,9 +29,11 @@ LAYERS = all_layers()
 
 # small shapes that exercise tails and corner parameters
 EXTRA = {
-    "ragged_b64_r1": synth.Layer("ragged_b64_r1", N=520, K=192, block=64, r=1, n_outlier=2,
+    "ragged_b64_r1": synth.Layer("ragged_b64_r1", N=520, K=768, block=64, r=1, n_outlier=8,
                                  outlier_tag="ragged_b64"),
-    "b128_r64": synth.Layer("b128_r64", N=96, K=128, block=128, r=64, n_outlier=1,
+    "k192_b64": synth.Layer("k192_b64", N=136, K=192, block=64, r=3, n_outlier=2,
+                            outlier_tag="k192"),
+    "b128_r64": synth.Layer("b128_r64", N=96, K=256, block=128, r=64, n_outlier=3,
                             outlier_tag="b128"),
     "seg2_b512_r32": synth.Layer("seg2_b512_r32", N=2 * 264, K=512, block=512, r=32, n_seg=2,
                                  n_outlier=5, outlier_tag="seg2_b512"),

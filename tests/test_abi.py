@@ -128,6 +128,12 @@ def test_decode_rejects_large_m():
     assert call("dvssq_linear_decode", L, M=33) == dv.DVSSQ_EUNSUPPORTED
 
 
+def test_decode_needs_k_multiple_of_unit():
+    # decode works on units of max(block, 256) inputs; prefill has no such limit
+    L = dv.pack_info(136, 192, 3, 64, 1, M_max=64)
+    assert call("dvssq_linear_decode", L, M=1) == dv.DVSSQ_EUNSUPPORTED
+
+
 def test_fwht_error_paths():
     f = dv.lib().dvssq_fwht
     assert f(None, Y, 4, 256, 256, None) == dv.DVSSQ_EINVAL
