@@ -86,17 +86,25 @@ uint64_t next_generation() {
   return g;
 }
 
-// Split-K factor of the decode kernel: the smallest S (dividing K/64, at most
-// kMaxSplit) that gives >= 160 consumer workgroups while the LDS copy of the
-// rotated activations (M rows x K/S inputs, f16) stays within 96 KB.
-int decode_split(int K, int groups, int M) {
-  const int nchunk = K / DVSSQ_GROUP;
-  int best = 1;
-  for (int S = 1; S <= kMaxSplit && S <= nchunk; ++S) {
-    if (nchunk % S) continue;
-    const int64_t lds = static_cast<int64_t>(M) * (K / S + 8) * 2;
+// Split-K factor of the decode kernel: S equal parts of K, each a multiple of
+// 128 inputs (so no 128-input span crosses a rotation unit) and at most
+// decode_max_spans() spans, whose on-chip staging fits in LDS.  The smallest
+// such S that gives >= 512 consumer workgroups within 80 KB of LDS (two
+// workgroups per compute unit); failing that, the largest such S (LDS use
+// falls as S grows).  0 when no S fits.
+// Largest M decoded in one launch (producers and consumers together); larger
+// M uses a separate rotation launch first.
+constexpr int kDecodeFusedMaxM = 32;
+
+int decode_split(int K, int groups, int M, int unit, int nsr_pad) {
+  const int nspan = K / 128;
+  int best = 0;
+  for (int S = 1; S <= kMaxSplit && S <= nspan; ++S) {
+    if (nspan % S || nspan / S > decode_max_spans()) continue;
+    const size_t lds = decode_lds_bytes(M, unit, K / S, nsr_pad);
+    if (lds > 160 * 1024) continue;
+    if (lds <= 80 * 1024 && static_cast<int64_t>(groups) * S >= 512) return S;
     best = S;
-    if (lds <= 96 * 1024 && static_cast<int64_t>(groups) * S >= 160) return S;
   }
   return best;
 }
@@ -180,6 +188,9 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   if (rc != DVSSQ_OK) return rc;
   if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
   if (L->K % decode_unit(L->block) != 0) return DVSSQ_EUNSUPPORTED;
+  const int g4 = decode_groups(L->n_int4), g8 = decode_groups(L->n_int8);
+  const int S = decode_split(L->K, g4 + g8, M, decode_unit(L->block), nsr_pad_of(L->n_seg, L->r));
+  if (S == 0) return DVSSQ_EUNSUPPORTED;
   const WsLayout W = ws_layout(*L);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   const Blob B{static_cast<const uint8_t *>(blob), L};
@@ -210,13 +221,15 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.block = L->block;
   d.unit = decode_unit(L->block);
   d.nunit = L->K / d.unit;
+  d.nprod = decode_producers(d.nunit, M);
   d.nsr = L->n_seg * L->r;
   d.nsr_pad = nsr_pad_of(L->n_seg, L->r);
-  d.g4 = decode_groups(L->n_int4);
-  d.g8 = decode_groups(L->n_int8);
-  d.S = decode_split(L->K, d.g4 + d.g8, M);
+  d.g4 = g4;
+  d.g8 = g8;
+  d.S = S;
   d.KW = L->K / d.S;
   d.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
+  d.fused = M <= kDecodeFusedMaxM ? 1 : 0;
   d.hscale = inv_sqrt_block(L->block);
   const hipError_t e = launch_decode(d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;

@@ -21,7 +21,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 64;      // INT4 group size
 constexpr int kDecodeRows = 32; // M rows held by the decode workspace (MFMA tile height)
-constexpr int kChunk = 256;     // decode split-K chunk (inputs), 4 groups
 
 // ------------------------------------------------------------------ scalar helpers
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
@@ -50,8 +49,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16_f16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                 0, 0, 0);
 }
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
@@ -73,8 +70,9 @@ __device__ __forceinline__ uint32_t pk_fma(uint32_t a, uint32_t b, uint32_t c) {
 __device__ __forceinline__ uint32_t pk_add(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) + __builtin_bit_cast(f16x2, b));
 }
-// 8 INT4 codes (one dword, natural order) -> 8 exact f16 (n - 8) s, slots k+0,4,1,5,2,6,3,7.
-// Each nibble pair is moved to bits 6-9 of the two halves; or-ed with 0x4C00
+// One dword of packed INT4 codes (byte j: code k+j low, k+j+4 high) -> 8 exact
+// f16 (n - 8) s in slots k+0,2,4,6,1,3,5,7.  Each nibble pair is moved to bits
+// 6-9 of the two halves; or-ed with 0x4C00
 // that is the f16 value 16 + n.  With s = m 2^E (m < 256), -24 s = -3m 2^(E+3)
 // has at most 10 significant bits and (n - 8) s at most 11, so the fused
 // fma(16 + n, s, -24 s) returns (n - 8) s exactly.
@@ -88,15 +86,14 @@ __device__ __forceinline__ u32x4 int4_to_f16(uint32_t w, uint32_t s2, uint32_t c
   return r;
 }
 
-// 8 INT8 codes (k+0..3 in lo, k+4..7 in hi) -> 8 exact f16 q, slots k+0,4,1,5,2,6,3,7
+// 8 INT8 codes (k+0..3 in lo, k+4..7 in hi) -> 8 exact f16 q, slots k+0,2,4,6,1,3,5,7
 __device__ __forceinline__ u32x4 int8_to_f16(uint32_t lo, uint32_t hi) {
   const uint32_t m1152 = 0xE480E480u;  // f16 -1152 twice
+  // byte pairs (k0,k2) (k4,k6) (k1,k3) (k5,k7); selector bytes 0-3 pick lo, 4-7 hi, 0x0C zero
+  const uint32_t sel[4] = {0x0C020C00u, 0x0C060C04u, 0x0C030C01u, 0x0C070C05u};
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t sel = 0x0C000C00u | ((4u + i) << 16) | static_cast<uint32_t>(i);
-    r[i] = pk_add(__builtin_amdgcn_perm(hi, lo, sel) ^ 0x64806480u, m1152);
-  }
+  for (int i = 0; i < 4; ++i) r[i] = pk_add(__builtin_amdgcn_perm(hi, lo, sel[i]) ^ 0x64806480u, m1152);
   return r;
 }
 
@@ -107,11 +104,11 @@ constexpr int kMaxSplit = 16;   // largest decode split-K factor
 
 struct WsLayout {
   // decode
-  int64_t d_xq;    // f16 [32][K]: rotated x scaled by 2^-e per (row, unit), runs of 8 in order 0,4,1,5,2,6,3,7
+  int64_t d_xq;    // f16 [32][K]: rotated x scaled by 2^-e per (row, unit), runs of 8 in order 0,2,4,6,1,3,5,7
   int64_t d_sc;    // fp32 [nunit][32]: 2^e of each (unit, row)
   int64_t d_tp;    // fp32 [nunit][32][nsr_pad]: partial t = x_rot V^T of each unit
-  int64_t d_flag;  // u64 [nunit]: generation stamp written by the unit's producer
-  int64_t d_cnt;   // int32 [groups]: split-K arrivals per 64-row group
+  int64_t d_flag;  // u64 [nunit * 4]: generation stamp written by each producer
+  int64_t d_cnt;   // int32 [groups]: split-K arrivals per 16-row group
   int64_t d_part;  // fp32 [kMaxSplit][32][N]: split-K partial outputs
   int64_t d_end;
   // prefill
@@ -125,7 +122,8 @@ struct WsLayout {
 inline int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 inline int nsr_pad_of(int n_seg, int r) { return (n_seg * r + 31) / 32 * 32; }
 inline int decode_unit(int block) { return block > 256 ? block : 256; }
-inline int decode_groups(int n) { return (n + 63) / 64; }
+inline int decode_groups(int n) { return (n + 15) / 16; }   // 16 packed rows per consumer group
+inline int decode_producers(int nunit, int M) { return nunit * ((M + 7) / 8); }
 
 inline WsLayout ws_layout(const dvssq_layout &L) {
   WsLayout w{};
@@ -136,7 +134,7 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
   w.d_xq = cur;   cur = align256(cur + 2 * kDecodeRows * K);
   w.d_sc = cur;   cur = align256(cur + 4 * nunit * kDecodeRows);
   w.d_tp = cur;   cur = align256(cur + 4 * nunit * kDecodeRows * nsp);
-  w.d_flag = cur; cur = align256(cur + 8 * nunit);
+  w.d_flag = cur; cur = align256(cur + 8 * decode_producers(nunit, kDecodeRows));
   w.d_cnt = cur;  cur = align256(cur + 4 * (decode_groups(L.n_int4) + decode_groups(L.n_int8)));
   w.d_part = cur; cur = align256(cur + 4 * int64_t(kMaxSplit) * kDecodeRows * N);
   w.d_end = cur;
@@ -152,7 +150,7 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
 // ------------------------------------------------------------------ kernel arguments
 struct PrologueArgs {
   const uint16_t *x;   // bf16 [M][K]
-  uint16_t *xr;        // [M][K]: bf16 natural order, or f16 scaled, runs of 8 in order 0,4,1,5,2,6,3,7
+  uint16_t *xr;        // [M][K]: bf16 natural order, or f16 scaled, runs of 8 in order 0,2,4,6,1,3,5,7
   float *sc;           // fp32 [M] 2^e per row (f16 output) or null
   const uint16_t *V;   // bf16 [nsr][K] or null (no t)
   float *t;            // fp32 [M][nsr_pad] or null
@@ -177,12 +175,13 @@ struct DecodeArgs {
   uint16_t *xq;        // f16 [32][K]
   float *sc;           // fp32 [nunit][32]
   float *tp;           // fp32 [nunit][32][nsr_pad]
-  uint64_t *flag;      // [nunit]
+  uint64_t *flag;      // [nprod]
   int *cnt;            // [g4 + g8]
   float *part;         // fp32 [S][32][N]
   uint16_t *y;         // bf16 [M][N]
   uint64_t gen;        // generation stamp of this call
-  int N, K, r, n_seg, n4, n8, M, block, unit, nunit, nsr, nsr_pad, S, KW, g4, g8, rotate;
+  int N, K, r, n_seg, n4, n8, M, block, unit, nunit, nprod, nsr, nsr_pad, S, KW, g4, g8, rotate;
+  int fused;           // 1: producers and consumers in one launch; 0: two launches
   float hscale;        // 1/sqrt(block)
 };
 
@@ -193,7 +192,7 @@ struct PrefillArgs {
   const float *s8;
   const uint16_t *U;
   const int32_t *idx;
-  const uint16_t *xr;  // f16 [M][K] scaled per row, runs of 8 in order 0,4,1,5,2,6,3,7
+  const uint16_t *xr;  // f16 [M][K] scaled per row, runs of 8 in order 0,2,4,6,1,3,5,7
   const float *sc;     // fp32 [M] 2^e per row
   const float *t;      // fp32 [M][nsr_pad]
   uint16_t *y;         // bf16 [M][N]
@@ -205,6 +204,7 @@ struct PrefillArgs {
 hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 size_t decode_lds_bytes(int M, int unit, int KW, int nsr_pad);
+int decode_max_spans();   // most 128-input spans one decode workgroup takes
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
 }  // namespace dvssq

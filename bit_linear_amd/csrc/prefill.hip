@@ -5,7 +5,7 @@
 // into LDS as exact f16 values -- INT4 rows as (n - 8) s_g (same card, INT4
 // equation), INT8 rows as the code q, whose fp32 row scale (Spark-X2.5-4B-
 // Hadamard-GSQ model card, Tier A) is applied to the accumulator afterwards.
-// Both operands hold each run of 8 inputs in the order 0,4,1,5,2,6,3,7, which
+// Both operands hold each run of 8 inputs in the order 0,2,4,6,1,3,5,7, which
 // leaves the K-reduction unchanged.  The epilogue undoes the row scale, then
 // adds the low-rank term as one bf16 MFMA slab of t (bf16) times the U rows.
 #include "dvssq_internal.h"

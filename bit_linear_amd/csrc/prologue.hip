@@ -12,7 +12,7 @@
 // log2(VPL) butterfly stages in registers, then the stages across lanes (xor
 // 1..32).  The fp32 block is staged in LDS and copied out either as bf16 in
 // natural order (dvssq_fwht), or -- for the prefill GEMM -- as f16 scaled by
-// a power of two per row and stored in runs of 8 in the order 0,4,1,5,2,6,3,7
+// a power of two per row and stored in runs of 8 in the order 0,2,4,6,1,3,5,7
 // (the order the weight decoder produces).  The row's exponent comes from the
 // bound max|x H| <= sqrt(block) max|x|, so the scaled values stay below 2^15.
 // t is accumulated on the matrix cores (32x32x16 bf16 MFMA) over the
@@ -145,10 +145,10 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
       u32x4 o;
       if (a.out_f16) {
         const float d = ldexpf(1.0f, -rowexp[ml]);
-        o[0] = pack_f16x2(w[0] * d, w[4] * d);
-        o[1] = pack_f16x2(w[1] * d, w[5] * d);
-        o[2] = pack_f16x2(w[2] * d, w[6] * d);
-        o[3] = pack_f16x2(w[3] * d, w[7] * d);
+        o[0] = pack_f16x2(w[0] * d, w[2] * d);
+        o[1] = pack_f16x2(w[4] * d, w[6] * d);
+        o[2] = pack_f16x2(w[1] * d, w[3] * d);
+        o[3] = pack_f16x2(w[5] * d, w[7] * d);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);

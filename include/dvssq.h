@@ -31,9 +31,11 @@
  * rows that read the same x), each in ascending original output index.
  *   idx  int32 [N]            packed row p -> original output column idx[p];
  *                             its segment is idx[p] / (N / n_seg)
- *   q4   uint8 [n_int4][K/2]  byte j of a row: code of input 2j in the low
- *                             nibble, of input 2j+1 in the high nibble; nibble
- *                             = q + 8 with q in [-8, 7]
+ *   q4   uint8 [n_int4][K/2]  each run of 8 inputs k = 8i .. 8i+7 of a row
+ *                             fills the 4 bytes 4i .. 4i+3: byte 4i+j holds the
+ *                             code of input 8i+j in its low nibble and that of
+ *                             input 8i+j+4 in its high nibble; nibble = q + 8
+ *                             with q in [-8, 7]
  *   s4   bf16  [n_int4][K/64] scale of inputs 64g .. 64g+63
  *   q8   int8  [n_int8][K]    two's complement q in [-128, 127]
  *   s8   fp32  [n_int8]       per-row scale

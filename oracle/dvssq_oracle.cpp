@@ -38,7 +38,9 @@
 // INT4 tier first, then INT8 tier; inside a tier segment 0's rows then
 // segment 1's, each in ascending original index:
 //   idx  int32 [N]           packed row -> original output column
-//   q4   uint8 [N4][K/2]     byte j: code k=2j in the low nibble, 2j+1 high;
+//   q4   uint8 [N4][K/2]     each run of 8 codes k = 8i .. 8i+7 fills the 4
+//                            bytes 4i .. 4i+3: byte 4i+j holds code 8i+j in
+//                            the low nibble and 8i+j+4 in the high nibble;
 //                            nibble = q + 8
 //   s4   bf16  [N4][K/64]
 //   q8   int8  [N8][K]
@@ -406,7 +408,8 @@ struct Packed {
       const uint8_t *c = q4() + p * (K / 2);
       const uint16_t *s = s4() + p * (K / kGroup);
       for (int64_t k = 0; k < K; ++k) {
-        const int nib = (k & 1) ? (c[k >> 1] >> 4) : (c[k >> 1] & 0xF);
+        const uint8_t byte = c[4 * (k / 8) + (k % 4)];
+        const int nib = (k % 8 >= 4) ? (byte >> 4) : (byte & 0xF);
         w[k] = static_cast<double>(nib - 8) * double_from_bf16(s[k / kGroup]);
       }
     } else {
@@ -578,8 +581,9 @@ int orc_quantize(const uint16_t *W, int N, int K, int r, int b, int n_seg, const
         uint16_t *sg = s4 + p * (K / kGroup);
         quant_int4_row(w, K, q.data(), sg);
         uint8_t *c = q4 + p * (K / 2);
-        for (int64_t k = 0; k < K; k += 2)
-          c[k / 2] = static_cast<uint8_t>(((q[k] + 8) & 0xF) | (((q[k + 1] + 8) & 0xF) << 4));
+        for (int64_t k = 0; k < K; k += 8)
+          for (int j = 0; j < 4; ++j)
+            c[k / 2 + j] = static_cast<uint8_t>(((q[k + j] + 8) & 0xF) | (((q[k + j + 4] + 8) & 0xF) << 4));
         for (int64_t k = 0; k < K; ++k)
           R[n * K + k] = w[k] - static_cast<double>(q[k]) * double_from_bf16(sg[k / kGroup]);
       }

@@ -271,9 +271,8 @@ def _decode_blob_numpy(blob, N, K, r, n_seg):
     n4, n8 = L["N4"], L["N8"]
     idx = blob[L["off_idx"]:L["off_idx"] + 4 * N].view(np.int32)
     q4 = blob[L["off_q4"]:L["off_q4"] + n4 * K // 2].reshape(n4, K // 2)
-    codes = np.empty((n4, K), dtype=np.int64)
-    codes[:, 0::2] = (q4 & 0xF).astype(np.int64) - 8
-    codes[:, 1::2] = (q4 >> 4).astype(np.int64) - 8
+    runs = q4.reshape(n4, K // 8, 4)      # 4 bytes per run of 8 codes
+    codes = np.concatenate([(runs & 0xF), (runs >> 4)], axis=2).astype(np.int64).reshape(n4, K) - 8
     s4 = synth.bf16_bits_to_f64(blob[L["off_s4"]:L["off_s4"] + 2 * n4 * K // 64].view(np.uint16)).reshape(n4, K // 64)
     q8 = blob[L["off_q8"]:L["off_q8"] + n8 * K].view(np.int8).reshape(n8, K).astype(np.float64)
     s8 = blob[L["off_s8"]:L["off_s8"] + 4 * n8].view(np.float32).astype(np.float64)
