@@ -92,6 +92,10 @@ uint64_t next_generation() {
 // such S that gives >= 512 consumer workgroups within 80 KB of LDS (two
 // workgroups per compute unit); failing that, the largest such S (LDS use
 // falls as S grows).  0 when no S fits.
+// Largest M decoded by the small-M kernel (int8 matrix cores, 16-wavefront
+// consumer workgroups).
+constexpr int kSmallMaxM = 4;
+
 // Largest M decoded in one launch (producers and consumers together); larger
 // M uses a separate rotation launch first.
 constexpr int kDecodeFusedMaxM = 32;
@@ -189,7 +193,10 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
   if (L->K % decode_unit(L->block) != 0) return DVSSQ_EUNSUPPORTED;
   const int g4 = decode_groups(L->n_int4), g8 = decode_groups(L->n_int8);
-  const int S = decode_split(L->K, g4 + g8, M, decode_unit(L->block), nsr_pad_of(L->n_seg, L->r));
+  const int unit = decode_unit(L->block), nsp = nsr_pad_of(L->n_seg, L->r);
+  SmallPlan sp{};
+  const bool small = M <= kSmallMaxM && plan_decode_small(*L, M, &sp);
+  const int S = small ? sp.S : decode_split(L->K, g4 + g8, M, unit, nsp);
   if (S == 0) return DVSSQ_EUNSUPPORTED;
   const WsLayout W = ws_layout(*L);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
@@ -209,8 +216,15 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.flag = reinterpret_cast<uint64_t *>(wsb + W.d_flag);
   d.cnt = reinterpret_cast<int *>(wsb + W.d_cnt);
   d.part = reinterpret_cast<float *>(wsb + W.d_part);
+  d.xg1 = reinterpret_cast<int8_t *>(wsb + W.d_xq);
+  d.xg2 = d.xg1 + static_cast<int64_t>(kDecodeRows) * L->K;
+  d.x8g = reinterpret_cast<int *>(wsb + W.d_x8g);
+  d.escg = reinterpret_cast<float *>(wsb + W.d_escg);
+  d.cntw = reinterpret_cast<uint64_t *>(wsb + W.d_cntw);
   d.y = static_cast<uint16_t *>(y);
   d.gen = next_generation();
+  d.tag = static_cast<uint32_t>(d.gen ^ (d.gen >> 32));
+  if (d.tag == 0) d.tag = 1;
   d.N = L->N;
   d.K = L->K;
   d.r = L->r;
@@ -224,14 +238,17 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.nprod = decode_producers(d.nunit, M);
   d.nsr = L->n_seg * L->r;
   d.nsr_pad = nsr_pad_of(L->n_seg, L->r);
-  d.g4 = g4;
-  d.g8 = g8;
+  d.g4 = small ? (g4 + sp.RT - 1) / sp.RT : g4;
+  d.g8 = small ? (g8 + sp.RT - 1) / sp.RT : g8;
   d.S = S;
+  d.RT = small ? sp.RT : 0;
+  d.MAXG = small ? sp.MAXG : 0;
   d.KW = L->K / d.S;
   d.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
   d.fused = M <= kDecodeFusedMaxM ? 1 : 0;
   d.hscale = inv_sqrt_block(L->block);
-  const hipError_t e = launch_decode(d, static_cast<hipStream_t>(stream));
+  const hipError_t e = small ? launch_decode_small(d, static_cast<hipStream_t>(stream))
+                               : launch_decode(d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 

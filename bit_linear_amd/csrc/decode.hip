@@ -77,10 +77,15 @@ __device__ __forceinline__ void drain_stores() {
 
 // --------------------------------------------------------------------------- producer
 
-// VPU: inputs per lane of one unit (unit = 64 * VPU).  FUSED: consumers run in
-// the same launch (device-scope stores, then the generation flag).
-template <int VPU, bool FUSED>
+// Producer outputs x_rot (f16), scales and t.  kModeFused: device-scope
+// stores, then the generation flag (consumers in the same launch);
+// kModeSplit: plain stores (consumers in the next launch).
+constexpr int kModeFused = 0, kModeSplit = 1;
+
+// VPU: inputs per lane of one unit (unit = 64 * VPU).
+template <int VPU, int MODE>
 __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
+  constexpr bool FUSED = MODE != kModeSplit;   // device-scope stores
   constexpr int P = 64 * VPU;
   constexpr int LDR = P + 8;                 // bf16 LDS row
   constexpr int RPW = kProdRows / kWaves;    // rows per wavefront
@@ -245,9 +250,10 @@ __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) s += red[((w * 2 + i / 32) * 32 + ml) * 32 + (i % 32)];
-    st<FUSED>(a.tp + (static_cast<int64_t>(u) * kDecodeRows + m0 + ml) * a.nsr_pad + i, s);
+    const int64_t ti = (static_cast<int64_t>(u) * kDecodeRows + m0 + ml) * a.nsr_pad + i;
+    st<FUSED>(a.tp + ti, s);
   }
-  if constexpr (FUSED) {
+  if constexpr (MODE == kModeFused) {
     drain_stores();
     __syncthreads();
     if (tid == 0) st_dev(a.flag + pidx, a.gen);
@@ -510,13 +516,13 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   }
 }
 
-template <bool FUSED>
+template <int MODE>
 __device__ __forceinline__ void produce_any(const DecodeArgs &a, int pidx, uint8_t *smem) {
   switch (a.unit) {
-    case 256: produce<4, FUSED>(a, pidx, smem); break;
-    case 512: produce<8, FUSED>(a, pidx, smem); break;
-    case 1024: produce<16, FUSED>(a, pidx, smem); break;
-    default: produce<32, FUSED>(a, pidx, smem); break;
+    case 256: produce<4, MODE>(a, pidx, smem); break;
+    case 512: produce<8, MODE>(a, pidx, smem); break;
+    case 1024: produce<16, MODE>(a, pidx, smem); break;
+    default: produce<32, MODE>(a, pidx, smem); break;
   }
 }
 
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int b = blockIdx.x;
   if (FUSED && b < a.nprod) {
-    produce_any<true>(a, b, smem);
+    produce_any<kModeFused>(a, b, smem);
   } else {
     const int c = FUSED ? b - a.nprod : b;
     if (c / a.S < a.g4) consume<MSUB, MAXS, false, FUSED>(a, c, smem);
@@ -537,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
 __global__ __launch_bounds__(kThreads) void decode_prologue_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  produce_any<false>(a, blockIdx.x, smem);
+  produce_any<kModeSplit>(a, blockIdx.x, smem);
 }
 
 hipError_t set_lds(const void *fn, size_t lds, bool &done) {

@@ -1,0 +1,674 @@
+// Small-M decode path (1 <= M <= 4) of y = (x H) W_hat^T + ((x H) V^T) U^T in
+// one kernel launch (MiniCPM5-2B-Hadamard-GSQ model card, Mathematical
+// Foundations 2, runtime equation; rotation: same card, Mathematical
+// Foundations 1, and Spark-X2.5-4B-Hadamard-GSQ model card, Tier B equation;
+// tiers: MiniCPM card INT4 equation and Spark card Tier A).
+//
+// t producers (the lowest block indices, one per rotation unit of max(block,
+// 256) inputs) rotate their unit of x and store the partial t = x_rot V^T with
+// device-scope stores, then publish a 64-bit generation flag.
+//
+// Consumers are 16-wavefront workgroups (about one per compute unit): RT tiles
+// of 16 packed rows, each served by KQ wavefronts that split the K-range, plus
+// at least one spare wavefront that waits for the t producers and copies t to
+// LDS.  A wavefront's memory counter completes in order, so every load whose
+// result is needed before the main loop is issued before the weight loads:
+// each compute wavefront first loads the activations of one (row, unit) item,
+// then all of its weight loads, then rotates and quantizes its item into LDS
+// while the weights stream in.  Each (row, unit) becomes a 15-bit integer
+// X = 256 x1 + x2 with a power-of-two scale 2^e, stored as two int8 planes with
+// 8 x (the sum of X over every group of 64 inputs), and multiplied with the
+// codes on the int8 matrix cores (16x16x64), which sum exactly in int32:
+//   INT4 group g:  sum_k (n_k - 8) X_k = sum_k n_k X_k - 8 sum_k X_k, the
+//                  nibbles n_k in [0, 15] being valid int8 operands; the
+//                  group's bf16 scale is applied in fp32;
+//   INT8 rows:     sum_k q_k X_k, the row scale applied at the end.
+// The unit scale 2^e multiplies each unit's partial sum.  Rotation: a
+// Sylvester block of 256 is H_16 (x) H_16, so a 256-input block viewed as a
+// 16x16 matrix X becomes Hs X H_16 (Hs = H_16, or I (x) H_{b/16} for b < 256):
+// one bf16 MFMA for X H_16 (exact products, fp32 sums) and two for the second
+// factor on that fp32 result split into bf16 high and low parts; units of
+// 512 .. 2048 inputs combine their 256-blocks with butterflies in registers.
+#include "dvssq_internal.h"
+
+namespace dvssq {
+
+namespace {
+
+constexpr int kThreads = 1024;          // 16 wavefronts per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kTile = 16;               // packed rows per MFMA tile
+constexpr int kProdRows = 8;            // activation rows per producer
+constexpr int kTab = 4;                 // token rows of the per-row LDS tables
+constexpr int kUDwords = 4;             // U-slab dwords per thread (<= 7 tiles x 16 rows x r <= 64)
+constexpr long kSpinLimit = 1L << 22;   // bounded wait for a producer flag
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int16_t s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void st_dev(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 ld_dev16(const void *p) {
+  const uint64_t *q = static_cast<const uint64_t *>(p);
+  const uint64_t lo = ld_dev(q), hi = ld_dev(q + 1);
+  u32x4 r;
+  r[0] = static_cast<uint32_t>(lo);
+  r[1] = static_cast<uint32_t>(lo >> 32);
+  r[2] = static_cast<uint32_t>(hi);
+  r[3] = static_cast<uint32_t>(hi >> 32);
+  return r;
+}
+// wait until every store this thread issued has completed
+__device__ __forceinline__ void drain_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0,
+                                               0);
+}
+__device__ __forceinline__ f32x4 mfma16_bf16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                   0, 0);
+}
+
+// bf16 entry (a, b) of the 16x16 block-diagonal matrix with Sylvester blocks H_R
+__device__ __forceinline__ uint32_t sylvester_bf16(int a, int b, int R) {
+  if ((a / R) != (b / R)) return 0u;
+  return (__popc(a & b & (R - 1)) & 1) ? 0xBF80u : 0x3F80u;
+}
+
+// cross-lane steps on the DPP network (rows of 16 lanes): xor 1, xor 2 inside
+// a quad, mirror inside 8 and inside 16 lanes
+#define DVSSQ_DPP(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), (ctrl), 0xF, 0xF, false)
+__device__ __forceinline__ float wave_max(float v) {
+  int b = __float_as_int(v);
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0xB1))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0x4E))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0x141))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0x140))));
+  const float m0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float m1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float m2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float m3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+}
+__device__ __forceinline__ int quad_sum(int v) {
+  v += DVSSQ_DPP(v, 0xB1);
+  v += DVSSQ_DPP(v, 0x4E);
+  return v;
+}
+// four bytes (the low byte of each value) in one dword, v0 lowest
+__device__ __forceinline__ uint32_t pack_bytes(int v0, int v1, int v2, int v3) {
+  const uint32_t lo = __builtin_amdgcn_perm(static_cast<uint32_t>(v1), static_cast<uint32_t>(v0), 0x0C0C0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(static_cast<uint32_t>(v3), static_cast<uint32_t>(v2), 0x0C0C0400u);
+  return lo | (hi << 16);
+}
+
+// Rotation of one (row, unit) item by one wavefront: lane holds, for every
+// 256-block c, the inputs 256 c + 16 (lane % 16) + 4 (lane / 16) + j, j < 4
+// (xw: the bf16 input pairs), and gets x_rot at the same positions.
+template <int C>
+__device__ __forceinline__ void rotate_item(const DecodeArgs &a, const u32x2 (&xw)[C], float (&y)[C][4]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  if (!a.rotate) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      y[c][0] = __uint_as_float(xw[c][0] << 16);
+      y[c][1] = __uint_as_float(xw[c][0] & 0xFFFF0000u);
+      y[c][2] = __uint_as_float(xw[c][1] << 16);
+      y[c][3] = __uint_as_float(xw[c][1] & 0xFFFF0000u);
+    }
+    return;
+  }
+  const int Rb = min(a.block / 16, 16);
+  u32x2 h1, h2;
+  h1[0] = sylvester_bf16(4 * q, n, 16) | (sylvester_bf16(4 * q + 1, n, 16) << 16);
+  h1[1] = sylvester_bf16(4 * q + 2, n, 16) | (sylvester_bf16(4 * q + 3, n, 16) << 16);
+  h2[0] = sylvester_bf16(4 * q, n, Rb) | (sylvester_bf16(4 * q + 1, n, Rb) << 16);
+  h2[1] = sylvester_bf16(4 * q + 2, n, Rb) | (sylvester_bf16(4 * q + 3, n, Rb) << 16);
+  const f32x4 zf = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const f32x4 F = mfma16_bf16(xw[c], h1, zf);  // X H_16, lane: rows 4q+j, column n
+    u32x2 hi, lo;
+    hi[0] = pack_bf16x2(F[0], F[1]);
+    hi[1] = pack_bf16x2(F[2], F[3]);
+    lo[0] = pack_bf16x2(F[0] - __uint_as_float(hi[0] << 16), F[1] - __uint_as_float(hi[0] & 0xFFFF0000u));
+    lo[1] = pack_bf16x2(F[2] - __uint_as_float(hi[1] << 16), F[3] - __uint_as_float(hi[1] & 0xFFFF0000u));
+    f32x4 D = mfma16_bf16(hi, h2, zf);             // (Hs X H_16)^T, high part ...
+    D = mfma16_bf16(lo, h2, D);                    // ... plus low part
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[c][j] = D[j];
+  }
+#pragma unroll
+  for (int sft = 1; sft < C; sft <<= 1)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      if (!(c & sft))
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = y[c][j], p1 = y[c + sft][j];
+          y[c][j] = p0 + p1;
+          y[c + sft][j] = p0 - p1;
+        }
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[c][j] *= a.hscale;
+}
+
+// --------------------------------------------------------------------------- producer
+
+// Partial t of one rotation unit (C blocks of 256) for up to 8 activation rows.
+template <int C>
+__device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
+  constexpr int P = 256 * C;
+  constexpr int LDB = P + 8;             // bf16 x_rot row in LDS
+  constexpr int KS = P / 32;             // k-steps of the t product
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const int u = pidx % a.nunit, rg = pidx / a.nunit;
+  const int m0 = rg * kProdRows, mrows = min(kProdRows, a.M - m0);
+  const int k0 = u * P;
+  const int nsp = a.nsr_pad, ni = nsp / 16;
+  uint16_t *xb = reinterpret_cast<uint16_t *>(smem);                   // [8][LDB]
+  float *tred = reinterpret_cast<float *>(smem + kProdRows * LDB * 2);  // [kWaves][4][64]
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+  // t split: wavefront w takes 16 columns (it) of t and one chunk (kc) of the k-steps
+  const int nkc = kWaves / ni;
+  const int it = wave % ni, kc = wave / ni;
+  const bool t_wave = kc < nkc;
+  const int ksp = (KS + nkc - 1) / nkc;
+  u32x4 vb[8];
+  auto vload = [&](int j, int slot) {
+    const int ks = min(kc * ksp + j, KS - 1);
+    const int row = min(it * 16 + n, a.nsr - 1);
+    vb[slot] = *reinterpret_cast<const u32x4 *>(a.V + static_cast<int64_t>(row) * a.K + k0 + 32 * ks + 8 * q);
+  };
+  const bool r_wave = wave < mrows;
+  const int m = m0 + min(wave, mrows - 1);
+  u32x2 xw[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+    xw[c] = *reinterpret_cast<const u32x2 *>(a.x + static_cast<int64_t>(m) * a.K + k0 + 256 * c + 16 * n + 4 * q);
+  if (t_wave)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vload(j, j);
+
+  // 1. rotate one row per wavefront; bf16 copy for the t product
+  if (r_wave) {
+    float y[C][4];
+    rotate_item<C>(a, xw, y);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      u32x2 w;
+      w[0] = pack_bf16x2(y[c][0], y[c][1]);
+      w[1] = pack_bf16x2(y[c][2], y[c][3]);
+      *reinterpret_cast<u32x2 *>(xb + wave * LDB + 256 * c + 16 * n + 4 * q) = w;
+    }
+  } else if (wave < kProdRows) {
+    for (int j = lane; j < P / 2; j += 64) *reinterpret_cast<uint32_t *>(xb + wave * LDB + 2 * j) = 0u;
+  }
+  __syncthreads();
+
+  // 2. partial t of this unit: t[m][i] = sum_k x_rot[m][k] V[i][k] (bf16 MFMA)
+  f32x4 tacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (t_wave) {
+    for (int j0 = 0; j0 < ksp; j0 += 8) {
+      if (j0 > 0)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vload(j0 + j, j);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ks = kc * ksp + j0 + j;
+        const bool ok = j0 + j < ksp && ks < KS && n < kProdRows;
+        u32x4 av = *reinterpret_cast<const u32x4 *>(xb + (n & (kProdRows - 1)) * LDB + 32 * min(ks, KS - 1) + 8 * q);
+        av = ok ? av : z4;
+        tacc = mfma_bf16(av, vb[j], tacc);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) tred[(wave * 4 + r) * 64 + lane] = tacc[r];
+  __syncthreads();
+  // tacc of wavefront (kc, it): row m = 4 (lane / 16) + r, column it * 16 + lane % 16
+  for (int e = tid; e < mrows * nsp; e += kThreads) {
+    const int ml = e / nsp, i = e % nsp;
+    const int lw = 16 * (ml / 4) + (i % 16), r = ml % 4;
+    float s = 0.0f;
+    for (int c = 0; c < nkc; ++c) s += tred[((c * ni + i / 16) * 4 + r) * 64 + lw];
+    st_dev(a.tp + (static_cast<int64_t>(u) * kDecodeRows + m0 + ml) * nsp + i, s);
+  }
+  drain_stores();
+  __syncthreads();
+  if (tid == 0) st_dev(a.flag + pidx, a.gen);
+}
+
+// --------------------------------------------------------------------------- consumer
+
+// MT: largest M (1 or 4); C: 256-blocks per rotation unit; MAXG: groups of 64
+// inputs loaded per wavefront; T8: INT8 tier.  a.RT tiles of 16 rows per
+// workgroup, KQ = 15 / RT wavefronts per tile; the wavefronts from RT * KQ on
+// wait for t.
+template <int MT, int C, int MAXG, bool T8>
+__device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
+  constexpr int R = MT == 1 ? 1 : 4;    // accumulator rows per lane that can hold a token
+  const int RT = a.RT, KQ = (kWaves - 1) / RT, NCW = RT * KQ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const bool active = wave < NCW;                       // compute wavefront
+  const int rt = min(wave / KQ, RT - 1), kq = wave % KQ;
+  const int grp = cidx / a.S, split = cidx % a.S;
+  const int rows = T8 ? a.n8 : a.n4;
+  const int ntiles = (rows + kTile - 1) / kTile;
+  const int tile0 = (T8 ? grp - a.g4 : grp) * RT;       // first tile of the workgroup inside the tier
+  const int tile = tile0 + rt;
+  const bool tile_ok = tile < ntiles;
+  const int gbase = min(tile, ntiles - 1) * kTile;
+  const int pl = gbase + n;
+  const bool row_ok = tile_ok && pl < rows;
+  const int plc = min(pl, rows - 1);
+  const int base = (T8 ? a.n4 : 0) + gbase;             // first packed row of the tile
+  const int pc = base + (plc - gbase);
+  const int M = a.M, KW = a.KW;
+  constexpr int P = 256 * C;
+  const int k0 = split * KW;
+  const int ngrp = KW / kGroup;
+  const int gpw = (ngrp + KQ - 1) / KQ;
+  const int g0 = kq * gpw, g1 = min(ngrp, g0 + gpw);
+  const int gs = max(0, min(g0, ngrp - MAXG));          // first loaded group (MAXG <= ngrp)
+  const int nu = KW / P, u0 = k0 / P;
+  constexpr int gpu = P / kGroup;
+  const int KG = a.K / kGroup;
+  const int nsp = a.nsr_pad;
+  const int nitem = M * nu;                             // (row, unit) items to rotate
+
+  // LDS: int8 planes, 8 x group sums, unit scales, partial tiles, U slabs, t
+  int8_t *xs1 = reinterpret_cast<int8_t *>(smem);
+  int8_t *xs2 = xs1 + M * KW;
+  int *x8 = reinterpret_cast<int *>(xs2 + M * KW);                   // [ngrp][4]
+  float *esc = reinterpret_cast<float *>(x8 + ngrp * kTab);          // [nu][4]
+  float *red = esc + nu * kTab;                                      // [kWaves][4][64]
+  uint32_t *ush = reinterpret_cast<uint32_t *>(red + kWaves * 4 * 64);  // [kUDwords * kThreads]
+  float *tpart = reinterpret_cast<float *>(ush + kUDwords * kThreads);     // [nu][M][nsp]
+  float *ts = tpart + nu * M * nsp;                                  // [M][nsp]
+
+  // ---- 1. activations of this wavefront's first item, before anything else
+  int item = wave;
+  u32x2 xw[C];
+  {
+    const int it = min(item, nitem - 1), m = it % M, u = it / M;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      xw[c] = *reinterpret_cast<const u32x2 *>(a.x + static_cast<int64_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n + 4 * q);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. weight loads of this wavefront, then the U slab, columns, INT8 scale
+  u32x2 c4[T8 ? 1 : MAXG];
+  uint32_t sb[T8 ? 1 : MAXG];
+  u32x4 c8[T8 ? MAXG : 1];
+  if (active) {
+    const uint8_t *p4 = a.q4 + static_cast<int64_t>(plc) * (a.K / 2) + (k0 + 64 * gs + 16 * q) / 2;
+    const uint16_t *ps = a.s4 + static_cast<int64_t>(plc) * KG + k0 / kGroup + gs;
+    const int8_t *p8 = a.q8 + static_cast<int64_t>(plc) * a.K + k0 + 64 * gs + 16 * q;
+#pragma unroll
+    for (int i = 0; i < MAXG; ++i) {
+      if constexpr (!T8) {
+        c4[i] = *reinterpret_cast<const u32x2 *>(p4 + 32 * i);
+        sb[i] = ps[i];
+      } else {
+        c8[i] = *reinterpret_cast<const u32x4 *>(p8 + 64 * i);
+      }
+    }
+  }
+  // U rows of the workgroup's tiles: one contiguous range, fetched as aligned dwords
+  const int wbase = (T8 ? a.n4 : 0) + min(tile0, ntiles - 1) * kTile;
+  const int64_t ue0 = static_cast<int64_t>(wbase) * a.r;
+  const int64_t ud0 = ue0 / 2;
+  const int64_t ud_last = (static_cast<int64_t>(a.N) * a.r + 1) / 2 - 1;
+  const uint32_t *U32 = reinterpret_cast<const uint32_t *>(a.U);
+  uint32_t uw[kUDwords];
+#pragma unroll
+  for (int j = 0; j < kUDwords; ++j) uw[j] = U32[std::min<int64_t>(ud0 + tid + kThreads * j, ud_last)];
+  const int col = a.idx[pc];
+  const float s8 = T8 ? a.s8[plc] : 1.0f;
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. items -> quantized int8 planes in LDS (compute wavefronts); the
+  // spare wavefronts wait for the t producers of the range and copy t
+  if (active) {
+    for (; item < nitem; item += NCW) {
+      const int m = item % M, u = item / M;
+      if (item != wave) {   // later items (M > 1): loaded now
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          xw[c] = *reinterpret_cast<const u32x2 *>(a.x + static_cast<int64_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n +
+                                                    4 * q);
+      }
+      float y[C][4];
+      rotate_item<C>(a, xw, y);
+      float mx = 0.0f;
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(y[c][j]));
+      mx = wave_max(mx);
+      // 15-bit quantization: max |X| in [2^13, 2^14]
+      const int e = (mx > 0.0f && mx <= 3.0e38f) ? max(-100, min(114, ilogbf(mx) - 13)) : 0;
+      const float down = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        int X[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[j] = __float2int_rn(y[c][j] * down);
+        const int kk = u * P + 256 * c + 16 * n + 4 * q;
+        *reinterpret_cast<uint32_t *>(xs1 + m * KW + kk) =
+            pack_bytes((X[0] + 128) >> 8, (X[1] + 128) >> 8, (X[2] + 128) >> 8, (X[3] + 128) >> 8);
+        *reinterpret_cast<uint32_t *>(xs2 + m * KW + kk) = pack_bytes(X[0], X[1], X[2], X[3]);
+        // group of 64 = kk / 64: the lanes with the same n / 4
+        int gsum = quad_sum(X[0] + X[1] + X[2] + X[3]);
+        gsum += __shfl_xor(gsum, 16, 64);
+        gsum += __shfl_xor(gsum, 32, 64);
+        if ((lane & 0x33) == 0) x8[(kk / kGroup) * kTab + m] = 8 * gsum;
+      }
+      if (lane == 0) esc[u * kTab + m] = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
+    }
+  } else {
+    const int sw = wave - NCW, nsw = kWaves - NCW;       // spare wavefront index and count
+    for (int i = sw * 64 + lane; i < nu; i += nsw * 64) {
+      long spins = 0;
+      while (ld_dev(a.flag + u0 + i) != a.gen && spins < kSpinLimit) {
+        __builtin_amdgcn_s_sleep(1);
+        ++spins;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int e = sw * 64 + lane; e < nu * M * a.nsr; e += nsw * 64) {
+      const int i = e % a.nsr, mu = e / a.nsr;
+      tpart[mu * nsp + i] = ld_dev(a.tp + (static_cast<int64_t>(u0 + mu / M) * kDecodeRows + mu % M) * nsp + i);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < M * nsp; e += kThreads) {
+    const int m = e / nsp, i = e % nsp;
+    float s = 0.0f;
+    if (i < a.nsr)
+      for (int u = 0; u < nu; ++u) s += tpart[(u * M + m) * nsp + i];
+    ts[e] = s;
+  }
+
+  // ---- 4. main loop: two int8 MFMAs per group, straight-line and masked; the
+  // MFMAs of group i+1 are issued before the scalar work of group i
+  const i32x4 zi = {0, 0, 0, 0};
+  float acc[R], accu[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = accu[r] = 0.0f;
+  const int mA = MT == 1 ? 0 : min(n, M - 1);
+  const int8_t *pa1 = xs1 + mA * KW + 16 * q, *pa2 = xs2 + mA * KW + 16 * q;
+  auto bop = [&](int i) -> u32x4 {
+    u32x4 b;
+    if constexpr (!T8) {
+      const uint32_t w0 = c4[i][0], w1 = c4[i][1];
+      b[0] = w0 & 0x0F0F0F0Fu;
+      b[1] = (w0 >> 4) & 0x0F0F0F0Fu;
+      b[2] = w1 & 0x0F0F0F0Fu;
+      b[3] = (w1 >> 4) & 0x0F0F0F0Fu;
+    } else {
+      b = c8[i];
+    }
+    return b;
+  };
+  i32x4 d1, d2;
+  {
+    const u32x4 b = bop(0);
+    d1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * gs), b, zi);
+    d2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * gs), b, zi);
+  }
+#pragma unroll
+  for (int i = 0; i < MAXG; ++i) {
+    const int g = gs + i;
+    const bool valid = g >= g0 && g < g1;
+    i32x4 e1 = zi, e2 = zi;
+    if (i + 1 < MAXG) {
+      const u32x4 b = bop(i + 1 < MAXG ? i + 1 : i);
+      e1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * (g + 1)), b, zi);
+      e2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * (g + 1)), b, zi);
+    }
+    float sg;
+    i32x4 xg = zi;
+    if constexpr (!T8) {
+      sg = valid ? bf16_to_f32(sb[i]) : 0.0f;
+      xg = *reinterpret_cast<const i32x4 *>(x8 + g * kTab);
+    } else {
+      sg = valid ? 1.0f : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int v = (d1[r] << 8) + d2[r] - xg[r];
+      accu[r] = fmaf(sg, static_cast<float>(v), accu[r]);
+    }
+    const bool bnd = valid && (((g + 1) % gpu == 0) || (g == g1 - 1));
+    const f32x4 ev = *reinterpret_cast<const f32x4 *>(esc + (g / gpu) * kTab);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc[r] = fmaf(bnd ? ev[r] : 0.0f, accu[r], acc[r]);
+      accu[r] = bnd ? 0.0f : accu[r];
+    }
+    d1 = e1;
+    d2 = e2;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- 5. partial tiles and U slabs -> LDS
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = r < R ? acc[r] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < kUDwords; ++j) ush[tid + kThreads * j] = uw[j];
+  __syncthreads();
+  if (kq != 0 || !active) return;
+
+  // ---- 6. first wavefront of each tile: sum the K-slices, add the low-rank term
+  f32x4 cacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float s = 0.0f;
+    for (int w = 0; w < KQ; ++w) s += red[((rt * KQ + w) * 4 + r) * 64 + lane];
+    cacc[r] = s * s8;
+  }
+  {
+    const int seg = col / (a.N / a.n_seg);
+    const uint16_t *u16 = reinterpret_cast<const uint16_t *>(ush);
+    const int uoff = static_cast<int>(ue0 - 2 * ud0) + (base - wbase) * a.r;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    for (int st = 0; st < nsp / 32; ++st) {
+      u32x4 bv;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        uint32_t pair = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int ig = 32 * st + 8 * q + 2 * h + e;
+          const int il = ig - seg * a.r;
+          const bool ok = row_ok && ig < a.nsr && il >= 0 && il < a.r;
+          const uint32_t uv = ok ? u16[n * a.r + il + uoff] : 0u;
+          pair |= uv << (16 * e);
+        }
+        bv[h] = pair;
+      }
+      u32x4 av = z4;
+      if (n < M) {
+        const float *t = ts + n * nsp + 32 * st + 8 * q;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) av[h] = pack_bf16x2(t[2 * h], t[2 * h + 1]);
+      }
+      cacc = mfma_bf16(av, bv, cacc);
+    }
+  }
+
+  // ---- 7. output: direct, or split-K partials summed by the last arriver
+  if (a.S == 1) {
+    if (!row_ok) return;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int m = 4 * q + r;
+      if (m < M) a.y[static_cast<int64_t>(m) * a.N + col] = f32_to_bf16(cacc[r]);
+    }
+    return;
+  }
+  if (!tile_ok) return;
+  const int p = base + n;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int m = 4 * q + r;
+    if (m < M && row_ok) st_dev(a.part + (static_cast<int64_t>(split) * kDecodeRows + m) * a.N + p, cacc[r]);
+  }
+  drain_stores();
+  int last = 0;
+  if (lane == 0) {
+    uint64_t *cnt = a.cntw + (T8 ? (a.n4 + kTile - 1) / kTile : 0) + tile;
+    uint64_t old = ld_dev(cnt), nw;
+    do {
+      nw = (static_cast<uint32_t>(old >> 32) == a.tag) ? old + 1 : ((static_cast<uint64_t>(a.tag) << 32) | 1u);
+    } while (!__hip_atomic_compare_exchange_strong(cnt, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT));
+    last = static_cast<uint32_t>(nw) == static_cast<uint32_t>(a.S);
+  }
+  last = __shfl(last, 0, 64);
+  if (!last) return;
+  const int nrows = min(kTile, rows - gbase);
+  for (int e = lane; e < kTile * M; e += 64) {
+    const int rr = e % kTile, m = e / kTile;
+    if (rr >= nrows) continue;
+    const int pp = base + rr;
+    float s = 0.0f;
+    for (int sp = 0; sp < a.S; ++sp) s += ld_dev(a.part + (static_cast<int64_t>(sp) * kDecodeRows + m) * a.N + pp);
+    a.y[static_cast<int64_t>(m) * a.N + a.idx[pp]] = f32_to_bf16(s);
+  }
+}
+
+template <int MT, int C, int MAXG>
+__global__ __launch_bounds__(kThreads) void decode_small_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int b = blockIdx.x;
+  if (b < a.nprod) {
+    produce<C>(a, b, smem);
+    return;
+  }
+  const int c = b - a.nprod;
+  if (c / a.S < a.g4) consume<MT, C, MAXG, false>(a, c, smem);
+  else consume<MT, C, MAXG, true>(a, c, smem);
+}
+
+size_t producer_lds(int unit) {
+  return static_cast<size_t>(kProdRows) * (unit + 8) * 2 + static_cast<size_t>(kWaves) * 4 * 64 * 4;
+}
+
+size_t consumer_lds(int M, int unit, int KW, int nsr_pad) {
+  const size_t nu = KW / unit, ngrp = KW / kGroup;
+  return static_cast<size_t>(2) * M * KW + ngrp * kTab * 4 + nu * kTab * 4 + static_cast<size_t>(kWaves) * 4 * 64 * 4 +
+         static_cast<size_t>(kUDwords) * kThreads * 4 + nu * M * nsr_pad * 4 + static_cast<size_t>(M) * nsr_pad * 4;
+}
+
+size_t small_lds(int M, int unit, int KW, int nsr_pad) {
+  return std::max(producer_lds(unit), consumer_lds(M, unit, KW, nsr_pad));
+}
+
+template <int MT, int C, int MAXG>
+hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
+  const size_t lds = small_lds(a.M, a.unit, a.KW, a.nsr_pad);
+  if (lds > 65536) {
+    static bool done = false;
+    if (!done) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_small_kernel<MT, C, MAXG>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+      done = true;
+    }
+  }
+  const int grid = a.nprod + (a.g4 + a.g8) * a.S;
+  hipLaunchKernelGGL((decode_small_kernel<MT, C, MAXG>), dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int MT, int C>
+hipError_t launch_g(const DecodeArgs &a, hipStream_t s) {
+  if (a.MAXG == 8) return launch_t<MT, C, 8>(a, s);
+  return launch_t<MT, C, 4>(a, s);
+}
+
+template <int MT>
+hipError_t launch_m(const DecodeArgs &a, hipStream_t s) {
+  switch (a.unit) {
+    case 256: return launch_g<MT, 1>(a, s);
+    case 512: return launch_g<MT, 2>(a, s);
+    case 1024: return launch_g<MT, 4>(a, s);
+    default: return launch_g<MT, 8>(a, s);
+  }
+}
+
+}  // namespace
+
+// Workgroup shape and split: RT tiles of 16 rows per workgroup (15/RT
+// wavefronts per tile split K), S equal parts of K, each a whole number of
+// rotation units, with at most 8 groups of 64 per wavefront (the register
+// file holds 16 wavefronts of at most 128 registers) and the LDS within 160 KB.  The score is the
+// share of compute units kept busy, wgs / (256 * rounds); a split costs a
+// reduction (0.2 + 0.01 S of the score) and every extra round 0.1; ties go to
+// fewer workgroups.
+bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
+  if (M < 1 || M > 4) return false;
+  const int unit = L.block > 256 ? L.block : 256;
+  if (L.K % unit) return false;
+  const int nunit = L.K / unit;
+  const int nsp = (L.n_seg * L.r + 31) / 32 * 32;
+  const int t4 = (L.n_int4 + kTile - 1) / kTile, t8 = (L.n_int8 + kTile - 1) / kTile;
+  const int gmax = 8;
+  double best = -1.0;
+  int best_wgs = 0;
+  for (int RT : {1, 2, 3, 4, 5, 7}) {
+    const int KQ = (kWaves - 1) / RT;
+    for (int S = 1; S <= kMaxSplit && S <= nunit; ++S) {
+      if (nunit % S) continue;
+      const int KW = L.K / S, ngrp = KW / kGroup;
+      const int gpw = (ngrp + KQ - 1) / KQ;
+      if (gpw > gmax) continue;
+      const int maxg = gpw <= 4 ? 4 : 8;
+      if (maxg > ngrp) continue;
+      if (small_lds(M, unit, KW, nsp) > 160 * 1024) continue;
+      const int wgs = ((t4 + RT - 1) / RT + (t8 + RT - 1) / RT) * S;
+      const int slots = 256;
+      const int rounds = (wgs + slots - 1) / slots;
+      const double score = static_cast<double>(wgs) / (static_cast<double>(slots) * rounds) -
+                           (S > 1 ? 0.2 + 0.01 * S : 0.0) - 0.1 * (rounds - 1);
+      if (score > best + 1e-9 || (score > best - 1e-9 && wgs < best_wgs)) {
+        best = score;
+        best_wgs = wgs;
+        plan->RT = RT;
+        plan->S = S;
+        plan->MAXG = maxg;
+      }
+    }
+  }
+  return best >= 0.0;
+}
+
+hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s) {
+  if (a.unit != 256 && a.unit != 512 && a.unit != 1024 && a.unit != 2048) return hipErrorInvalidValue;
+  return a.M <= 1 ? launch_m<1>(a, s) : launch_m<4>(a, s);
+}
+
+}  // namespace dvssq

@@ -110,6 +110,9 @@ struct WsLayout {
   int64_t d_flag;  // u64 [nunit * 4]: generation stamp written by each producer
   int64_t d_cnt;   // int32 [groups]: split-K arrivals per 16-row group
   int64_t d_part;  // fp32 [kMaxSplit][32][N]: split-K partial outputs
+  int64_t d_x8g;   // int32 [K/64][32]: 8 x (sum of the quantized x of a group) (small-M path)
+  int64_t d_escg;  // fp32 [nunit][32]: 2^e of each (unit, row) (small-M path)
+  int64_t d_cntw;  // u64 [groups]: tagged split-K arrival counters (small-M path)
   int64_t d_end;
   // prefill
   int64_t p_xr;    // f16 [M_max][K] rotated x scaled by 2^-e per row (or bf16 for dvssq_fwht)
@@ -137,6 +140,9 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
   w.d_flag = cur; cur = align256(cur + 8 * decode_producers(nunit, kDecodeRows));
   w.d_cnt = cur;  cur = align256(cur + 4 * (decode_groups(L.n_int4) + decode_groups(L.n_int8)));
   w.d_part = cur; cur = align256(cur + 4 * int64_t(kMaxSplit) * kDecodeRows * N);
+  w.d_x8g = cur;  cur = align256(cur + 4 * (K / kGroup) * kDecodeRows);
+  w.d_escg = cur; cur = align256(cur + 4 * nunit * kDecodeRows);
+  w.d_cntw = cur; cur = align256(cur + 8 * (decode_groups(L.n_int4) + decode_groups(L.n_int8)));
   w.d_end = cur;
   cur = 0;
   w.p_xr = cur;   cur = align256(cur + 2 * static_cast<int64_t>(L.M_max) * K);
@@ -178,10 +184,16 @@ struct DecodeArgs {
   uint64_t *flag;      // [nprod]
   int *cnt;            // [g4 + g8]
   float *part;         // fp32 [S][32][N]
+  int8_t *xg1, *xg2;   // small-M path: x_rot quantized to X = 256 x1 + x2, int8 planes [32][K]
+  int *x8g;            // small-M path: [K/64][32] 8 x sum of X over each group
+  float *escg;         // small-M path: [nunit][32] 2^e of each (unit, row)
+  uint64_t *cntw;      // tagged arrival counters [g4 + g8] (small-M path)
   uint16_t *y;         // bf16 [M][N]
   uint64_t gen;        // generation stamp of this call
+  uint32_t tag;        // 32-bit tag of this call (small-M path), never 0
   int N, K, r, n_seg, n4, n8, M, block, unit, nunit, nprod, nsr, nsr_pad, S, KW, g4, g8, rotate;
   int fused;           // 1: producers and consumers in one launch; 0: two launches
+  int RT, MAXG;        // small-M path: 16-row tiles per workgroup, most groups per wavefront
   float hscale;        // 1/sqrt(block)
 };
 
@@ -205,6 +217,15 @@ hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hi
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 size_t decode_lds_bytes(int M, int unit, int KW, int nsr_pad);
 int decode_max_spans();   // most 128-input spans one decode workgroup takes
+// small-M decode (M <= 4): int8 matrix cores, 16-wavefront workgroups
+struct SmallPlan {
+  int RT;    // 16-row tiles per workgroup (1, 2, 4)
+  int S;     // split-K factor
+  int MAXG;  // groups of 64 inputs loaded per wavefront (4, 8, 12)
+};
+// false when no plan fits (the caller then takes the general decode path)
+bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan);
+hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
 }  // namespace dvssq
