@@ -1,21 +1,27 @@
 """Benchmark of the DV-SSQ linear layer on one MI355X.
 
 Headline (one JSON line on stdout): effective weight GB/s of the Spark-shaped
-up_proj decode call (K=2560, N=10240, r=16, M=1) = the packed layer's own bytes
-(algo_bytes) per call / time per call, with the prefill TFLOP/s of the fused
-gate+up layer (K=2560, N=2x10240, r=24, M=2048) beside it.
+up_proj decode call (K=2560, N=10240, r=16, H_256, M=1) = the packed layer's
+bytes (algo_bytes) per call / time per call.  A "step" is one
+dvssq_linear_decode call: rotation, t = x_rot V^T, both weight tiers, the
+low-rank term, any split-K reduction and the bf16 scatter, in one launch.
+
+Beside it: the roofline of that kernel (HBM bound; achieved = algorithmic
+bytes per launch -- packed layer + x + y -- over the average launch time
+measured with HIP events on the launch stream), a table of the other decode
+shapes and of the prefill GEMM (TFLOP/s against the bf16 dense MFMA peak),
+and the oracle timed on the host cores as a baseline.
 
 Inputs are synthetic and already resident in HBM when timing starts.  The
-timed blob is a random, well-formed packed layer of the workload's shape
-(timing does not depend on the code values); C distinct copies totalling >= 1
-GiB are cycled so the 256 MB last-level cache cannot serve repeats.
-
-A "step" is one dvssq_linear_decode call: rotation, group sums, t = x_rot V^T,
-both tiers, the low-rank term, the split-K reduction and the bf16 scatter.
+timed blobs are random, well-formed packed layers of each shape (timing does
+not depend on the code values); C distinct copies totalling >= 1 GiB are
+cycled so the 256 MB last-level cache cannot serve repeats.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import math
 import os
@@ -31,6 +37,8 @@ import numpy as np  # noqa: E402
 METRIC = "effective weight GB/s (M=1 decode) and TFLOP/s (M=2048 prefill), % of roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_spark_up_m1_traffic.json")
+KERNEL_SOURCES = ("decode_small.hip", "dvssq_internal.h", "api.hip")
 
 
 def parse():
@@ -39,11 +47,22 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-m", type=int, default=1)
-    ap.add_argument("--prefill-steps", type=int, default=50)
+    ap.add_argument("--prefill-steps", type=int, default=30)
+    ap.add_argument("--table-steps", type=int, default=400, help="calls per secondary decode shape")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-table", action="store_true", help="skip the secondary shapes")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 256 MiB device copy (scale reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_linear_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def make_copies(dv, torch, lay, M_max, min_bytes=1 << 30, max_copies=256):
@@ -61,6 +80,8 @@ def make_copies(dv, torch, lay, M_max, min_bytes=1 << 30, max_copies=256):
 
 
 def time_calls(torch, fn, steps, warmup):
+    """Average ms per call over `steps` back-to-back calls between two events on
+    the launch stream, after `warmup` untimed calls."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -73,6 +94,46 @@ def time_calls(torch, fn, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(end) / steps, wall
+
+
+class Runner:
+    """Decode / prefill calls of one layer shape through the C ABI."""
+
+    def __init__(self, dv, torch, lay, M, M_max, min_bytes=1 << 30, max_copies=256):
+        import synth
+        self.torch, self.lay, self.M = torch, lay, M
+        self.L, self.blob, self.copies, self.C = make_copies(dv, torch, lay, M_max, min_bytes, max_copies)
+        self.x_bits = synth.activations_bf16(0, lay.outlier_tag or lay.name, M, lay.K)
+        self.x = torch.from_numpy(self.x_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+        self.y = torch.empty((M, lay.N), dtype=torch.bfloat16, device="cuda")
+        self.ws = dv.device_buffer(self.L.ws_bytes)
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.ptrs = [self.copies[i].data_ptr() for i in range(self.C)]
+        self.lib, self.Lp = dv.lib(), ctypes.byref(self.L)
+        self.dv = dv
+
+    def decode(self, i):
+        rc = self.lib.dvssq_linear_decode(self.Lp, self.ptrs[i % self.C], self.x.data_ptr(), self.y.data_ptr(),
+                                          self.M, self.ws.data_ptr(), 0, self.stream)
+        if rc:
+            raise self.dv.DvssqError(rc, "dvssq_linear_decode")
+
+    def prefill(self, i):
+        rc = self.lib.dvssq_linear_prefill(self.Lp, self.ptrs[i % self.C], self.x.data_ptr(), self.y.data_ptr(),
+                                           self.M, self.ws.data_ptr(), 0, self.stream)
+        if rc:
+            raise self.dv.DvssqError(rc, "dvssq_linear_prefill")
+
+    def algo_bytes(self):
+        return self.L.algo_bytes + 2 * self.M * (self.lay.K + self.lay.N)
+
+    def flops(self):
+        lay, M = self.lay, self.M
+        return 2.0 * M * lay.N * lay.K + 2.0 * M * lay.r * (lay.n_seg * lay.K + lay.N)
+
+    def free(self):
+        del self.copies, self.x, self.y, self.ws
+        self.torch.cuda.empty_cache()
 
 
 def cpu_baseline(lay, blob, x_bits, seconds):
@@ -88,15 +149,28 @@ def cpu_baseline(lay, blob, x_bits, seconds):
     L = oracle.layout(lay.N, lay.K, lay.r, lay.n_seg)
     return {"value": round(L["algo_bytes"] * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{reps} full fp64 oracle forwards of the same layer and x (M={x_bits.shape[0]}), "
-                      f"{el:.1f} s"}
+            "sample": f"{reps} complete fp64 oracle forwards of the headline layer (spark_up, M={x_bits.shape[0]}) "
+                      f"on the same packed layer and x, {el:.1f} s"}
+
+
+def traffic_record():
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's multi-GPU "
-              "sharding is described, not run.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs the layer on a "
+              "single GPU; its multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -104,61 +178,57 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
-    up = synth.WORKLOADS["spark_up"].layers[0]
+    layers = {l.name: l for w in synth.WORKLOADS.values() for l in w.layers}
+    up = layers["spark_up"]
     M = args.decode_m
-    L, blob, copies, C = make_copies(dv, torch, up, 32)
-    x_bits = synth.activations_bf16(0, up.outlier_tag, M, up.K)
-    x = torch.from_numpy(x_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
-    y = torch.empty((M, up.N), dtype=torch.bfloat16, device="cuda")
-    ws = dv.device_buffer(L.ws_bytes)
-    stream = torch.cuda.current_stream().cuda_stream
-    ptrs = [copies[i].data_ptr() for i in range(C)]
-    lib, Lref = dv.lib(), L
-    import ctypes as Cc
-    Lp = Cc.byref(Lref)
-    xp, yp, wp = x.data_ptr(), y.data_ptr(), ws.data_ptr()
-
-    def dec(i):
-        rc = lib.dvssq_linear_decode(Lp, ptrs[i % C], xp, yp, M, wp, 0, stream)
-        if rc:
-            raise dv.DvssqError(rc, "dvssq_linear_decode")
-
-    ms, wall = time_calls(torch, dec, args.steps, args.warmup)
-    gbs = L.algo_bytes / (ms * 1e-3) / 1e9
+    head = Runner(dv, torch, up, M, 32)
+    ms, wall = time_calls(torch, head.decode, args.steps, args.warmup)
+    gbs = head.L.algo_bytes / (ms * 1e-3) / 1e9
+    achieved = head.algo_bytes() / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": f"spark_up decode K={up.K} N={up.N} r={up.r} H_{up.block} M={M}",
-                   "algo_bytes": L.algo_bytes, "blob_copies": C},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                   "packed_bytes": head.L.algo_bytes, "blob_copies": head.C, "wall_s": round(wall, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(),
+                     "kernel": "decode_small_kernel", "algo_bytes_per_launch": head.algo_bytes(),
+                     "us_per_launch": round(ms * 1e3, 3)},
     }
-    if not args.no_prefill:
-        gu = synth.WORKLOADS["spark_gateup"].layers[0]
-        Mp = 2048
-        Lg, _, gcopies, Cg = make_copies(dv, torch, gu, Mp, min_bytes=256 << 20, max_copies=16)
-        xg = torch.from_numpy(synth.activations_bf16(0, gu.outlier_tag, Mp, gu.K).view(np.int16)).to("cuda").view(torch.bfloat16)
-        yg = torch.empty((Mp, gu.N), dtype=torch.bfloat16, device="cuda")
-        wsg = dv.device_buffer(Lg.ws_bytes)
-        gptr = [gcopies[i].data_ptr() for i in range(Cg)]
-        Lgp = Cc.byref(Lg)
+    head_blob, head_x = head.blob, head.x_bits
+    head.free()
 
-        def pre(i):
-            rc = lib.dvssq_linear_prefill(Lgp, gptr[i % Cg], xg.data_ptr(), yg.data_ptr(), Mp,
-                                          wsg.data_ptr(), 0, stream)
-            if rc:
-                raise dv.DvssqError(rc, "dvssq_linear_prefill")
+    if args.copy_probe:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
-        msp, _ = time_calls(torch, pre, args.prefill_steps, 5)
-        flops = 2.0 * Mp * gu.N * gu.K + 2.0 * Mp * gu.r * (gu.n_seg * gu.K + gu.N)
-        tf = flops / (msp * 1e-3) / 1e12
-        out["prefill"] = {"workload": f"spark_gateup prefill K={gu.K} N={gu.N} r={gu.r} M={Mp}",
-                          "ms_per_call": round(msp, 5), "tflops": round(tf, 2),
-                          "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    if not args.no_table:
+        table = []
+        for name, Ms in (("spark_up", (4, 16)), ("spark_down", (1, 8, 32)), ("minicpm_gate", (1,)),
+                         ("minicpm_down", (1,)), ("spark_gateup", (1,))):
+            for m in Ms:
+                r = Runner(dv, torch, layers[name], m, 32)
+                t, _ = time_calls(torch, r.decode, args.table_steps, 20)
+                g = r.algo_bytes() / (t * 1e-3) / 1e9
+                table.append({"workload": f"{name} decode M={m}", "us_per_call": round(t * 1e3, 3),
+                              "gbs": round(g, 1), "frac_hbm": round(g / HBM_PEAK_GBS, 4)})
+                r.free()
+        for name, m in (("spark_gateup", 512), ("spark_gateup", 2048), ("minicpm_gate", 4096),
+                        ("minicpm_down", 4096)):
+            r = Runner(dv, torch, layers[name], m, m, min_bytes=256 << 20, max_copies=16)
+            t, _ = time_calls(torch, r.prefill, args.prefill_steps, 3)
+            tf = r.flops() / (t * 1e-3) / 1e12
+            table.append({"workload": f"{name} prefill M={m}", "us_per_call": round(t * 1e3, 2),
+                          "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
+            r.free()
+        out["table"] = table
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(up, blob, x_bits, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(up, head_blob, head_x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
