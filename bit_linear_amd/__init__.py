@@ -49,6 +49,15 @@ class DvssqError(RuntimeError):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run bit_linear_amd/build.py (hipcc, gfx950)")
 
+# One HIP runtime per process: PyTorch loads the HIP runtime it ships by path.
+# Importing it first lets libdvssq.so bind to that same runtime (same soname)
+# instead of loading a second copy from the ROCm install, which would then
+# compete with PyTorch's for the device.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 _lib = C.CDLL(LIB_PATH)
 _P = C.c_void_p
 _lib.dvssq_pack_info.restype = C.c_int

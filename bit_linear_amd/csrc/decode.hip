@@ -566,17 +566,17 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
     static bool done = false;
     const hipError_t e = set_lds(reinterpret_cast<const void *>(decode_kernel<MSUB, MAXS, true>), lds, done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_kernel<MSUB, MAXS, true>), dim3(a.nprod + groups), dim3(kThreads), lds, s, a);
-    return hipGetLastError();
+    return launch_kernel(reinterpret_cast<const void *>(decode_kernel<MSUB, MAXS, true>), dim3(a.nprod + groups),
+                         dim3(kThreads), lds, s, a);
   }
-  hipLaunchKernelGGL(decode_prologue_kernel, dim3(a.nprod), dim3(kThreads), prologue_lds_bytes(a.unit), s, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_kernel(reinterpret_cast<const void *>(decode_prologue_kernel), dim3(a.nprod), dim3(kThreads),
+                               prologue_lds_bytes(a.unit), s, a);
   if (e != hipSuccess) return e;
   static bool done = false;
   e = set_lds(reinterpret_cast<const void *>(decode_kernel<MSUB, MAXS, false>), lds, done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<MSUB, MAXS, false>), dim3(groups), dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  return launch_kernel(reinterpret_cast<const void *>(decode_kernel<MSUB, MAXS, false>), dim3(groups), dim3(kThreads),
+                       lds, s, a);
 }
 
 template <int MSUB>

@@ -40,7 +40,9 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 16;               // packed rows per MFMA tile
 constexpr int kProdRows = 8;            // activation rows per producer
 constexpr int kTab = 4;                 // token rows of the per-row LDS tables
-constexpr int kUDwords = 4;             // U-slab dwords per thread (<= 7 tiles x 16 rows x r <= 64)
+constexpr int kMaxRT = 7;               // largest number of 16-row tiles per workgroup
+constexpr int kUVec = kMaxRT * kTile * 64 * 2 / 16 / 64;  // 16-byte U loads per spare lane (r <= 64)
+constexpr int kRowVec = (kMaxRT * kTile + 63) / 64;         // column / INT8-scale loads per spare lane
 constexpr long kSpinLimit = 1L << 22;   // bounded wait for a producer flag
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -72,6 +74,27 @@ __device__ __forceinline__ void drain_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Groups of 64 inputs per wavefront when KQ wavefronts split ngrp groups: an
+// even number, so that every wavefront's first group is even and its group
+// scales load as aligned pairs.
+__host__ __device__ inline int groups_per_wave(int ngrp, int KQ) { return ((ngrp + KQ - 1) / KQ + 1) & ~1; }
+
+// Buffer resources over one array (raw addressing, byte offsets).  A load at
+// an offset at or past num_records returns zeros and makes no memory access.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
 __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
@@ -259,6 +282,64 @@ __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
 
 // --------------------------------------------------------------------------- consumer
 
+// Spare wavefronts of a consumer workgroup: load the U rows, output columns
+// and INT8 row scales of the workgroup's rows (wbase .. wbase + wrows - 1),
+// then wait for the t producers of the K-range and sum their partial t.  Each
+// result goes to LDS between the workgroup's two barriers, (A) and (B), which
+// the compute wavefronts pass at the same points of their own path.
+template <bool T8>
+__device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows, int u0, int nu, u32x4 *ush,
+                      int *cols, float *s8s, float *ts) {
+  const int lane = threadIdx.x & 63;
+  const int M = a.M, nsp = a.nsr_pad;
+  u32x4 uv[kUVec];
+  uint32_t rv[kRowVec], sv[kRowVec];
+  const auto ru = make_rsrc(a.U, static_cast<uint32_t>(a.N) * a.r * 2);
+  const uint32_t ub = static_cast<uint32_t>(wbase) * a.r * 2, ubytes = static_cast<uint32_t>(wrows) * a.r * 2;
+#pragma unroll
+  for (int j = 0; j < kUVec; ++j) {
+    const uint32_t o = static_cast<uint32_t>(sw * 64 + lane + nsw * 64 * j) * 16;
+    uv[j] = buf_load16(ru, o < ubytes ? ub + o : kOutOfRange);
+  }
+  const auto ri = make_rsrc(a.idx, static_cast<uint32_t>(a.N) * 4);
+  const auto rs8 = make_rsrc(a.s8, static_cast<uint32_t>(a.n8) * 4);
+#pragma unroll
+  for (int j = 0; j < kRowVec; ++j) {
+    const int e = sw * 64 + lane + nsw * 64 * j;
+    const bool ok = e < wrows;
+    rv[j] = buf_load4(ri, ok ? static_cast<uint32_t>(wbase + e) * 4 : kOutOfRange);
+    sv[j] = T8 ? buf_load4(rs8, ok ? static_cast<uint32_t>(wbase + e - a.n4) * 4 : kOutOfRange) : 0u;
+  }
+  __syncthreads();   // (A)
+#pragma unroll
+  for (int j = 0; j < kUVec; ++j)
+    if (sw * 64 + lane + nsw * 64 * j < kUVec * 64) ush[sw * 64 + lane + nsw * 64 * j] = uv[j];
+#pragma unroll
+  for (int j = 0; j < kRowVec; ++j) {
+    const int e = sw * 64 + lane + nsw * 64 * j;
+    if (e < kMaxRT * kTile) {
+      cols[e] = static_cast<int>(rv[j]);
+      s8s[e] = T8 ? __uint_as_float(sv[j]) : 1.0f;
+    }
+  }
+  for (int i = sw * 64 + lane; i < nu; i += nsw * 64) {
+    long spins = 0;
+    while (ld_dev(a.flag + u0 + i) != a.gen && spins < kSpinLimit) {
+      __builtin_amdgcn_s_sleep(1);
+      ++spins;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int e = sw * 64 + lane; e < M * nsp; e += nsw * 64) {
+    const int m = e / nsp, i = e % nsp;
+    float s = 0.0f;
+    if (i < a.nsr)
+      for (int u = 0; u < nu; ++u) s += ld_dev(a.tp + (static_cast<int64_t>(u0 + u) * kDecodeRows + m) * nsp + i);
+    ts[e] = s;
+  }
+  __syncthreads();   // (B)
+}
+
 // MT: largest M (1 or 4); C: 256-blocks per rotation unit; MAXG: groups of 64
 // inputs loaded per wavefront; T8: INT8 tier.  a.RT tiles of 16 rows per
 // workgroup, KQ = 15 / RT wavefronts per tile; the wavefronts from RT * KQ on
@@ -287,7 +368,7 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   constexpr int P = 256 * C;
   const int k0 = split * KW;
   const int ngrp = KW / kGroup;
-  const int gpw = (ngrp + KQ - 1) / KQ;
+  const int gpw = groups_per_wave(ngrp, KQ);
   const int g0 = kq * gpw, g1 = min(ngrp, g0 + gpw);
   const int gs = max(0, min(g0, ngrp - MAXG));          // first loaded group (MAXG <= ngrp)
   const int nu = KW / P, u0 = k0 / P;
@@ -302,114 +383,101 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   int *x8 = reinterpret_cast<int *>(xs2 + M * KW);                   // [ngrp][4]
   float *esc = reinterpret_cast<float *>(x8 + ngrp * kTab);          // [nu][4]
   float *red = esc + nu * kTab;                                      // [kWaves][4][64]
-  uint32_t *ush = reinterpret_cast<uint32_t *>(red + kWaves * 4 * 64);  // [kUDwords * kThreads]
-  float *tpart = reinterpret_cast<float *>(ush + kUDwords * kThreads);     // [nu][M][nsp]
-  float *ts = tpart + nu * M * nsp;                                  // [M][nsp]
+  u32x4 *ush = reinterpret_cast<u32x4 *>(red + kWaves * 4 * 64);   // U rows wbase .. wbase + 16 RT - 1
+  int *cols = reinterpret_cast<int *>(ush + kUVec * 64);           // [16 RT] output columns
+  float *s8s = reinterpret_cast<float *>(cols + kMaxRT * kTile);   // [16 RT] INT8 row scales
+  float *ts = s8s + kMaxRT * kTile;                                // [M][nsp]
 
-  // ---- 1. activations of this wavefront's first item, before anything else
-  int item = wave;
+  const int wbase = (T8 ? a.n4 : 0) + min(tile0, ntiles - 1) * kTile;   // first packed row of the workgroup
+  if (!active) {
+    const int wrows = min(RT * kTile, (T8 ? a.n4 + a.n8 : a.n4) - wbase);
+    spare<T8>(a, wave - NCW, kWaves - NCW, wbase, wrows, u0, nu, ush, cols, s8s, ts);
+    return;
+  }
+
+  // ---- 1. activations of this wavefront's first item, before anything else.
+  // Loads go through buffer resources: a lane with nothing to load gets an
+  // offset past the end, which reads zeros without touching memory, so the
+  // loads are issued unconditionally and each wait covers only what it needs.
+  const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * a.K * 2);
   u32x2 xw[C];
   {
-    const int it = min(item, nitem - 1), m = it % M, u = it / M;
+    const int m = wave % M, u = wave / M;
+    const uint32_t off = wave < nitem ? (static_cast<uint32_t>(m) * a.K + k0 + u * P + 16 * n + 4 * q) * 2
+                                        : kOutOfRange;
+#pragma unroll
+    for (int c = 0; c < C; ++c) xw[c] = buf_load8(rx, off + 512 * c);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. weight loads of this wavefront
+  u32x2 c4[T8 ? 1 : MAXG];
+  uint32_t sb[T8 ? 1 : MAXG / 2];                      // bf16 group scales, two per dword
+  u32x4 c8[T8 ? MAXG : 1];
+  const bool load_w = row_ok;
+  if constexpr (!T8) {
+    const auto r4 = make_rsrc(a.q4, static_cast<uint32_t>(a.n4) * (a.K / 2));
+    const auto rs = make_rsrc(a.s4, static_cast<uint32_t>(a.n4) * KG * 2);
+    const uint32_t o4 = load_w ? static_cast<uint32_t>(plc) * (a.K / 2) + (k0 + 64 * gs + 16 * q) / 2 : kOutOfRange;
+    const uint32_t os = load_w ? (static_cast<uint32_t>(plc) * KG + k0 / kGroup + gs) * 2 : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < MAXG; ++i) c4[i] = buf_load8(r4, gs + i >= g0 && gs + i < g1 ? o4 + 32 * i : kOutOfRange);
+#pragma unroll
+    for (int i = 0; i < MAXG / 2; ++i)
+      sb[i] = buf_load4(rs, gs + 2 * i + 1 >= g0 && gs + 2 * i < g1 ? os + 4 * i : kOutOfRange);
+  } else {
+    const auto r8 = make_rsrc(a.q8, static_cast<uint32_t>(a.n8) * a.K);
+    const uint32_t o8 = load_w ? static_cast<uint32_t>(plc) * a.K + k0 + 64 * gs + 16 * q : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < MAXG; ++i) c8[i] = buf_load16(r8, gs + i >= g0 && gs + i < g1 ? o8 + 64 * i : kOutOfRange);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. items -> quantized int8 planes in LDS.  The first item is handled
+  // outside any loop, so its wait covers only the activation loads issued
+  // before the weights; later items (M > 1) are loaded here.
+  auto quantize = [&](int it, const u32x2(&xv)[C]) {
+    const int m = it % M, u = it / M;
+    float y[C][4];
+    rotate_item<C>(a, xv, y);
+    float mx = 0.0f;
 #pragma unroll
     for (int c = 0; c < C; ++c)
-      xw[c] = *reinterpret_cast<const u32x2 *>(a.x + static_cast<int64_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n + 4 * q);
-  }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(y[c][j]));
+    mx = wave_max(mx);
+    // 15-bit quantization: max |X| in [2^13, 2^14]
+    const int e = (mx > 0.0f && mx <= 3.0e38f) ? max(-100, min(114, ilogbf(mx) - 13)) : 0;
+    const float down = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      int X[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) X[j] = __float2int_rn(y[c][j] * down);
+      const int kk = u * P + 256 * c + 16 * n + 4 * q;
+      *reinterpret_cast<uint32_t *>(xs1 + m * KW + kk) =
+          pack_bytes((X[0] + 128) >> 8, (X[1] + 128) >> 8, (X[2] + 128) >> 8, (X[3] + 128) >> 8);
+      *reinterpret_cast<uint32_t *>(xs2 + m * KW + kk) = pack_bytes(X[0], X[1], X[2], X[3]);
+      // group of 64 = kk / 64: the lanes with the same n / 4
+      int gsum = quad_sum(X[0] + X[1] + X[2] + X[3]);
+      gsum += __shfl_xor(gsum, 16, 64);
+      gsum += __shfl_xor(gsum, 32, 64);
+      if ((lane & 0x33) == 0) x8[(kk / kGroup) * kTab + m] = 8 * gsum;
+    }
+    if (lane == 0) esc[u * kTab + m] = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
+  };
+  if (wave < nitem) quantize(wave, xw);
   __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 2. weight loads of this wavefront, then the U slab, columns, INT8 scale
-  u32x2 c4[T8 ? 1 : MAXG];
-  uint32_t sb[T8 ? 1 : MAXG];
-  u32x4 c8[T8 ? MAXG : 1];
-  if (active) {
-    const uint8_t *p4 = a.q4 + static_cast<int64_t>(plc) * (a.K / 2) + (k0 + 64 * gs + 16 * q) / 2;
-    const uint16_t *ps = a.s4 + static_cast<int64_t>(plc) * KG + k0 / kGroup + gs;
-    const int8_t *p8 = a.q8 + static_cast<int64_t>(plc) * a.K + k0 + 64 * gs + 16 * q;
+  for (int it = wave + NCW; it < nitem; it += NCW) {
+    const int m = it % M, u = it / M;
+    u32x2 xv[C];
 #pragma unroll
-    for (int i = 0; i < MAXG; ++i) {
-      if constexpr (!T8) {
-        c4[i] = *reinterpret_cast<const u32x2 *>(p4 + 32 * i);
-        sb[i] = ps[i];
-      } else {
-        c8[i] = *reinterpret_cast<const u32x4 *>(p8 + 64 * i);
-      }
-    }
+    for (int c = 0; c < C; ++c)
+      xv[c] = *reinterpret_cast<const u32x2 *>(a.x + static_cast<int64_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n +
+                                                4 * q);
+    quantize(it, xv);
   }
-  // U rows of the workgroup's tiles: one contiguous range, fetched as aligned dwords
-  const int wbase = (T8 ? a.n4 : 0) + min(tile0, ntiles - 1) * kTile;
-  const int64_t ue0 = static_cast<int64_t>(wbase) * a.r;
-  const int64_t ud0 = ue0 / 2;
-  const int64_t ud_last = (static_cast<int64_t>(a.N) * a.r + 1) / 2 - 1;
-  const uint32_t *U32 = reinterpret_cast<const uint32_t *>(a.U);
-  uint32_t uw[kUDwords];
-#pragma unroll
-  for (int j = 0; j < kUDwords; ++j) uw[j] = U32[std::min<int64_t>(ud0 + tid + kThreads * j, ud_last)];
-  const int col = a.idx[pc];
-  const float s8 = T8 ? a.s8[plc] : 1.0f;
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 3. items -> quantized int8 planes in LDS (compute wavefronts); the
-  // spare wavefronts wait for the t producers of the range and copy t
-  if (active) {
-    for (; item < nitem; item += NCW) {
-      const int m = item % M, u = item / M;
-      if (item != wave) {   // later items (M > 1): loaded now
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-          xw[c] = *reinterpret_cast<const u32x2 *>(a.x + static_cast<int64_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n +
-                                                    4 * q);
-      }
-      float y[C][4];
-      rotate_item<C>(a, xw, y);
-      float mx = 0.0f;
-#pragma unroll
-      for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(y[c][j]));
-      mx = wave_max(mx);
-      // 15-bit quantization: max |X| in [2^13, 2^14]
-      const int e = (mx > 0.0f && mx <= 3.0e38f) ? max(-100, min(114, ilogbf(mx) - 13)) : 0;
-      const float down = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        int X[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) X[j] = __float2int_rn(y[c][j] * down);
-        const int kk = u * P + 256 * c + 16 * n + 4 * q;
-        *reinterpret_cast<uint32_t *>(xs1 + m * KW + kk) =
-            pack_bytes((X[0] + 128) >> 8, (X[1] + 128) >> 8, (X[2] + 128) >> 8, (X[3] + 128) >> 8);
-        *reinterpret_cast<uint32_t *>(xs2 + m * KW + kk) = pack_bytes(X[0], X[1], X[2], X[3]);
-        // group of 64 = kk / 64: the lanes with the same n / 4
-        int gsum = quad_sum(X[0] + X[1] + X[2] + X[3]);
-        gsum += __shfl_xor(gsum, 16, 64);
-        gsum += __shfl_xor(gsum, 32, 64);
-        if ((lane & 0x33) == 0) x8[(kk / kGroup) * kTab + m] = 8 * gsum;
-      }
-      if (lane == 0) esc[u * kTab + m] = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
-    }
-  } else {
-    const int sw = wave - NCW, nsw = kWaves - NCW;       // spare wavefront index and count
-    for (int i = sw * 64 + lane; i < nu; i += nsw * 64) {
-      long spins = 0;
-      while (ld_dev(a.flag + u0 + i) != a.gen && spins < kSpinLimit) {
-        __builtin_amdgcn_s_sleep(1);
-        ++spins;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    for (int e = sw * 64 + lane; e < nu * M * a.nsr; e += nsw * 64) {
-      const int i = e % a.nsr, mu = e / a.nsr;
-      tpart[mu * nsp + i] = ld_dev(a.tp + (static_cast<int64_t>(u0 + mu / M) * kDecodeRows + mu % M) * nsp + i);
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < M * nsp; e += kThreads) {
-    const int m = e / nsp, i = e % nsp;
-    float s = 0.0f;
-    if (i < a.nsr)
-      for (int u = 0; u < nu; ++u) s += tpart[(u * M + m) * nsp + i];
-    ts[e] = s;
-  }
+  __syncthreads();   // (A) planes, group sums and unit scales are in LDS
 
   // ---- 4. main loop: two int8 MFMAs per group, straight-line and masked; the
   // MFMAs of group i+1 are issued before the scalar work of group i
@@ -417,82 +485,84 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   float acc[R], accu[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = accu[r] = 0.0f;
-  const int mA = MT == 1 ? 0 : min(n, M - 1);
-  const int8_t *pa1 = xs1 + mA * KW + 16 * q, *pa2 = xs2 + mA * KW + 16 * q;
-  auto bop = [&](int i) -> u32x4 {
-    u32x4 b;
-    if constexpr (!T8) {
-      const uint32_t w0 = c4[i][0], w1 = c4[i][1];
-      b[0] = w0 & 0x0F0F0F0Fu;
-      b[1] = (w0 >> 4) & 0x0F0F0F0Fu;
-      b[2] = w1 & 0x0F0F0F0Fu;
-      b[3] = (w1 >> 4) & 0x0F0F0F0Fu;
-    } else {
-      b = c8[i];
-    }
-    return b;
-  };
-  i32x4 d1, d2;
   {
-    const u32x4 b = bop(0);
-    d1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * gs), b, zi);
-    d2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * gs), b, zi);
-  }
+    const int mA = MT == 1 ? 0 : min(n, M - 1);
+    const int8_t *pa1 = xs1 + mA * KW + 16 * q, *pa2 = xs2 + mA * KW + 16 * q;
+    auto bop = [&](int i) -> u32x4 {
+      u32x4 b;
+      if constexpr (!T8) {
+        const uint32_t w0 = c4[i][0], w1 = c4[i][1];
+        b[0] = w0 & 0x0F0F0F0Fu;
+        b[1] = (w0 >> 4) & 0x0F0F0F0Fu;
+        b[2] = w1 & 0x0F0F0F0Fu;
+        b[3] = (w1 >> 4) & 0x0F0F0F0Fu;
+      } else {
+        b = c8[i];
+      }
+      return b;
+    };
+    i32x4 d1, d2;
+    {
+      const u32x4 b = bop(0);
+      d1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * gs), b, zi);
+      d2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * gs), b, zi);
+    }
 #pragma unroll
-  for (int i = 0; i < MAXG; ++i) {
-    const int g = gs + i;
-    const bool valid = g >= g0 && g < g1;
-    i32x4 e1 = zi, e2 = zi;
-    if (i + 1 < MAXG) {
-      const u32x4 b = bop(i + 1 < MAXG ? i + 1 : i);
-      e1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * (g + 1)), b, zi);
-      e2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * (g + 1)), b, zi);
-    }
-    float sg;
-    i32x4 xg = zi;
-    if constexpr (!T8) {
-      sg = valid ? bf16_to_f32(sb[i]) : 0.0f;
-      xg = *reinterpret_cast<const i32x4 *>(x8 + g * kTab);
-    } else {
-      sg = valid ? 1.0f : 0.0f;
-    }
+    for (int i = 0; i < MAXG; ++i) {
+      const int g = gs + i;
+      const bool valid = g >= g0 && g < g1;
+      i32x4 e1 = zi, e2 = zi;
+      if (i + 1 < MAXG) {
+        const u32x4 b = bop(i + 1 < MAXG ? i + 1 : i);
+        e1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * (g + 1)), b, zi);
+        e2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * (g + 1)), b, zi);
+      }
+      float sg;
+      i32x4 xg = zi;
+      if constexpr (!T8) {
+        const uint32_t sw = sb[i / 2];
+        sg = valid ? __uint_as_float((i & 1) ? (sw & 0xFFFF0000u) : (sw << 16)) : 0.0f;
+        xg = *reinterpret_cast<const i32x4 *>(x8 + g * kTab);
+      } else {
+        sg = valid ? 1.0f : 0.0f;
+      }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int v = (d1[r] << 8) + d2[r] - xg[r];
-      accu[r] = fmaf(sg, static_cast<float>(v), accu[r]);
-    }
-    const bool bnd = valid && (((g + 1) % gpu == 0) || (g == g1 - 1));
-    const f32x4 ev = *reinterpret_cast<const f32x4 *>(esc + (g / gpu) * kTab);
+      for (int r = 0; r < R; ++r) {
+        const int v = (d1[r] << 8) + d2[r] - xg[r];
+        accu[r] = fmaf(sg, static_cast<float>(v), accu[r]);
+      }
+      const bool bnd = valid && (((g + 1) % gpu == 0) || (g == g1 - 1));
+      const f32x4 ev = *reinterpret_cast<const f32x4 *>(esc + (g / gpu) * kTab);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      acc[r] = fmaf(bnd ? ev[r] : 0.0f, accu[r], acc[r]);
-      accu[r] = bnd ? 0.0f : accu[r];
+      for (int r = 0; r < R; ++r) {
+        acc[r] = fmaf(bnd ? ev[r] : 0.0f, accu[r], acc[r]);
+        accu[r] = bnd ? 0.0f : accu[r];
+      }
+      d1 = e1;
+      d2 = e2;
+      __builtin_amdgcn_sched_barrier(0);
     }
-    d1 = e1;
-    d2 = e2;
-    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- 5. partial tiles and U slabs -> LDS
+  // ---- 5. partial tiles -> LDS
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = r < R ? acc[r] : 0.0f;
-#pragma unroll
-  for (int j = 0; j < kUDwords; ++j) ush[tid + kThreads * j] = uw[j];
-  __syncthreads();
-  if (kq != 0 || !active) return;
+  __syncthreads();   // (B) partial tiles, U rows, columns, INT8 scales and t are in LDS
+  if (kq != 0) return;
 
   // ---- 6. first wavefront of each tile: sum the K-slices, add the low-rank term
+  const int col = cols[rt * kTile + n];
   f32x4 cacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float s = 0.0f;
     for (int w = 0; w < KQ; ++w) s += red[((rt * KQ + w) * 4 + r) * 64 + lane];
-    cacc[r] = s * s8;
+    cacc[r] = s * s8s[rt * kTile + n];
   }
   {
-    const int seg = col / (a.N / a.n_seg);
+    const int seg = (a.n_seg == 2 && plc >= rows / 2) ? 1 : 0;   // segments in packed order
     const uint16_t *u16 = reinterpret_cast<const uint16_t *>(ush);
-    const int uoff = static_cast<int>(ue0 - 2 * ud0) + (base - wbase) * a.r;
+    const int uoff = (base - wbase) * a.r;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
     for (int st = 0; st < nsp / 32; ++st) {
       u32x4 bv;
@@ -580,7 +650,8 @@ size_t producer_lds(int unit) {
 size_t consumer_lds(int M, int unit, int KW, int nsr_pad) {
   const size_t nu = KW / unit, ngrp = KW / kGroup;
   return static_cast<size_t>(2) * M * KW + ngrp * kTab * 4 + nu * kTab * 4 + static_cast<size_t>(kWaves) * 4 * 64 * 4 +
-         static_cast<size_t>(kUDwords) * kThreads * 4 + nu * M * nsr_pad * 4 + static_cast<size_t>(M) * nsr_pad * 4;
+         static_cast<size_t>(kUVec) * 64 * 16 + 2 * kMaxRT * kTile * 4 +
+         static_cast<size_t>(M) * nsr_pad * 4;
 }
 
 size_t small_lds(int M, int unit, int KW, int nsr_pad) {
@@ -600,8 +671,8 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
     }
   }
   const int grid = a.nprod + (a.g4 + a.g8) * a.S;
-  hipLaunchKernelGGL((decode_small_kernel<MT, C, MAXG>), dim3(grid), dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  return launch_kernel(reinterpret_cast<const void *>(decode_small_kernel<MT, C, MAXG>), dim3(grid), dim3(kThreads), lds,
+                       s, a);
 }
 
 template <int MT, int C>
@@ -631,6 +702,11 @@ hipError_t launch_m(const DecodeArgs &a, hipStream_t s) {
 // fewer workgroups.
 bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
   if (M < 1 || M > 4) return false;
+  // byte offsets of the buffer loads stay below 2^31
+  const int64_t big = std::max<int64_t>(static_cast<int64_t>(L.n_int4) * L.K / 2,
+                                        std::max<int64_t>(static_cast<int64_t>(L.n_int8) * L.K,
+                                                          static_cast<int64_t>(L.N) * L.r * 2));
+  if (big >= (int64_t{1} << 31) || static_cast<int64_t>(M) * L.K * 2 >= (int64_t{1} << 31)) return false;
   const int unit = L.block > 256 ? L.block : 256;
   if (L.K % unit) return false;
   const int nunit = L.K / unit;
@@ -644,7 +720,7 @@ bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
     for (int S = 1; S <= kMaxSplit && S <= nunit; ++S) {
       if (nunit % S) continue;
       const int KW = L.K / S, ngrp = KW / kGroup;
-      const int gpw = (ngrp + KQ - 1) / KQ;
+      const int gpw = groups_per_wave(ngrp, KQ);
       if (gpw > gmax) continue;
       const int maxg = gpw <= 4 ? 4 : 8;
       if (maxg > ngrp) continue;

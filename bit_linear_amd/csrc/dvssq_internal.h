@@ -19,6 +19,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Launch of a kernel whose only parameter is an argument struct.  Returns the
+// status of this launch itself (not a sticky error left by earlier calls).
+template <typename Args>
+inline hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, size_t lds, hipStream_t s, const Args &a) {
+  void *args[] = {const_cast<Args *>(&a)};
+  return hipLaunchKernel(fn, grid, block, args, lds, s);
+}
+
 constexpr int kGroup = 64;      // INT4 group size
 constexpr int kDecodeRows = 32; // M rows held by the decode workspace (MFMA tile height)
 

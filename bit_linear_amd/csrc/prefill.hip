@@ -183,8 +183,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
     attr_set = true;
   }
   const int grid = (a.n4_tiles + a.n8_tiles) * a.m_tiles;
-  hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  return launch_kernel(reinterpret_cast<const void *>(prefill_kernel), dim3(grid), dim3(kThreads), lds, s, a);
 }
 
 }  // namespace dvssq

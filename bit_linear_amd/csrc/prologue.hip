@@ -216,8 +216,7 @@ hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
     }
   }
   dim3 grid((a.M + MT - 1) / MT, n_wg_blocks);
-  hipLaunchKernelGGL((prologue_kernel<VPL, MT>), grid, dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  return launch_kernel(reinterpret_cast<const void *>(prologue_kernel<VPL, MT>), grid, dim3(kThreads), lds, s, a);
 }
 
 }  // namespace
