@@ -243,7 +243,22 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.S = S;
   d.RT = small ? sp.RT : 0;
   d.MAXG = small ? sp.MAXG : 0;
+  d.KQ = small ? sp.KQ : 0;
+  d.GPW = small ? sp.GPW : 0;
   d.KW = L->K / d.S;
+  if (small) {
+    d.ngrp_w = d.KW / kGroup;
+    d.nu_w = d.KW / d.unit;
+    d.magic_s = d.S > 1 ? static_cast<uint32_t>(((uint64_t{1} << 32) + d.S - 1) / d.S) : 0u;
+    d.lut_rt = d.lut_kq = d.lut_m = d.lut_u = 0;
+    for (int w = 0; w < 16; ++w) {
+      const uint64_t rt = static_cast<uint64_t>(std::min(w / sp.KQ, 15)), kq = static_cast<uint64_t>(w % sp.KQ);
+      d.lut_rt |= rt << (4 * w);
+      d.lut_kq |= kq << (4 * w);
+      d.lut_m |= static_cast<uint64_t>(w % M) << (4 * w);
+      d.lut_u |= static_cast<uint64_t>(w / M) << (4 * w);
+    }
+  }
   d.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
   d.fused = M <= kDecodeFusedMaxM ? 1 : 0;
   d.hscale = inv_sqrt_block(L->block);

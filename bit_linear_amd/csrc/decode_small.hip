@@ -112,6 +112,19 @@ __device__ __forceinline__ uint32_t sylvester_bf16(int a, int b, int R) {
   return (__popc(a & b & (R - 1)) & 1) ? 0xBF80u : 0x3F80u;
 }
 
+// bf16 entries (4q + j, n), j < 4, of H_16 (Sylvester, +-1) as two packed
+// pairs.  The sign is the parity of (4q + j) & n = parity(q & (n >> 2)) xor
+// parity(j & (n & 3)); the second term, as a 4-bit mask over j, is 0x0, 0xA,
+// 0xC, 0x6 for n & 3 = 0 .. 3.
+__device__ __forceinline__ u32x2 sylvester_h16(int n, int q) {
+  uint32_t t = (0x6CA0u >> (4 * (n & 3))) & 0xFu;
+  t ^= (__popc(q & (n >> 2)) & 1) ? 0xFu : 0u;
+  u32x2 h;
+  h[0] = 0x3F803F80u | ((t & 1u) << 15) | ((t & 2u) << 30);
+  h[1] = 0x3F803F80u | ((t & 4u) << 13) | ((t & 8u) << 28);
+  return h;
+}
+
 // cross-lane steps on the DPP network (rows of 16 lanes): xor 1, xor 2 inside
 // a quad, mirror inside 8 and inside 16 lanes
 #define DVSSQ_DPP(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), (ctrl), 0xF, 0xF, false)
@@ -155,12 +168,13 @@ __device__ __forceinline__ void rotate_item(const DecodeArgs &a, const u32x2 (&x
     }
     return;
   }
-  const int Rb = min(a.block / 16, 16);
-  u32x2 h1, h2;
-  h1[0] = sylvester_bf16(4 * q, n, 16) | (sylvester_bf16(4 * q + 1, n, 16) << 16);
-  h1[1] = sylvester_bf16(4 * q + 2, n, 16) | (sylvester_bf16(4 * q + 3, n, 16) << 16);
-  h2[0] = sylvester_bf16(4 * q, n, Rb) | (sylvester_bf16(4 * q + 1, n, Rb) << 16);
-  h2[1] = sylvester_bf16(4 * q + 2, n, Rb) | (sylvester_bf16(4 * q + 3, n, Rb) << 16);
+  const u32x2 h1 = sylvester_h16(n, q);
+  u32x2 h2 = h1;
+  if (a.block < 256) {
+    const int Rb = a.block / 16;
+    h2[0] = sylvester_bf16(4 * q, n, Rb) | (sylvester_bf16(4 * q + 1, n, Rb) << 16);
+    h2[1] = sylvester_bf16(4 * q + 2, n, Rb) | (sylvester_bf16(4 * q + 3, n, Rb) << 16);
+  }
   const f32x4 zf = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < C; ++c) {
@@ -342,42 +356,34 @@ __device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows
 
 // MT: largest M (1 or 4); C: 256-blocks per rotation unit; MAXG: groups of 64
 // inputs loaded per wavefront; T8: INT8 tier.  a.RT tiles of 16 rows per
-// workgroup, KQ = 15 / RT wavefronts per tile; the wavefronts from RT * KQ on
-// wait for t.
+// workgroup, a.KQ wavefronts per tile splitting the K-range in runs of a.GPW
+// groups (an even number); the wavefronts from RT * KQ on are spare.  Values
+// that are the same across a wavefront are kept in scalar registers: the
+// vector ALU, shared by the four wavefronts of each SIMD, is the scarce unit.
 template <int MT, int C, int MAXG, bool T8>
 __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   constexpr int R = MT == 1 ? 1 : 4;    // accumulator rows per lane that can hold a token
-  const int RT = a.RT, KQ = (kWaves - 1) / RT, NCW = RT * KQ;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, q = lane >> 4;
-  const bool active = wave < NCW;                       // compute wavefront
-  const int rt = min(wave / KQ, RT - 1), kq = wave % KQ;
-  const int grp = cidx / a.S, split = cidx % a.S;
-  const int rows = T8 ? a.n8 : a.n4;
-  const int ntiles = (rows + kTile - 1) / kTile;
-  const int tile0 = (T8 ? grp - a.g4 : grp) * RT;       // first tile of the workgroup inside the tier
-  const int tile = tile0 + rt;
-  const bool tile_ok = tile < ntiles;
-  const int gbase = min(tile, ntiles - 1) * kTile;
-  const int pl = gbase + n;
-  const bool row_ok = tile_ok && pl < rows;
-  const int plc = min(pl, rows - 1);
-  const int base = (T8 ? a.n4 : 0) + gbase;             // first packed row of the tile
-  const int pc = base + (plc - gbase);
-  const int M = a.M, KW = a.KW;
   constexpr int P = 256 * C;
+  constexpr int gpu = P / kGroup;       // groups per rotation unit
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  // per-wavefront and per-workgroup indices from host-made tables, without divisions
+  const int RT = a.RT, KQ = a.KQ, NCW = RT * KQ;
+  const int rt = static_cast<int>((a.lut_rt >> (4 * wave)) & 15u), kq = static_cast<int>((a.lut_kq >> (4 * wave)) & 15u);
+  const int grp = a.S == 1 ? cidx : static_cast<int>(__umulhi(static_cast<uint32_t>(cidx), a.magic_s));
+  const int split = cidx - grp * a.S;
+  const int rows = T8 ? a.n8 : a.n4;
+  const int ntiles = static_cast<int>((static_cast<uint32_t>(rows) + kTile - 1) >> 4);
+  const int tile0 = (T8 ? grp - a.g4 : grp) * RT;       // first tile of the workgroup inside the tier
+  const int wbase = (T8 ? a.n4 : 0) + min(tile0, ntiles - 1) * kTile;   // first packed row of the workgroup
+  const int M = a.M, KW = a.KW;
   const int k0 = split * KW;
-  const int ngrp = KW / kGroup;
-  const int gpw = groups_per_wave(ngrp, KQ);
-  const int g0 = kq * gpw, g1 = min(ngrp, g0 + gpw);
-  const int gs = max(0, min(g0, ngrp - MAXG));          // first loaded group (MAXG <= ngrp)
-  const int nu = KW / P, u0 = k0 / P;
-  constexpr int gpu = P / kGroup;
-  const int KG = a.K / kGroup;
+  const int ngrp = a.ngrp_w;                            // groups of 64 in the K-range
+  const int nu = a.nu_w, u0 = split * nu;               // rotation units in the K-range, first one
   const int nsp = a.nsr_pad;
   const int nitem = M * nu;                             // (row, unit) items to rotate
 
-  // LDS: int8 planes, 8 x group sums, unit scales, partial tiles, U slabs, t
+  // LDS: int8 planes, 8 x group sums, unit scales, partial tiles, U rows, columns, INT8 scales, t
   int8_t *xs1 = reinterpret_cast<int8_t *>(smem);
   int8_t *xs2 = xs1 + M * KW;
   int *x8 = reinterpret_cast<int *>(xs2 + M * KW);                   // [ngrp][4]
@@ -388,12 +394,24 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   float *s8s = reinterpret_cast<float *>(cols + kMaxRT * kTile);   // [16 RT] INT8 row scales
   float *ts = s8s + kMaxRT * kTile;                                // [M][nsp]
 
-  const int wbase = (T8 ? a.n4 : 0) + min(tile0, ntiles - 1) * kTile;   // first packed row of the workgroup
-  if (!active) {
+  if (wave >= NCW) {
     const int wrows = min(RT * kTile, (T8 ? a.n4 + a.n8 : a.n4) - wbase);
     spare<T8>(a, wave - NCW, kWaves - NCW, wbase, wrows, u0, nu, ush, cols, s8s, ts);
     return;
   }
+  const int tile = tile0 + rt;
+  const bool tile_ok = tile < ntiles;
+  const int gbase = min(tile, ntiles - 1) * kTile;
+  const int base = (T8 ? a.n4 : 0) + gbase;             // first packed row of the tile
+  const int pl = gbase + n;                             // this lane's row inside the tier
+  const bool row_ok = tile_ok && pl < rows;
+  const int plc = min(pl, rows - 1);
+  const int gpw = a.GPW;
+  const int g0 = kq * gpw, g1 = min(ngrp, g0 + gpw);
+  const int gs = max(0, min(g0, ngrp - MAXG));          // first loaded group (MAXG <= ngrp), even
+  const int KG = static_cast<int>(static_cast<uint32_t>(a.K) >> 6);
+  // groups gs + i with i in [g0 - gs, g1 - gs) are this wavefront's
+  const uint32_t vmask = ((1u << max(0, g1 - gs)) - 1u) & ~((1u << max(0, g0 - gs)) - 1u);
 
   // ---- 1. activations of this wavefront's first item, before anything else.
   // Loads go through buffer resources: a lane with nothing to load gets an
@@ -402,42 +420,43 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * a.K * 2);
   u32x2 xw[C];
   {
-    const int m = wave % M, u = wave / M;
+    const int m = static_cast<int>((a.lut_m >> (4 * wave)) & 15u), u = static_cast<int>((a.lut_u >> (4 * wave)) & 15u);
     const uint32_t off = wave < nitem ? (static_cast<uint32_t>(m) * a.K + k0 + u * P + 16 * n + 4 * q) * 2
-                                        : kOutOfRange;
+                                      : kOutOfRange;
 #pragma unroll
     for (int c = 0; c < C; ++c) xw[c] = buf_load8(rx, off + 512 * c);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. weight loads of this wavefront
+  // ---- 2. weight loads of this wavefront: groups gs .. gs + MAXG - 1, those
+  // outside g0 .. g1 - 1 replaced by zeros (their scale pairs too: g0 and g1
+  // are even, so a pair of groups is either wholly inside or wholly outside)
   u32x2 c4[T8 ? 1 : MAXG];
   uint32_t sb[T8 ? 1 : MAXG / 2];                      // bf16 group scales, two per dword
   u32x4 c8[T8 ? MAXG : 1];
-  const bool load_w = row_ok;
   if constexpr (!T8) {
     const auto r4 = make_rsrc(a.q4, static_cast<uint32_t>(a.n4) * (a.K / 2));
     const auto rs = make_rsrc(a.s4, static_cast<uint32_t>(a.n4) * KG * 2);
-    const uint32_t o4 = load_w ? static_cast<uint32_t>(plc) * (a.K / 2) + (k0 + 64 * gs + 16 * q) / 2 : kOutOfRange;
-    const uint32_t os = load_w ? (static_cast<uint32_t>(plc) * KG + k0 / kGroup + gs) * 2 : kOutOfRange;
+    const uint32_t o4 = row_ok ? static_cast<uint32_t>(plc) * (static_cast<uint32_t>(a.K) >> 1) +
+                                     ((static_cast<uint32_t>(k0) + 64u * gs) >> 1) + 8u * q
+                               : kOutOfRange;
+    const uint32_t os = row_ok ? (static_cast<uint32_t>(plc) * KG + (static_cast<uint32_t>(k0) >> 6) + gs) * 2 : kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < MAXG; ++i) c4[i] = buf_load8(r4, gs + i >= g0 && gs + i < g1 ? o4 + 32 * i : kOutOfRange);
+    for (int i = 0; i < MAXG; ++i) c4[i] = buf_load8(r4, (vmask >> i) & 1u ? o4 + 32 * i : kOutOfRange);
 #pragma unroll
-    for (int i = 0; i < MAXG / 2; ++i)
-      sb[i] = buf_load4(rs, gs + 2 * i + 1 >= g0 && gs + 2 * i < g1 ? os + 4 * i : kOutOfRange);
+    for (int i = 0; i < MAXG / 2; ++i) sb[i] = buf_load4(rs, (vmask >> (2 * i)) & 1u ? os + 4 * i : kOutOfRange);
   } else {
     const auto r8 = make_rsrc(a.q8, static_cast<uint32_t>(a.n8) * a.K);
-    const uint32_t o8 = load_w ? static_cast<uint32_t>(plc) * a.K + k0 + 64 * gs + 16 * q : kOutOfRange;
+    const uint32_t o8 = row_ok ? static_cast<uint32_t>(plc) * a.K + k0 + 64 * gs + 16 * q : kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < MAXG; ++i) c8[i] = buf_load16(r8, gs + i >= g0 && gs + i < g1 ? o8 + 64 * i : kOutOfRange);
+    for (int i = 0; i < MAXG; ++i) c8[i] = buf_load16(r8, (vmask >> i) & 1u ? o8 + 64 * i : kOutOfRange);
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 3. items -> quantized int8 planes in LDS.  The first item is handled
   // outside any loop, so its wait covers only the activation loads issued
   // before the weights; later items (M > 1) are loaded here.
-  auto quantize = [&](int it, const u32x2(&xv)[C]) {
-    const int m = it % M, u = it / M;
+  auto quantize = [&](int m, int u, const u32x2(&xv)[C]) {
     float y[C][4];
     rotate_item<C>(a, xv, y);
     float mx = 0.0f;
@@ -458,33 +477,35 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
       *reinterpret_cast<uint32_t *>(xs1 + m * KW + kk) =
           pack_bytes((X[0] + 128) >> 8, (X[1] + 128) >> 8, (X[2] + 128) >> 8, (X[3] + 128) >> 8);
       *reinterpret_cast<uint32_t *>(xs2 + m * KW + kk) = pack_bytes(X[0], X[1], X[2], X[3]);
-      // group of 64 = kk / 64: the lanes with the same n / 4
-      int gsum = quad_sum(X[0] + X[1] + X[2] + X[3]);
-      gsum += __shfl_xor(gsum, 16, 64);
-      gsum += __shfl_xor(gsum, 32, 64);
-      if ((lane & 0x33) == 0) x8[(kk / kGroup) * kTab + m] = 8 * gsum;
+      if constexpr (!T8) {   // group of 64 = kk / 64: the lanes with the same n / 4
+        int gsum = quad_sum(X[0] + X[1] + X[2] + X[3]);
+        gsum += __shfl_xor(gsum, 16, 64);
+        gsum += __shfl_xor(gsum, 32, 64);
+        if ((lane & 0x33) == 0) x8[(kk / kGroup) * kTab + m] = 8 * gsum;
+      }
     }
     if (lane == 0) esc[u * kTab + m] = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
   };
-  if (wave < nitem) quantize(wave, xw);
+  if (wave < nitem)
+    quantize(static_cast<int>((a.lut_m >> (4 * wave)) & 15u), static_cast<int>((a.lut_u >> (4 * wave)) & 15u), xw);
   __builtin_amdgcn_sched_barrier(0);
   for (int it = wave + NCW; it < nitem; it += NCW) {
     const int m = it % M, u = it / M;
     u32x2 xv[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-      xv[c] = *reinterpret_cast<const u32x2 *>(a.x + static_cast<int64_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n +
-                                                4 * q);
-    quantize(it, xv);
+    for (int c = 0; c < C; ++c) xv[c] = buf_load8(rx, (static_cast<uint32_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n + 4 * q) * 2);
+    quantize(m, u, xv);
   }
   __syncthreads();   // (A) planes, group sums and unit scales are in LDS
 
-  // ---- 4. main loop: two int8 MFMAs per group, straight-line and masked; the
-  // MFMAs of group i+1 are issued before the scalar work of group i
-  const i32x4 zi = {0, 0, 0, 0};
-  float acc[R], accu[R];
+  // ---- 4. main loop: two int8 MFMAs per group (the second one starts from
+  // -8 x the group sum of X, the INT4 offset), straight-line; the MFMAs of
+  // group i+1 are issued before the scalar work of group i.  Each group adds
+  // D = 256 D1 + D2 times its scale (bf16 group scale x unit scale; for INT8
+  // rows the unit scale alone, the row scale comes at the end).
+  float acc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = accu[r] = 0.0f;
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
   {
     const int mA = MT == 1 ? 0 : min(n, M - 1);
     const int8_t *pa1 = xs1 + mA * KW + 16 * q, *pa2 = xs2 + mA * KW + 16 * q;
@@ -501,42 +522,42 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
       }
       return b;
     };
+    auto cinit = [&](int g) -> i32x4 {   // -8 x the group sums of X (INT4), 0 (INT8)
+      i32x4 c = {0, 0, 0, 0};
+      if constexpr (!T8) {
+        const i32x4 xg = *reinterpret_cast<const i32x4 *>(x8 + g * kTab);
+#pragma unroll
+        for (int r = 0; r < R; ++r) c[r] = -xg[r];
+      }
+      return c;
+    };
+    const i32x4 zi = {0, 0, 0, 0};
     i32x4 d1, d2;
     {
       const u32x4 b = bop(0);
       d1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * gs), b, zi);
-      d2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * gs), b, zi);
+      d2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * gs), b, cinit(gs));
     }
 #pragma unroll
     for (int i = 0; i < MAXG; ++i) {
       const int g = gs + i;
-      const bool valid = g >= g0 && g < g1;
       i32x4 e1 = zi, e2 = zi;
       if (i + 1 < MAXG) {
         const u32x4 b = bop(i + 1 < MAXG ? i + 1 : i);
         e1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * (g + 1)), b, zi);
-        e2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * (g + 1)), b, zi);
+        e2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * (g + 1)), b, cinit(g + 1));
       }
-      float sg;
-      i32x4 xg = zi;
+      // groups outside g0 .. g1 - 1 have zero codes; INT4 ones also a zero scale
+      const f32x4 ev = *reinterpret_cast<const f32x4 *>(esc + (g / gpu) * kTab);
+      float sg = 1.0f;
       if constexpr (!T8) {
         const uint32_t sw = sb[i / 2];
-        sg = valid ? __uint_as_float((i & 1) ? (sw & 0xFFFF0000u) : (sw << 16)) : 0.0f;
-        xg = *reinterpret_cast<const i32x4 *>(x8 + g * kTab);
-      } else {
-        sg = valid ? 1.0f : 0.0f;
+        sg = __uint_as_float((i & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int v = (d1[r] << 8) + d2[r] - xg[r];
-        accu[r] = fmaf(sg, static_cast<float>(v), accu[r]);
-      }
-      const bool bnd = valid && (((g + 1) % gpu == 0) || (g == g1 - 1));
-      const f32x4 ev = *reinterpret_cast<const f32x4 *>(esc + (g / gpu) * kTab);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        acc[r] = fmaf(bnd ? ev[r] : 0.0f, accu[r], acc[r]);
-        accu[r] = bnd ? 0.0f : accu[r];
+        const float cs = T8 ? ev[r] : sg * ev[r];
+        acc[r] = fmaf(cs, static_cast<float>((d1[r] << 8) + d2[r]), acc[r]);
       }
       d1 = e1;
       d2 = e2;
@@ -546,65 +567,60 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
 
   // ---- 5. partial tiles -> LDS
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = r < R ? acc[r] : 0.0f;
+  for (int r = 0; r < R; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
   __syncthreads();   // (B) partial tiles, U rows, columns, INT8 scales and t are in LDS
   if (kq != 0) return;
 
-  // ---- 6. first wavefront of each tile: sum the K-slices, add the low-rank term
+  // ---- 6. first wavefront of each tile: sum the K-slices, add the low-rank
+  // term.  Lane (n, q) takes the rank indices i = q, q + 4, ... of row n, the
+  // four lanes of a row then add up their shares.
   const int col = cols[rt * kTile + n];
-  f32x4 cacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float cacc[R];
+  {
+    const float s8 = s8s[rt * kTile + n];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float s = 0.0f;
-    for (int w = 0; w < KQ; ++w) s += red[((rt * KQ + w) * 4 + r) * 64 + lane];
-    cacc[r] = s * s8s[rt * kTile + n];
+    for (int r = 0; r < R; ++r) {
+      float s = 0.0f;
+      for (int w = 0; w < KQ; ++w) s += red[((rt * KQ + w) * 4 + r) * 64 + lane];
+      cacc[r] = s * s8;
+    }
   }
   {
     const int seg = (a.n_seg == 2 && plc >= rows / 2) ? 1 : 0;   // segments in packed order
-    const uint16_t *u16 = reinterpret_cast<const uint16_t *>(ush);
-    const int uoff = (base - wbase) * a.r;
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
-    for (int st = 0; st < nsp / 32; ++st) {
-      u32x4 bv;
+    const uint16_t *u16 = reinterpret_cast<const uint16_t *>(ush) + (rt * kTile + n) * a.r;
+    const float *tseg = ts + seg * a.r;
+    float lr[MT];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        uint32_t pair = 0;
+    for (int m = 0; m < MT; ++m) lr[m] = 0.0f;
+    for (int i = q; i < a.r; i += 4) {
+      const float uv = bf16_to_f32(u16[i]);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int ig = 32 * st + 8 * q + 2 * h + e;
-          const int il = ig - seg * a.r;
-          const bool ok = row_ok && ig < a.nsr && il >= 0 && il < a.r;
-          const uint32_t uv = ok ? u16[n * a.r + il + uoff] : 0u;
-          pair |= uv << (16 * e);
-        }
-        bv[h] = pair;
-      }
-      u32x4 av = z4;
-      if (n < M) {
-        const float *t = ts + n * nsp + 32 * st + 8 * q;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) av[h] = pack_bf16x2(t[2 * h], t[2 * h + 1]);
-      }
-      cacc = mfma_bf16(av, bv, cacc);
+      for (int m = 0; m < MT; ++m) lr[m] = fmaf(m < M ? tseg[m * nsp + i] : 0.0f, uv, lr[m]);
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      lr[m] += __shfl_xor(lr[m], 16, 64);
+      lr[m] += __shfl_xor(lr[m], 32, 64);
+    }
+    // token m sits in row m of the lanes with q = 0
+#pragma unroll
+    for (int r = 0; r < R; ++r) cacc[r] += (q == 0 && r < MT) ? lr[r < MT ? r : 0] : 0.0f;
   }
 
   // ---- 7. output: direct, or split-K partials summed by the last arriver
   if (a.S == 1) {
-    if (!row_ok) return;
+    if (!row_ok || q != 0) return;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int m = 4 * q + r;
-      if (m < M) a.y[static_cast<int64_t>(m) * a.N + col] = f32_to_bf16(cacc[r]);
-    }
+    for (int r = 0; r < R; ++r)
+      if (r < M) a.y[static_cast<int64_t>(r) * a.N + col] = f32_to_bf16(cacc[r]);
     return;
   }
   if (!tile_ok) return;
   const int p = base + n;
+  if (q == 0 && row_ok) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int m = 4 * q + r;
-    if (m < M && row_ok) st_dev(a.part + (static_cast<int64_t>(split) * kDecodeRows + m) * a.N + p, cacc[r]);
+    for (int r = 0; r < R; ++r)
+      if (r < M) st_dev(a.part + (static_cast<int64_t>(split) * kDecodeRows + r) * a.N + p, cacc[r]);
   }
   drain_stores();
   int last = 0;
@@ -638,8 +654,8 @@ __global__ __launch_bounds__(kThreads) void decode_small_kernel(DecodeArgs a) {
     produce<C>(a, b, smem);
     return;
   }
-  const int c = b - a.nprod;
-  if (c / a.S < a.g4) consume<MT, C, MAXG, false>(a, c, smem);
+  const int c = b - a.nprod;   // consumer index = group * S + split
+  if (c < a.g4 * a.S) consume<MT, C, MAXG, false>(a, c, smem);
   else consume<MT, C, MAXG, true>(a, c, smem);
 }
 
@@ -736,6 +752,8 @@ bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
         plan->RT = RT;
         plan->S = S;
         plan->MAXG = maxg;
+        plan->KQ = KQ;
+        plan->GPW = gpw;
       }
     }
   }

@@ -202,6 +202,11 @@ struct DecodeArgs {
   int N, K, r, n_seg, n4, n8, M, block, unit, nunit, nprod, nsr, nsr_pad, S, KW, g4, g8, rotate;
   int fused;           // 1: producers and consumers in one launch; 0: two launches
   int RT, MAXG;        // small-M path: 16-row tiles per workgroup, most groups per wavefront
+  int KQ, GPW;         // small-M path: wavefronts per tile, groups per wavefront (even)
+  int ngrp_w, nu_w;    // small-M path: groups of 64 and rotation units in one K-range (K / S)
+  uint32_t magic_s;    // small-M path: ceil(2^32 / S), S > 1: x / S = umulhi(x, magic_s) for x < 2^16
+  uint64_t lut_rt, lut_kq;  // small-M path: tile and K-slice of wavefront w in bits 4w .. 4w + 3
+  uint64_t lut_m, lut_u;    // small-M path: token row and unit of the first item of wavefront w
   float hscale;        // 1/sqrt(block)
 };
 
@@ -227,9 +232,11 @@ size_t decode_lds_bytes(int M, int unit, int KW, int nsr_pad);
 int decode_max_spans();   // most 128-input spans one decode workgroup takes
 // small-M decode (M <= 4): int8 matrix cores, 16-wavefront workgroups
 struct SmallPlan {
-  int RT;    // 16-row tiles per workgroup (1, 2, 4)
+  int RT;    // 16-row tiles per workgroup (1 .. 7)
   int S;     // split-K factor
-  int MAXG;  // groups of 64 inputs loaded per wavefront (4, 8, 12)
+  int MAXG;  // groups of 64 inputs loaded per wavefront (4, 8)
+  int KQ;    // wavefronts per tile
+  int GPW;   // groups of 64 per wavefront (even)
 };
 // false when no plan fits (the caller then takes the general decode path)
 bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan);
