@@ -94,7 +94,8 @@ uint64_t next_generation() {
 // falls as S grows).  0 when no S fits.
 // Largest M decoded by the small-M kernel (int8 matrix cores, 16-wavefront
 // consumer workgroups).
-constexpr int kSmallMaxM = 4;
+constexpr int kSmallMaxM = 16;
+constexpr int kPlanesMinM = 5;   // from this M on, producers quantize x_rot once for all consumers
 
 // Largest M decoded in one launch (producers and consumers together); larger
 // M uses a separate rotation launch first.
@@ -245,6 +246,7 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.MAXG = small ? sp.MAXG : 0;
   d.KQ = small ? sp.KQ : 0;
   d.GPW = small ? sp.GPW : 0;
+  d.planes = small && M >= kPlanesMinM;
   d.KW = L->K / d.S;
   if (small) {
     d.ngrp_w = d.KW / kGroup;

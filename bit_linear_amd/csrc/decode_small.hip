@@ -39,11 +39,12 @@ constexpr int kThreads = 1024;          // 16 wavefronts per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 16;               // packed rows per MFMA tile
 constexpr int kProdRows = 8;            // activation rows per producer
-constexpr int kTab = 4;                 // token rows of the per-row LDS tables
+constexpr int kTab = 16;                // token rows of the per-row LDS tables (M <= 16)
 constexpr int kMaxRT = 7;               // largest number of 16-row tiles per workgroup
 constexpr int kUVec = kMaxRT * kTile * 64 * 2 / 16 / 64;  // 16-byte U loads per spare lane (r <= 64)
 constexpr int kRowVec = (kMaxRT * kTile + 63) / 64;         // column / INT8-scale loads per spare lane
 constexpr long kSpinLimit = 1L << 22;   // bounded wait for a producer flag
+constexpr int kLoadBatch = 16;          // device-scope loads issued together before their first use
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int16_t s16x4 __attribute__((ext_vector_type(4)));
@@ -206,6 +207,37 @@ __device__ __forceinline__ void rotate_item(const DecodeArgs &a, const u32x2 (&x
     for (int j = 0; j < 4; ++j) y[c][j] *= a.hscale;
 }
 
+// 15-bit quantization of one rotated (row, unit) item held by a wavefront:
+// max |X| in [2^13, 2^14] with X = rint(x_rot 2^-e); X = 256 x1 + x2 with x2
+// the signed low byte.  Returns e; p1 / p2 get the lane's four x1 / x2 bytes of
+// each 256-block and gsum 8 x the sum of X over the lane's group of 64 inputs
+// (the same in the 16 lanes of that group).
+template <int C>
+__device__ __forceinline__ int quantize_item(const float (&y)[C][4], uint32_t (&p1)[C], uint32_t (&p2)[C],
+                                             int (&gsum)[C]) {
+  float mx = 0.0f;
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(y[c][j]));
+  mx = wave_max(mx);
+  const int e = (mx > 0.0f && mx <= 3.0e38f) ? max(-100, min(114, ilogbf(mx) - 13)) : 0;
+  const float down = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    int X[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) X[j] = __float2int_rn(y[c][j] * down);
+    p1[c] = pack_bytes((X[0] + 128) >> 8, (X[1] + 128) >> 8, (X[2] + 128) >> 8, (X[3] + 128) >> 8);
+    p2[c] = pack_bytes(X[0], X[1], X[2], X[3]);
+    int g = quad_sum(X[0] + X[1] + X[2] + X[3]);
+    g += __shfl_xor(g, 16, 64);
+    g += __shfl_xor(g, 32, 64);
+    gsum[c] = 8 * g;
+  }
+  return e;
+}
+
 // --------------------------------------------------------------------------- producer
 
 // Partial t of one rotation unit (C blocks of 256) for up to 8 activation rows.
@@ -245,7 +277,9 @@ __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) vload(j, j);
 
-  // 1. rotate one row per wavefront; bf16 copy for the t product
+  // 1. rotate one row per wavefront; bf16 copy for the t product; with
+  // a.planes, also the row's 15-bit planes, group sums and unit scale for the
+  // consumers (device-scope stores, drained before the flag)
   if (r_wave) {
     float y[C][4];
     rotate_item<C>(a, xw, y);
@@ -255,6 +289,19 @@ __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
       w[0] = pack_bf16x2(y[c][0], y[c][1]);
       w[1] = pack_bf16x2(y[c][2], y[c][3]);
       *reinterpret_cast<u32x2 *>(xb + wave * LDB + 256 * c + 16 * n + 4 * q) = w;
+    }
+    if (a.planes) {
+      uint32_t p1[C], p2[C];
+      int gsum[C];
+      const int e = quantize_item<C>(y, p1, p2, gsum);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int64_t kk = static_cast<int64_t>(m) * a.K + k0 + 256 * c + 16 * n + 4 * q;
+        st_dev(reinterpret_cast<uint32_t *>(a.xg1 + kk), p1[c]);
+        st_dev(reinterpret_cast<uint32_t *>(a.xg2 + kk), p2[c]);
+        if ((lane & 0x33) == 0) st_dev(a.x8g + ((k0 + 256 * c + 16 * n) / kGroup) * kDecodeRows + m, gsum[c]);
+      }
+      if (lane == 0) st_dev(a.escg + u * kDecodeRows + m, __uint_as_float(static_cast<uint32_t>(127 + e) << 23));
     }
   } else if (wave < kProdRows) {
     for (int j = lane; j < P / 2; j += 64) *reinterpret_cast<uint32_t *>(xb + wave * LDB + 2 * j) = 0u;
@@ -296,6 +343,70 @@ __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
 
 // --------------------------------------------------------------------------- consumer
 
+// t of the K-range into LDS: element e = m nsp + i (lanes t0, t0 + nt, ...)
+// is the sum of the partial t of units u0 .. u0 + nu - 1, in unit order; the
+// loads of a batch are all issued before the first is used, so their
+// latencies overlap.
+__device__ void sum_t(const DecodeArgs &a, int t0, int nt, int u0, int nu, float *ts) {
+  const int nsp = a.nsr_pad;
+  const int64_t ustride = static_cast<int64_t>(kDecodeRows) * nsp;
+  for (int e = t0; e < a.M * nsp; e += nt) {
+    const int m = e / nsp, i = e - m * nsp;
+    const float *src = a.tp + (static_cast<int64_t>(u0) * kDecodeRows + m) * nsp + i;
+    float s = 0.0f;
+    for (int u = 0; u < nu; u += kLoadBatch) {
+      float v[kLoadBatch];
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) v[j] = u + j < nu ? ld_dev(src + (u + j) * ustride) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) s += v[j];
+    }
+    ts[e] = i < a.nsr ? s : 0.0f;
+  }
+}
+
+// Copy of the producers' planes (rows 0 .. M-1, inputs k0 .. k0 + KW - 1),
+// 8 x group sums and unit scales into LDS by the lanes t0, t0 + nt, ... of the
+// workgroup; 16-byte chunks, read with device-scope loads.
+template <bool T8>
+__device__ void copy_planes(const DecodeArgs &a, int t0, int nt, int k0, int KW, int ngrp, int u0, int nu,
+                            int8_t *xs1, int8_t *xs2, int *x8, float *esc) {
+  constexpr int kBatch = 4;
+  const int M = a.M;
+  const int cpr = KW / 16;                               // chunks per row
+  const int nch = M * cpr;
+  const float inv = 1.0f / static_cast<float>(cpr);
+  for (int e0 = t0; e0 < nch; e0 += kBatch * nt) {
+    u32x4 v1[kBatch], v2[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int e = min(e0 + j * nt, nch - 1);
+      const int m = static_cast<int>((static_cast<float>(e) + 0.5f) * inv), c = e - m * cpr;
+      const int64_t g = static_cast<int64_t>(m) * a.K + k0 + 16 * c;
+      v1[j] = ld_dev16(a.xg1 + g);
+      v2[j] = ld_dev16(a.xg2 + g);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int e = e0 + j * nt;
+      if (e < nch) {
+        const int m = static_cast<int>((static_cast<float>(e) + 0.5f) * inv), c = e - m * cpr;
+        *reinterpret_cast<u32x4 *>(xs1 + m * KW + 16 * c) = v1[j];
+        *reinterpret_cast<u32x4 *>(xs2 + m * KW + 16 * c) = v2[j];
+      }
+    }
+  }
+  if constexpr (!T8)
+    for (int e = t0; e < ngrp * M; e += nt) {
+      const int g = e / M, m = e - g * M;
+      x8[g * kTab + m] = ld_dev(a.x8g + (k0 / kGroup + g) * kDecodeRows + m);
+    }
+  for (int e = t0; e < nu * M; e += nt) {
+    const int u = e / M, m = e - u * M;
+    esc[u * kTab + m] = ld_dev(a.escg + (u0 + u) * kDecodeRows + m);
+  }
+}
+
 // Spare wavefronts of a consumer workgroup: load the U rows, output columns
 // and INT8 row scales of the workgroup's rows (wbase .. wbase + wrows - 1),
 // then wait for the t producers of the K-range and sum their partial t.  Each
@@ -324,6 +435,22 @@ __device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows
     rv[j] = buf_load4(ri, ok ? static_cast<uint32_t>(wbase + e) * 4 : kOutOfRange);
     sv[j] = T8 ? buf_load4(rs8, ok ? static_cast<uint32_t>(wbase + e - a.n4) * 4 : kOutOfRange) : 0u;
   }
+  auto wait_flags = [&]() {
+    const int nrg = (M + kProdRows - 1) / kProdRows;
+    for (int i = sw * 64 + lane; i < nu * nrg; i += nsw * 64) {
+      const int rg = i / nu, uu = i - rg * nu;
+      long spins = 0;
+      while (ld_dev(a.flag + rg * a.nunit + u0 + uu) != a.gen && spins < kSpinLimit) {
+        __builtin_amdgcn_s_sleep(1);
+        ++spins;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  if (a.planes) {
+    wait_flags();
+    __syncthreads();   // (P)
+  }
   __syncthreads();   // (A)
 #pragma unroll
   for (int j = 0; j < kUVec; ++j)
@@ -336,21 +463,8 @@ __device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows
       s8s[e] = T8 ? __uint_as_float(sv[j]) : 1.0f;
     }
   }
-  for (int i = sw * 64 + lane; i < nu; i += nsw * 64) {
-    long spins = 0;
-    while (ld_dev(a.flag + u0 + i) != a.gen && spins < kSpinLimit) {
-      __builtin_amdgcn_s_sleep(1);
-      ++spins;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  for (int e = sw * 64 + lane; e < M * nsp; e += nsw * 64) {
-    const int m = e / nsp, i = e % nsp;
-    float s = 0.0f;
-    if (i < a.nsr)
-      for (int u = 0; u < nu; ++u) s += ld_dev(a.tp + (static_cast<int64_t>(u0 + u) * kDecodeRows + m) * nsp + i);
-    ts[e] = s;
-  }
+  if (!a.planes) wait_flags();
+  if (!a.planes) sum_t(a, sw * 64 + lane, nsw * 64, u0, nu, ts);
   __syncthreads();   // (B)
 }
 
@@ -363,9 +477,11 @@ __device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows
 template <int MT, int C, int MAXG, bool T8>
 __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   constexpr int R = MT == 1 ? 1 : 4;    // accumulator rows per lane that can hold a token
+  // lane (n, q) holds, in accumulator row r, token tq + r (MT > 1) or token 0 (MT = 1)
   constexpr int P = 256 * C;
   constexpr int gpu = P / kGroup;       // groups per rotation unit
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int tq = MT == 1 ? 0 : 4 * q;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   // per-wavefront and per-workgroup indices from host-made tables, without divisions
   const int RT = a.RT, KQ = a.KQ, NCW = RT * KQ;
@@ -421,7 +537,7 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   u32x2 xw[C];
   {
     const int m = static_cast<int>((a.lut_m >> (4 * wave)) & 15u), u = static_cast<int>((a.lut_u >> (4 * wave)) & 15u);
-    const uint32_t off = wave < nitem ? (static_cast<uint32_t>(m) * a.K + k0 + u * P + 16 * n + 4 * q) * 2
+    const uint32_t off = !a.planes && wave < nitem ? (static_cast<uint32_t>(m) * a.K + k0 + u * P + 16 * n + 4 * q) * 2
                                       : kOutOfRange;
 #pragma unroll
     for (int c = 0; c < C; ++c) xw[c] = buf_load8(rx, off + 512 * c);
@@ -459,42 +575,37 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   auto quantize = [&](int m, int u, const u32x2(&xv)[C]) {
     float y[C][4];
     rotate_item<C>(a, xv, y);
-    float mx = 0.0f;
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(y[c][j]));
-    mx = wave_max(mx);
-    // 15-bit quantization: max |X| in [2^13, 2^14]
-    const int e = (mx > 0.0f && mx <= 3.0e38f) ? max(-100, min(114, ilogbf(mx) - 13)) : 0;
-    const float down = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+    uint32_t p1[C], p2[C];
+    int gsum[C];
+    const int e = quantize_item<C>(y, p1, p2, gsum);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      int X[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) X[j] = __float2int_rn(y[c][j] * down);
       const int kk = u * P + 256 * c + 16 * n + 4 * q;
-      *reinterpret_cast<uint32_t *>(xs1 + m * KW + kk) =
-          pack_bytes((X[0] + 128) >> 8, (X[1] + 128) >> 8, (X[2] + 128) >> 8, (X[3] + 128) >> 8);
-      *reinterpret_cast<uint32_t *>(xs2 + m * KW + kk) = pack_bytes(X[0], X[1], X[2], X[3]);
-      if constexpr (!T8) {   // group of 64 = kk / 64: the lanes with the same n / 4
-        int gsum = quad_sum(X[0] + X[1] + X[2] + X[3]);
-        gsum += __shfl_xor(gsum, 16, 64);
-        gsum += __shfl_xor(gsum, 32, 64);
-        if ((lane & 0x33) == 0) x8[(kk / kGroup) * kTab + m] = 8 * gsum;
-      }
+      *reinterpret_cast<uint32_t *>(xs1 + m * KW + kk) = p1[c];
+      *reinterpret_cast<uint32_t *>(xs2 + m * KW + kk) = p2[c];
+      if (!T8 && (lane & 0x33) == 0) x8[(kk / kGroup) * kTab + m] = gsum[c];
     }
     if (lane == 0) esc[u * kTab + m] = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
   };
-  if (wave < nitem)
-    quantize(static_cast<int>((a.lut_m >> (4 * wave)) & 15u), static_cast<int>((a.lut_u >> (4 * wave)) & 15u), xw);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int it = wave + NCW; it < nitem; it += NCW) {
-    const int m = it % M, u = it / M;
-    u32x2 xv[C];
+  if (a.planes) {
+    // the producers quantized every (row, unit): once the spare wavefronts
+    // have seen their flags (barrier P), copy this K-range's planes, group
+    // sums and unit scales into LDS
+    __syncthreads();   // (P)
+    copy_planes<T8>(a, wave * 64 + lane, NCW * 64, k0, KW, ngrp, u0, nu, xs1, xs2, x8, esc);
+    sum_t(a, wave * 64 + lane, NCW * 64, u0, nu, ts);
+  } else {
+    if (wave < nitem)
+      quantize(static_cast<int>((a.lut_m >> (4 * wave)) & 15u), static_cast<int>((a.lut_u >> (4 * wave)) & 15u), xw);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int it = wave + NCW; it < nitem; it += NCW) {
+      const int m = it % M, u = it / M;
+      u32x2 xv[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) xv[c] = buf_load8(rx, (static_cast<uint32_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n + 4 * q) * 2);
-    quantize(m, u, xv);
+      for (int c = 0; c < C; ++c)
+        xv[c] = buf_load8(rx, (static_cast<uint32_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n + 4 * q) * 2);
+      quantize(m, u, xv);
+    }
   }
   __syncthreads();   // (A) planes, group sums and unit scales are in LDS
 
@@ -525,7 +636,7 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
     auto cinit = [&](int g) -> i32x4 {   // -8 x the group sums of X (INT4), 0 (INT8)
       i32x4 c = {0, 0, 0, 0};
       if constexpr (!T8) {
-        const i32x4 xg = *reinterpret_cast<const i32x4 *>(x8 + g * kTab);
+        const i32x4 xg = *reinterpret_cast<const i32x4 *>(x8 + g * kTab + tq);
 #pragma unroll
         for (int r = 0; r < R; ++r) c[r] = -xg[r];
       }
@@ -548,7 +659,7 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
         e2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * (g + 1)), b, cinit(g + 1));
       }
       // groups outside g0 .. g1 - 1 have zero codes; INT4 ones also a zero scale
-      const f32x4 ev = *reinterpret_cast<const f32x4 *>(esc + (g / gpu) * kTab);
+      const f32x4 ev = *reinterpret_cast<const f32x4 *>(esc + (g / gpu) * kTab + tq);
       float sg = 1.0f;
       if constexpr (!T8) {
         const uint32_t sw = sb[i / 2];
@@ -589,38 +700,48 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
     const int seg = (a.n_seg == 2 && plc >= rows / 2) ? 1 : 0;   // segments in packed order
     const uint16_t *u16 = reinterpret_cast<const uint16_t *>(ush) + (rt * kTile + n) * a.r;
     const float *tseg = ts + seg * a.r;
-    float lr[MT];
+    if constexpr (MT <= 4) {
+      float lr[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) lr[m] = 0.0f;
-    for (int i = q; i < a.r; i += 4) {
-      const float uv = bf16_to_f32(u16[i]);
+      for (int m = 0; m < MT; ++m) lr[m] = 0.0f;
+      for (int i = q; i < a.r; i += 4) {
+        const float uv = bf16_to_f32(u16[i]);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) lr[m] = fmaf(m < M ? tseg[m * nsp + i] : 0.0f, uv, lr[m]);
+        for (int m = 0; m < MT; ++m) lr[m] = fmaf(m < M ? tseg[m * nsp + i] : 0.0f, uv, lr[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        lr[m] += __shfl_xor(lr[m], 16, 64);
+        lr[m] += __shfl_xor(lr[m], 32, 64);
+      }
+      // token m sits in row m of the lanes with q = 0
+#pragma unroll
+      for (int r = 0; r < R; ++r) cacc[r] += (q == 0 && r < MT) ? lr[r < MT ? r : 0] : 0.0f;
+    } else {
+      // each lane adds the low-rank term of its own four tokens
+      for (int i = 0; i < a.r; ++i) {
+        const float uv = bf16_to_f32(u16[i]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) cacc[r] = fmaf(tq + r < M ? tseg[(tq + r) * nsp + i] : 0.0f, uv, cacc[r]);
+      }
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      lr[m] += __shfl_xor(lr[m], 16, 64);
-      lr[m] += __shfl_xor(lr[m], 32, 64);
-    }
-    // token m sits in row m of the lanes with q = 0
-#pragma unroll
-    for (int r = 0; r < R; ++r) cacc[r] += (q == 0 && r < MT) ? lr[r < MT ? r : 0] : 0.0f;
   }
 
   // ---- 7. output: direct, or split-K partials summed by the last arriver
+  const bool out_lane = row_ok && (MT != 1 || q == 0);
   if (a.S == 1) {
-    if (!row_ok || q != 0) return;
+    if (!out_lane) return;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (r < M) a.y[static_cast<int64_t>(r) * a.N + col] = f32_to_bf16(cacc[r]);
+      if (tq + r < M) a.y[static_cast<int64_t>(tq + r) * a.N + col] = f32_to_bf16(cacc[r]);
     return;
   }
   if (!tile_ok) return;
   const int p = base + n;
-  if (q == 0 && row_ok) {
+  if (out_lane) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (r < M) st_dev(a.part + (static_cast<int64_t>(split) * kDecodeRows + r) * a.N + p, cacc[r]);
+      if (tq + r < M) st_dev(a.part + (static_cast<int64_t>(split) * kDecodeRows + tq + r) * a.N + p, cacc[r]);
   }
   drain_stores();
   int last = 0;
@@ -640,8 +761,16 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
     const int rr = e % kTile, m = e / kTile;
     if (rr >= nrows) continue;
     const int pp = base + rr;
+    const float *src = a.part + static_cast<int64_t>(m) * a.N + pp;
+    const int64_t sstride = static_cast<int64_t>(kDecodeRows) * a.N;
     float s = 0.0f;
-    for (int sp = 0; sp < a.S; ++sp) s += ld_dev(a.part + (static_cast<int64_t>(sp) * kDecodeRows + m) * a.N + pp);
+    for (int sp = 0; sp < a.S; sp += kLoadBatch) {   // partials summed in split order
+      float v[kLoadBatch];
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) v[j] = sp + j < a.S ? ld_dev(src + (sp + j) * sstride) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) s += v[j];
+    }
     a.y[static_cast<int64_t>(m) * a.N + a.idx[pp]] = f32_to_bf16(s);
   }
 }
@@ -717,7 +846,7 @@ hipError_t launch_m(const DecodeArgs &a, hipStream_t s) {
 // reduction (0.2 + 0.01 S of the score) and every extra round 0.1; ties go to
 // fewer workgroups.
 bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
-  if (M < 1 || M > 4) return false;
+  if (M < 1 || M > 16) return false;
   // byte offsets of the buffer loads stay below 2^31
   const int64_t big = std::max<int64_t>(static_cast<int64_t>(L.n_int4) * L.K / 2,
                                         std::max<int64_t>(static_cast<int64_t>(L.n_int8) * L.K,
@@ -762,7 +891,7 @@ bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
 
 hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s) {
   if (a.unit != 256 && a.unit != 512 && a.unit != 1024 && a.unit != 2048) return hipErrorInvalidValue;
-  return a.M <= 1 ? launch_m<1>(a, s) : launch_m<4>(a, s);
+  return a.M <= 1 ? launch_m<1>(a, s) : a.M <= 4 ? launch_m<4>(a, s) : launch_m<16>(a, s);
 }
 
 }  // namespace dvssq

@@ -203,6 +203,7 @@ struct DecodeArgs {
   int fused;           // 1: producers and consumers in one launch; 0: two launches
   int RT, MAXG;        // small-M path: 16-row tiles per workgroup, most groups per wavefront
   int KQ, GPW;         // small-M path: wavefronts per tile, groups per wavefront (even)
+  int planes;          // small-M path: producers publish x_rot planes, consumers copy them (else rotate)
   int ngrp_w, nu_w;    // small-M path: groups of 64 and rotation units in one K-range (K / S)
   uint32_t magic_s;    // small-M path: ceil(2^32 / S), S > 1: x / S = umulhi(x, magic_s) for x < 2^16
   uint64_t lut_rt, lut_kq;  // small-M path: tile and K-slice of wavefront w in bits 4w .. 4w + 3
