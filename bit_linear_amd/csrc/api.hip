@@ -94,7 +94,7 @@ uint64_t next_generation() {
 // falls as S grows).  0 when no S fits.
 // Largest M decoded by the small-M kernel (int8 matrix cores, 16-wavefront
 // consumer workgroups).
-constexpr int kSmallMaxM = 16;
+constexpr int kSmallMaxM = 32;
 constexpr int kPlanesMinM = 5;   // from this M on, producers quantize x_rot once for all consumers
 
 // Largest M decoded in one launch (producers and consumers together); larger

@@ -39,7 +39,8 @@ constexpr int kThreads = 1024;          // 16 wavefronts per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 16;               // packed rows per MFMA tile
 constexpr int kProdRows = 8;            // activation rows per producer
-constexpr int kTab = 16;                // token rows of the per-row LDS tables (M <= 16)
+constexpr int kTab = 32;                // token rows of the per-row LDS tables (M <= 32)
+constexpr int kRed = 8;                 // partial-tile rows per lane in LDS (two token tiles of 4)
 constexpr int kMaxRT = 7;               // largest number of 16-row tiles per workgroup
 constexpr int kUVec = kMaxRT * kTile * 64 * 2 / 16 / 64;  // 16-byte U loads per spare lane (r <= 64)
 constexpr int kRowVec = (kMaxRT * kTile + 63) / 64;         // column / INT8-scale loads per spare lane
@@ -476,8 +477,9 @@ __device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows
 // vector ALU, shared by the four wavefronts of each SIMD, is the scarce unit.
 template <int MT, int C, int MAXG, bool T8>
 __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
-  constexpr int R = MT == 1 ? 1 : 4;    // accumulator rows per lane that can hold a token
-  // lane (n, q) holds, in accumulator row r, token tq + r (MT > 1) or token 0 (MT = 1)
+  constexpr int R = MT == 1 ? 1 : 4;    // accumulator rows per lane and token tile
+  constexpr int NT = MT > 16 ? 2 : 1;   // token tiles of 16
+  // lane (n, q) holds, in row r of token tile t, token 16 t + tq + r (MT > 1) or token 0 (MT = 1)
   constexpr int P = 256 * C;
   constexpr int gpu = P / kGroup;       // groups per rotation unit
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
@@ -504,8 +506,8 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   int8_t *xs2 = xs1 + M * KW;
   int *x8 = reinterpret_cast<int *>(xs2 + M * KW);                   // [ngrp][4]
   float *esc = reinterpret_cast<float *>(x8 + ngrp * kTab);          // [nu][4]
-  float *red = esc + nu * kTab;                                      // [kWaves][4][64]
-  u32x4 *ush = reinterpret_cast<u32x4 *>(red + kWaves * 4 * 64);   // U rows wbase .. wbase + 16 RT - 1
+  float *red = esc + nu * kTab;                                      // [kWaves][kRed][64]
+  u32x4 *ush = reinterpret_cast<u32x4 *>(red + kWaves * kRed * 64);  // U rows wbase .. wbase + 16 RT - 1
   int *cols = reinterpret_cast<int *>(ush + kUVec * 64);           // [16 RT] output columns
   float *s8s = reinterpret_cast<float *>(cols + kMaxRT * kTile);   // [16 RT] INT8 row scales
   float *ts = s8s + kMaxRT * kTile;                                // [M][nsp]
@@ -609,17 +611,24 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   }
   __syncthreads();   // (A) planes, group sums and unit scales are in LDS
 
-  // ---- 4. main loop: two int8 MFMAs per group (the second one starts from
-  // -8 x the group sum of X, the INT4 offset), straight-line; the MFMAs of
-  // group i+1 are issued before the scalar work of group i.  Each group adds
-  // D = 256 D1 + D2 times its scale (bf16 group scale x unit scale; for INT8
-  // rows the unit scale alone, the row scale comes at the end).
-  float acc[R];
+  // ---- 4. main loop: two int8 MFMAs per group and token tile (the second one
+  // starts from -8 x the group sum of X, the INT4 offset), straight-line; the
+  // MFMAs of group i+1 are issued before the scalar work of group i.  Each
+  // group adds D = 256 D1 + D2 times its scale (bf16 group scale x unit scale;
+  // for INT8 rows the unit scale alone, the row scale comes at the end).
+  float acc[NT][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[t][r] = 0.0f;
   {
-    const int mA = MT == 1 ? 0 : min(n, M - 1);
-    const int8_t *pa1 = xs1 + mA * KW + 16 * q, *pa2 = xs2 + mA * KW + 16 * q;
+    const int8_t *pa1[NT], *pa2[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int mA = MT == 1 ? 0 : min(16 * t + n, M - 1);
+      pa1[t] = xs1 + mA * KW + 16 * q;
+      pa2[t] = xs2 + mA * KW + 16 * q;
+    }
     auto bop = [&](int i) -> u32x4 {
       u32x4 b;
       if constexpr (!T8) {
@@ -633,74 +642,90 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
       }
       return b;
     };
-    auto cinit = [&](int g) -> i32x4 {   // -8 x the group sums of X (INT4), 0 (INT8)
+    auto cinit = [&](int g, int t) -> i32x4 {   // -8 x the group sums of X (INT4), 0 (INT8)
       i32x4 c = {0, 0, 0, 0};
       if constexpr (!T8) {
-        const i32x4 xg = *reinterpret_cast<const i32x4 *>(x8 + g * kTab + tq);
+        const i32x4 xg = *reinterpret_cast<const i32x4 *>(x8 + g * kTab + 16 * t + tq);
 #pragma unroll
         for (int r = 0; r < R; ++r) c[r] = -xg[r];
       }
       return c;
     };
     const i32x4 zi = {0, 0, 0, 0};
-    i32x4 d1, d2;
+    i32x4 d1[NT], d2[NT];
     {
       const u32x4 b = bop(0);
-      d1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * gs), b, zi);
-      d2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * gs), b, cinit(gs));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        d1[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1[t] + 64 * gs), b, zi);
+        d2[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2[t] + 64 * gs), b, cinit(gs, t));
+      }
     }
 #pragma unroll
     for (int i = 0; i < MAXG; ++i) {
       const int g = gs + i;
-      i32x4 e1 = zi, e2 = zi;
+      i32x4 e1[NT], e2[NT];
       if (i + 1 < MAXG) {
         const u32x4 b = bop(i + 1 < MAXG ? i + 1 : i);
-        e1 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1 + 64 * (g + 1)), b, zi);
-        e2 = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2 + 64 * (g + 1)), b, cinit(g + 1));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          e1[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1[t] + 64 * (g + 1)), b, zi);
+          e2[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2[t] + 64 * (g + 1)), b, cinit(g + 1, t));
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) e1[t] = e2[t] = zi;
       }
       // groups outside g0 .. g1 - 1 have zero codes; INT4 ones also a zero scale
-      const f32x4 ev = *reinterpret_cast<const f32x4 *>(esc + (g / gpu) * kTab + tq);
       float sg = 1.0f;
       if constexpr (!T8) {
         const uint32_t sw = sb[i / 2];
         sg = __uint_as_float((i & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float cs = T8 ? ev[r] : sg * ev[r];
-        acc[r] = fmaf(cs, static_cast<float>((d1[r] << 8) + d2[r]), acc[r]);
+      for (int t = 0; t < NT; ++t) {
+        const f32x4 ev = *reinterpret_cast<const f32x4 *>(esc + (g / gpu) * kTab + 16 * t + tq);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float cs = T8 ? ev[r] : sg * ev[r];
+          acc[t][r] = fmaf(cs, static_cast<float>((d1[t][r] << 8) + d2[t][r]), acc[t][r]);
+        }
+        d1[t] = e1[t];
+        d2[t] = e2[t];
       }
-      d1 = e1;
-      d2 = e2;
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // ---- 5. partial tiles -> LDS
 #pragma unroll
-  for (int r = 0; r < R; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[(wave * kRed + t * R + r) * 64 + lane] = acc[t][r];
   __syncthreads();   // (B) partial tiles, U rows, columns, INT8 scales and t are in LDS
   if (kq != 0) return;
 
-  // ---- 6. first wavefront of each tile: sum the K-slices, add the low-rank
-  // term.  Lane (n, q) takes the rank indices i = q, q + 4, ... of row n, the
-  // four lanes of a row then add up their shares.
+  // ---- 6. first wavefront of each tile: sum the K-slices, add the low-rank term
   const int col = cols[rt * kTile + n];
-  float cacc[R];
+  float cacc[NT][R];
   {
     const float s8 = s8s[rt * kTile + n];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float s = 0.0f;
-      for (int w = 0; w < KQ; ++w) s += red[((rt * KQ + w) * 4 + r) * 64 + lane];
-      cacc[r] = s * s8;
-    }
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float s = 0.0f;
+        for (int w = 0; w < KQ; ++w) s += red[((rt * KQ + w) * kRed + t * R + r) * 64 + lane];
+        cacc[t][r] = s * s8;
+      }
   }
   {
     const int seg = (a.n_seg == 2 && plc >= rows / 2) ? 1 : 0;   // segments in packed order
     const uint16_t *u16 = reinterpret_cast<const uint16_t *>(ush) + (rt * kTile + n) * a.r;
     const float *tseg = ts + seg * a.r;
     if constexpr (MT <= 4) {
+      // lane (n, q) takes the rank indices q, q + 4, ... of row n; the four
+      // lanes of a row then add up their shares
       float lr[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) lr[m] = 0.0f;
@@ -716,13 +741,18 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
       }
       // token m sits in row m of the lanes with q = 0
 #pragma unroll
-      for (int r = 0; r < R; ++r) cacc[r] += (q == 0 && r < MT) ? lr[r < MT ? r : 0] : 0.0f;
+      for (int r = 0; r < R; ++r) cacc[0][r] += (q == 0 && r < MT) ? lr[r < MT ? r : 0] : 0.0f;
     } else {
-      // each lane adds the low-rank term of its own four tokens
+      // each lane adds the low-rank term of its own tokens
       for (int i = 0; i < a.r; ++i) {
         const float uv = bf16_to_f32(u16[i]);
 #pragma unroll
-        for (int r = 0; r < R; ++r) cacc[r] = fmaf(tq + r < M ? tseg[(tq + r) * nsp + i] : 0.0f, uv, cacc[r]);
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int m = 16 * t + tq + r;
+            cacc[t][r] = fmaf(m < M ? tseg[m * nsp + i] : 0.0f, uv, cacc[t][r]);
+          }
       }
     }
   }
@@ -732,16 +762,24 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   if (a.S == 1) {
     if (!out_lane) return;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (tq + r < M) a.y[static_cast<int64_t>(tq + r) * a.N + col] = f32_to_bf16(cacc[r]);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int m = 16 * t + tq + r;
+        if (m < M) a.y[static_cast<int64_t>(m) * a.N + col] = f32_to_bf16(cacc[t][r]);
+      }
     return;
   }
   if (!tile_ok) return;
   const int p = base + n;
   if (out_lane) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (tq + r < M) st_dev(a.part + (static_cast<int64_t>(split) * kDecodeRows + tq + r) * a.N + p, cacc[r]);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int m = 16 * t + tq + r;
+        if (m < M) st_dev(a.part + (static_cast<int64_t>(split) * kDecodeRows + m) * a.N + p, cacc[t][r]);
+      }
   }
   drain_stores();
   int last = 0;
@@ -794,7 +832,7 @@ size_t producer_lds(int unit) {
 
 size_t consumer_lds(int M, int unit, int KW, int nsr_pad) {
   const size_t nu = KW / unit, ngrp = KW / kGroup;
-  return static_cast<size_t>(2) * M * KW + ngrp * kTab * 4 + nu * kTab * 4 + static_cast<size_t>(kWaves) * 4 * 64 * 4 +
+  return static_cast<size_t>(2) * M * KW + ngrp * kTab * 4 + nu * kTab * 4 + static_cast<size_t>(kWaves) * kRed * 64 * 4 +
          static_cast<size_t>(kUVec) * 64 * 16 + 2 * kMaxRT * kTile * 4 +
          static_cast<size_t>(M) * nsr_pad * 4;
 }
@@ -846,7 +884,7 @@ hipError_t launch_m(const DecodeArgs &a, hipStream_t s) {
 // reduction (0.2 + 0.01 S of the score) and every extra round 0.1; ties go to
 // fewer workgroups.
 bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
-  if (M < 1 || M > 16) return false;
+  if (M < 1 || M > 32) return false;
   // byte offsets of the buffer loads stay below 2^31
   const int64_t big = std::max<int64_t>(static_cast<int64_t>(L.n_int4) * L.K / 2,
                                         std::max<int64_t>(static_cast<int64_t>(L.n_int8) * L.K,
@@ -891,7 +929,7 @@ bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
 
 hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s) {
   if (a.unit != 256 && a.unit != 512 && a.unit != 1024 && a.unit != 2048) return hipErrorInvalidValue;
-  return a.M <= 1 ? launch_m<1>(a, s) : a.M <= 4 ? launch_m<4>(a, s) : launch_m<16>(a, s);
+  return a.M <= 1 ? launch_m<1>(a, s) : a.M <= 4 ? launch_m<4>(a, s) : a.M <= 16 ? launch_m<16>(a, s) : launch_m<32>(a, s);
 }
 
 }  // namespace dvssq
