@@ -187,6 +187,18 @@ int dvssq_fwht(const void *x, void *xrot, int32_t M, int32_t K, int32_t block, v
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
+// Compute units of the current device, queried once per device (256 on MI355X).
+static int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M,
                         void *ws, uint32_t flags, void *stream) {
   int rc = check_call(L, blob, x, y, M, ws, DVSSQ_DECODE_MAX_M);
@@ -196,7 +208,7 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   const int g4 = decode_groups(L->n_int4), g8 = decode_groups(L->n_int8);
   const int unit = decode_unit(L->block), nsp = nsr_pad_of(L->n_seg, L->r);
   SmallPlan sp{};
-  const bool small = M <= kSmallMaxM && plan_decode_small(*L, M, &sp);
+  const bool small = M <= kSmallMaxM && plan_decode_small(*L, M, compute_units(), &sp);
   const int S = small ? sp.S : decode_split(L->K, g4 + g8, M, unit, nsp);
   if (S == 0) return DVSSQ_EUNSUPPORTED;
   const WsLayout W = ws_layout(*L);
@@ -236,7 +248,7 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.block = L->block;
   d.unit = decode_unit(L->block);
   d.nunit = L->K / d.unit;
-  d.nprod = decode_producers(d.nunit, M);
+  d.nprod = small ? small_producers(d.nunit, M) : decode_producers(d.nunit, M);
   d.nsr = L->n_seg * L->r;
   d.nsr_pad = nsr_pad_of(L->n_seg, L->r);
   d.g4 = small ? (g4 + sp.RT - 1) / sp.RT : g4;

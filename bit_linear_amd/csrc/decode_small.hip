@@ -38,7 +38,7 @@ namespace {
 constexpr int kThreads = 1024;          // 16 wavefronts per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 16;               // packed rows per MFMA tile
-constexpr int kProdRows = 8;            // activation rows per producer
+constexpr int kProdRows = 16;           // activation rows per producer (one per wavefront)
 constexpr int kTab = 32;                // token rows of the per-row LDS tables (M <= 32)
 constexpr int kRed = 8;                 // partial-tile rows per lane in LDS (two token tiles of 4)
 constexpr int kMaxRT = 7;               // largest number of 16-row tiles per workgroup
@@ -436,9 +436,9 @@ __device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows
     rv[j] = buf_load4(ri, ok ? static_cast<uint32_t>(wbase + e) * 4 : kOutOfRange);
     sv[j] = T8 ? buf_load4(rs8, ok ? static_cast<uint32_t>(wbase + e - a.n4) * 4 : kOutOfRange) : 0u;
   }
-  auto wait_flags = [&]() {
+  auto wait_flags = [&]() {   // every spare wavefront waits for every flag it depends on
     const int nrg = (M + kProdRows - 1) / kProdRows;
-    for (int i = sw * 64 + lane; i < nu * nrg; i += nsw * 64) {
+    for (int i = lane; i < nu * nrg; i += 64) {
       const int rg = i / nu, uu = i - rg * nu;
       long spins = 0;
       while (ld_dev(a.flag + rg * a.nunit + u0 + uu) != a.gen && spins < kSpinLimit) {
@@ -876,14 +876,17 @@ hipError_t launch_m(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// Workgroup shape and split: RT tiles of 16 rows per workgroup (15/RT
-// wavefronts per tile split K), S equal parts of K, each a whole number of
-// rotation units, with at most 8 groups of 64 per wavefront (the register
-// file holds 16 wavefronts of at most 128 registers) and the LDS within 160 KB.  The score is the
-// share of compute units kept busy, wgs / (256 * rounds); a split costs a
-// reduction (0.2 + 0.01 S of the score) and every extra round 0.1; ties go to
-// fewer workgroups.
-bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
+// Workgroup shape and split for a GPU of `cus` compute units: RT tiles of 16
+// rows per workgroup (15 / RT wavefronts per tile split K), S equal parts of
+// K, each a whole number of rotation units, with at most 8 groups of 64 per
+// wavefront (the register file holds 16 wavefronts of at most 128 registers)
+// and the LDS within 160 KB.  Every workgroup, a t producer included, holds a
+// whole compute unit.  The plan minimises an estimated cost fitted to
+// measured runs: the rounds of workgroups, each weighted by the activation
+// planes a workgroup copies per byte of its weights (M > 4), plus 0.4 + 0.05 S
+// for a split (it adds a reduction), minus 0.2 x the share of compute units
+// kept busy; ties go to more workgroups.
+bool plan_decode_small(const dvssq_layout &L, int M, int cus, SmallPlan *plan) {
   if (M < 1 || M > 32) return false;
   // byte offsets of the buffer loads stay below 2^31
   const int64_t big = std::max<int64_t>(static_cast<int64_t>(L.n_int4) * L.K / 2,
@@ -895,9 +898,11 @@ bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
   const int nunit = L.K / unit;
   const int nsp = (L.n_seg * L.r + 31) / 32 * 32;
   const int t4 = (L.n_int4 + kTile - 1) / kTile, t8 = (L.n_int8 + kTile - 1) / kTile;
+  const int nprod = small_producers(nunit, M);
   const int gmax = 8;
-  double best = -1.0;
+  double best = -1e30;
   int best_wgs = 0;
+  bool found = false;
   for (int RT : {1, 2, 3, 4, 5, 7}) {
     const int KQ = (kWaves - 1) / RT;
     for (int S = 1; S <= kMaxSplit && S <= nunit; ++S) {
@@ -908,12 +913,15 @@ bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
       const int maxg = gpw <= 4 ? 4 : 8;
       if (maxg > ngrp) continue;
       if (small_lds(M, unit, KW, nsp) > 160 * 1024) continue;
-      const int wgs = ((t4 + RT - 1) / RT + (t8 + RT - 1) / RT) * S;
-      const int slots = 256;
-      const int rounds = (wgs + slots - 1) / slots;
-      const double score = static_cast<double>(wgs) / (static_cast<double>(slots) * rounds) -
-                           (S > 1 ? 0.2 + 0.01 * S : 0.0) - 0.1 * (rounds - 1);
-      if (score > best + 1e-9 || (score > best - 1e-9 && wgs < best_wgs)) {
+      // every workgroup, the t producers included, holds a whole compute unit
+      const int wgs = ((t4 + RT - 1) / RT + (t8 + RT - 1) / RT) * S + nprod;
+      const int rounds = (wgs + cus - 1) / cus;
+      // activation planes a workgroup copies (M > 4) per byte of its weights
+      const double planes = M >= 5 ? 2.0 * M / (RT * kTile * (0.5 + 2.0 / kGroup)) : 0.0;
+      const double util = static_cast<double>(wgs) / (static_cast<double>(cus) * rounds);
+      const double cost = rounds * (1.0 + 0.5 * planes) + (S > 1 ? 0.4 + 0.05 * S : 0.0) - 0.2 * util;
+      const double score = -cost;
+      if (score > best + 1e-9 || (score > best - 1e-9 && wgs > best_wgs)) {
         best = score;
         best_wgs = wgs;
         plan->RT = RT;
@@ -921,11 +929,14 @@ bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan) {
         plan->MAXG = maxg;
         plan->KQ = KQ;
         plan->GPW = gpw;
+        found = true;
       }
     }
   }
-  return best >= 0.0;
+  return found;
 }
+
+int small_producers(int nunit, int M) { return nunit * ((M + kProdRows - 1) / kProdRows); }
 
 hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s) {
   if (a.unit != 256 && a.unit != 512 && a.unit != 1024 && a.unit != 2048) return hipErrorInvalidValue;

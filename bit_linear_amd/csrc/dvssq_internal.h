@@ -240,7 +240,8 @@ struct SmallPlan {
   int GPW;   // groups of 64 per wavefront (even)
 };
 // false when no plan fits (the caller then takes the general decode path)
-bool plan_decode_small(const dvssq_layout &L, int M, SmallPlan *plan);
+bool plan_decode_small(const dvssq_layout &L, int M, int cus, SmallPlan *plan);
+int small_producers(int nunit, int M);   // t producers of the small-M kernel (one per unit and 16 rows)
 hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
