@@ -302,11 +302,21 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   p.K = L->K;
   p.nsr = L->n_seg * L->r;
   p.nsr_pad = nsp;
-  p.blocks_per_wg = L->K / L->block;
+  // one workgroup column per Hadamard block (the row scale comes from the whole
+  // row in every column); the last column of a row group to finish sums t
+  p.tpart = reinterpret_cast<float *>(wsb + W.p_tpart);
+  p.cnt = reinterpret_cast<uint64_t *>(wsb + W.p_cnt);
+  {
+    const uint64_t gen = next_generation();
+    p.tag = static_cast<uint32_t>(gen ^ (gen >> 32));
+    if (p.tag == 0) p.tag = 1;
+  }
+  p.blocks_per_wg = 1;
   p.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
   p.out_f16 = 1;
   p.hscale = inv_sqrt_block(L->block);
-  hipError_t e = launch_prologue(p, L->block, 1, s);
+  p.exp_bias = (p.rotate ? (__builtin_ctz(static_cast<unsigned>(L->block)) + 1) / 2 : 0) + 1 - 15;
+  hipError_t e = launch_prologue(p, L->block, L->K / L->block, s);
   if (e != hipSuccess) return DVSSQ_EHIP;
 
   PrefillArgs f{};

@@ -126,6 +126,8 @@ struct WsLayout {
   int64_t p_xr;    // f16 [M_max][K] rotated x scaled by 2^-e per row (or bf16 for dvssq_fwht)
   int64_t p_sc;    // fp32 [M_max] 2^e per row
   int64_t p_t;     // fp32 [M_max][nsr_pad] t = x_rot V^T
+  int64_t p_tpart; // fp32 [K / block][M_max][nsr_pad] partial t of each Hadamard block
+  int64_t p_cnt;   // u64 [ceil(M_max / 16)] tagged arrival counters of the prologue's row groups
   int64_t p_end;
   int64_t total;
 };
@@ -156,6 +158,8 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
   w.p_xr = cur;   cur = align256(cur + 2 * static_cast<int64_t>(L.M_max) * K);
   w.p_sc = cur;   cur = align256(cur + 4 * static_cast<int64_t>(L.M_max));
   w.p_t = cur;    cur = align256(cur + 4 * static_cast<int64_t>(L.M_max) * nsp);
+  w.p_tpart = cur; cur = align256(cur + 4 * (K / L.block) * static_cast<int64_t>(L.M_max) * nsp);
+  w.p_cnt = cur;  cur = align256(cur + 8 * ((static_cast<int64_t>(L.M_max) + 15) / 16));
   w.p_end = cur;
   w.total = w.d_end > w.p_end ? w.d_end : w.p_end;
   return w;
@@ -168,11 +172,15 @@ struct PrologueArgs {
   float *sc;           // fp32 [M] 2^e per row (f16 output) or null
   const uint16_t *V;   // bf16 [nsr][K] or null (no t)
   float *t;            // fp32 [M][nsr_pad] or null
+  float *tpart;        // K-split: fp32 [gridDim.y][M][nsr_pad] partial t of each Hadamard block
+  uint64_t *cnt;       // K-split: tagged arrival counters, one per row group
+  uint32_t tag;        // K-split: tag of this call, never 0
   int M, K, nsr, nsr_pad;
   int blocks_per_wg;   // Hadamard blocks handled (and t-accumulated) by one workgroup
   int rotate;          // 0: x is already rotated (copy + t only)
   int out_f16;         // 1: f16 scaled permuted output and sc; 0: bf16 natural
   float hscale;        // 1/sqrt(block)
+  int exp_bias;        // f16 output: row exponent = ilogb(max |x|) + exp_bias (log2 sqrt(block) if rotating, + 1 - 15)
 };
 
 struct DecodeArgs {

@@ -25,6 +25,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until every store this thread issued has completed
+__device__ __forceinline__ void drain_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int VPL>  // values per lane = block / 64
 __device__ __forceinline__ void load_row(const uint16_t *src, float (&v)[VPL]) {
   if constexpr (VPL >= 8) {
@@ -75,7 +89,6 @@ template <int VPL, int MT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   constexpr int B = 64 * VPL;
   constexpr int LDR = B + 4;  // padded LDS row (fp32)
-  constexpr int LOG2_SQRT_B = (__builtin_ctz(B) + 1) / 2;
   extern __shared__ __align__(16) float lds[];
   __shared__ int rowexp[MT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -87,26 +100,9 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   const bool want_t = a.nsr > 0;
   const int n_it = (a.nsr_pad + 31) / 32;
 
-  // 0. per-row power-of-two scale (f16 output only)
+  // 0. per-row power-of-two scale (f16 output only), written by rowscale_kernel
   if (a.out_f16) {
-    for (int ml = wave; ml < MT; ml += 4) {
-      float mx = 0.0f;
-      if (ml < mrows)
-        for (int blk = b0; blk < b1; ++blk) {
-          float v[VPL];
-          load_row<VPL>(a.x + static_cast<int64_t>(m0 + ml) * a.K + blk * B + lane * VPL, v);
-#pragma unroll
-          for (int j = 0; j < VPL; ++j) mx = fmaxf(mx, fabsf(v[j]));
-        }
-#pragma unroll
-      for (int s = 1; s < 64; s <<= 1) mx = fmaxf(mx, __shfl_xor(mx, s, 64));
-      int e = 0;
-      if (mx > 0.0f && mx <= 3.0e38f) e = max(-120, min(120, ilogbf(mx) + (a.rotate ? LOG2_SQRT_B : 0) + 1 - 15));
-      if (lane == 0) {
-        rowexp[ml] = e;
-        if (ml < mrows) a.sc[m0 + ml] = ldexpf(1.0f, e);
-      }
-    }
+    for (int ml = tid; ml < MT; ml += kThreads) rowexp[ml] = ml < mrows ? ilogbf(a.sc[m0 + ml]) : 0;
     __syncthreads();
   }
 
@@ -116,24 +112,56 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[it][e] = 0.0f;
 
+  // t pairs of this wavefront per block: K-steps s = wave, wave + 4, ... (of
+  // 16 inputs) times the n_it column tiles of 32; V is loaded in batches of
+  // kVB pairs, the first batch of a block before its rows are rotated
+  constexpr int SN = B / 64;
+  constexpr int kVB = 8;
+  const int npair = want_t ? SN * n_it : 0;
+  const int arow = lane & 31, half = lane >> 5;
+  u32x4 vb[kVB];
+  auto vload = [&](int kb, int p0) {
+#pragma unroll
+    for (int j = 0; j < kVB; ++j) {
+      const int pr = min(p0 + j, max(npair - 1, 0));
+      const int st = wave + 4 * (pr >> (n_it - 1)), it = pr & (n_it - 1);
+      const int i = 32 * it + arow;
+      vb[j] = (want_t && i < a.nsr)
+                  ? *reinterpret_cast<const u32x4 *>(a.V + static_cast<int64_t>(i) * a.K + kb + 16 * st + 8 * half)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // rows of this wavefront rotated together: their loads are issued at once
+  constexpr int RB = VPL <= 4 ? 8 : VPL <= 8 ? 4 : VPL <= 16 ? 2 : 1;
+
   for (int blk = b0; blk < b1; ++blk) {
     const int kb = blk * B;
+    if (npair > 0) vload(kb, 0);
     // 1. rotate each row of this block (one wavefront per row), stage fp32 in LDS
-    for (int ml = wave; ml < MT; ml += 4) {
-      float *row = lds + ml * LDR + lane * VPL;
-      if (ml < mrows) {
-        float v[VPL];
-        load_row<VPL>(a.x + static_cast<int64_t>(m0 + ml) * a.K + kb + lane * VPL, v);
-        if (a.rotate) {
-          fwht_wave<VPL>(v, lane);
+    for (int ml0 = wave; ml0 < MT; ml0 += 4 * RB) {
+      float v[RB][VPL];
 #pragma unroll
-          for (int j = 0; j < VPL; ++j) v[j] *= a.hscale;
+      for (int j = 0; j < RB; ++j) {
+        const int ml = min(ml0 + 4 * j, mrows - 1);
+        load_row<VPL>(a.x + static_cast<int64_t>(m0 + ml) * a.K + kb + lane * VPL, v[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const int ml = ml0 + 4 * j;
+        if (ml >= MT) break;
+        float *row = lds + ml * LDR + lane * VPL;
+        if (ml < mrows) {
+          if (a.rotate) {
+            fwht_wave<VPL>(v[j], lane);
+#pragma unroll
+            for (int q = 0; q < VPL; ++q) v[j][q] *= a.hscale;
+          }
+#pragma unroll
+          for (int q = 0; q < VPL; ++q) row[q] = v[j][q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < VPL; ++q) row[q] = 0.0f;
         }
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) row[j] = v[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) row[j] = 0.0f;
       }
     }
     __syncthreads();
@@ -156,23 +184,21 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
       *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) = o;
     }
     // 3. t += x_rot(block) V(block)^T on the matrix cores; K-steps of 16 split over the waves
-    if (want_t) {
-      const int arow = lane & 31, half = lane >> 5;
-      for (int s = wave; s < B / 16; s += 4) {
+    for (int p0 = 0; p0 < npair; p0 += kVB) {
+      if (p0 > 0) vload(kb, p0);
+#pragma unroll
+      for (int j = 0; j < kVB; ++j) {
+        if (p0 + j >= npair) break;
+        const int pr = p0 + j;
+        const int st = wave + 4 * (pr >> (n_it - 1)), it = pr & (n_it - 1);
         u32x4 av = {0u, 0u, 0u, 0u};
         if (arow < MT) {
-          const float *w = lds + arow * LDR + 16 * s + 8 * half;
+          const float *w = lds + arow * LDR + 16 * st + 8 * half;
 #pragma unroll
           for (int q = 0; q < 4; ++q) av[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
         }
-        for (int it = 0; it < n_it; ++it) {
-          const int i = 32 * it + arow;
-          u32x4 bv = {0u, 0u, 0u, 0u};
-          if (i < a.nsr)
-            bv = *reinterpret_cast<const u32x4 *>(a.V + static_cast<int64_t>(i) * a.K + kb + 16 * s + 8 * half);
-          if (it == 0) acc[0] = mfma32x32x16(av, bv, acc[0]);
-          else acc[1] = mfma32x32x16(av, bv, acc[1]);
-        }
+        if (it == 0) acc[0] = mfma32x32x16(av, vb[j], acc[0]);
+        else acc[1] = mfma32x32x16(av, vb[j], acc[1]);
       }
     }
     __syncthreads();
@@ -190,13 +216,77 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
       }
   }
   __syncthreads();
+  if (gridDim.y == 1) {
+    for (int e = tid; e < mrows * a.nsr_pad; e += kThreads) {
+      const int ml = e / a.nsr_pad, i = e % a.nsr_pad;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) s += red[((w * 2 + i / 32) * 32 + ml) * 32 + (i % 32)];
+      a.t[static_cast<int64_t>(m0 + ml) * a.nsr_pad + i] = s;
+    }
+    return;
+  }
+  // K split over the workgroup columns: publish this column's partial, count
+  // arrivals on the row group's tagged counter; the last column sums the
+  // partials in column order
   for (int e = tid; e < mrows * a.nsr_pad; e += kThreads) {
     const int ml = e / a.nsr_pad, i = e % a.nsr_pad;
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) s += red[((w * 2 + i / 32) * 32 + ml) * 32 + (i % 32)];
+    st_dev(a.tpart + (static_cast<int64_t>(blockIdx.y) * a.M + m0 + ml) * a.nsr_pad + i, s);
+  }
+  drain_stores();
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t *cnt = a.cnt + blockIdx.x;
+    uint64_t old = ld_dev(cnt), nw;
+    do {
+      nw = (static_cast<uint32_t>(old >> 32) == a.tag) ? old + 1 : ((static_cast<uint64_t>(a.tag) << 32) | 1u);
+    } while (!__hip_atomic_compare_exchange_strong(cnt, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT));
+    rowexp[0] = static_cast<uint32_t>(nw) == gridDim.y;   // LDS flag: this column arrived last
+  }
+  __syncthreads();
+  if (!rowexp[0]) return;
+  constexpr int kPB = 16;
+  const int64_t pstride = static_cast<int64_t>(a.M) * a.nsr_pad;
+  for (int e = tid; e < mrows * a.nsr_pad; e += kThreads) {
+    const int ml = e / a.nsr_pad, i = e % a.nsr_pad;
+    const float *src = a.tpart + static_cast<int64_t>(m0 + ml) * a.nsr_pad + i;
+    float s = 0.0f;
+    for (int c0 = 0; c0 < static_cast<int>(gridDim.y); c0 += kPB) {
+      float v[kPB];
+#pragma unroll
+      for (int j = 0; j < kPB; ++j) v[j] = c0 + j < static_cast<int>(gridDim.y) ? ld_dev(src + (c0 + j) * pstride) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < kPB; ++j) s += v[j];
+    }
     a.t[static_cast<int64_t>(m0 + ml) * a.nsr_pad + i] = s;
   }
+}
+
+// Per-row power-of-two scale 2^e of the f16 x_rot: from the bound
+// max |x H| <= sqrt(block) max |x|, e puts the scaled row below 2^15.  One
+// wavefront per row, its 16-byte chunks read with several loads in flight.
+__global__ __launch_bounds__(kThreads) void rowscale_kernel(PrologueArgs a) {
+  const int lane = threadIdx.x & 63, m = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (m >= a.M) return;
+  const u32x4 *row = reinterpret_cast<const u32x4 *>(a.x + static_cast<int64_t>(m) * a.K);
+  const int nch = a.K / 8;
+  float mx = 0.0f;
+#pragma unroll 8
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4 w = row[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+  }
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) mx = fmaxf(mx, __shfl_xor(mx, sft, 64));
+  int e = 0;
+  if (mx > 0.0f && mx <= 3.0e38f) e = max(-120, min(120, ilogbf(mx) + a.exp_bias));
+  if (lane == 0) a.sc[m] = ldexpf(1.0f, e);
 }
 
 template <int VPL, int MT>
@@ -222,6 +312,11 @@ hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hipStream_t s) {
+  if (a.out_f16) {
+    const hipError_t e = launch_kernel(reinterpret_cast<const void *>(rowscale_kernel),
+                                       dim3((a.M + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, s, a);
+    if (e != hipSuccess) return e;
+  }
   switch (block) {
     case 64: return launch_vpl<1, 32>(a, n_wg_blocks, s);
     case 128: return launch_vpl<2, 32>(a, n_wg_blocks, s);
