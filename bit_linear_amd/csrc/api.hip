@@ -286,6 +286,8 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   int rc = check_call(L, blob, x, y, M, ws, L ? L->M_max : 0);
   if (rc != DVSSQ_OK) return rc;
   if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
+  // the GEMM addresses one workgroup's weight rows, t and U with 32-bit byte offsets
+  if (L->K > (1 << 22) || M > (1 << 22) || static_cast<int64_t>(L->N) * L->r > (1 << 29)) return DVSSQ_EUNSUPPORTED;
   const WsLayout W = ws_layout(*L);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   const Blob B{static_cast<const uint8_t *>(blob), L};
@@ -339,9 +341,9 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   f.M = M;
   f.nsr = p.nsr;
   f.nsr_pad = nsp;
-  f.n4_tiles = (L->n_int4 + 127) / 128;
-  f.n8_tiles = (L->n_int8 + 127) / 128;
-  f.m_tiles = (M + 127) / 128;
+  f.n4_tiles = (L->n_int4 + kPfTileN - 1) / kPfTileN;
+  f.n8_tiles = (L->n_int8 + kPfTileN - 1) / kPfTileN;
+  f.m_tiles = (M + kPfTileM - 1) / kPfTileM;
   e = launch_prefill(f, s);
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }

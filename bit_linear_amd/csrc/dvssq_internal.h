@@ -49,6 +49,26 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------------ buffer loads
+// Buffer resources over one array (raw addressing, byte offsets).  A load at
+// an offset at or past num_records returns zeros and makes no memory access.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 // ------------------------------------------------------------------ f16 operands
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -105,6 +125,22 @@ __device__ __forceinline__ u32x4 int8_to_f16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// ------------------------------------------------------------------ prefill tiles
+// The prefill GEMM takes kPfTileM tokens by kPfTileN weight rows per workgroup
+// and one INT4 group (64 inputs) per step.  Its x_rot operand is stored as
+// tiles of kPfTileM rows by 64 inputs (16 KB), tile (m / 128, k / 64) at
+// ((m / 128) (K / 64) + k / 64) 8192 f16, rows past M left unwritten.  Inside
+// a tile, run r = (k % 64) / 8 of 8 inputs fills chunk 2 (r % 4) + r / 4 of
+// 128 rows x 8 f16: one matrix-core step of 16 inputs per lane half reads two
+// whole chunks, and one step of the GEMM copies one contiguous tile.
+constexpr int kPfTileM = 128;
+constexpr int kPfTileN = 256;
+__host__ __device__ inline int64_t xr_tile_offset(int m, int k, int K) {
+  const int r = (k & 63) >> 3;
+  return ((static_cast<int64_t>(m >> 7) * (K >> 6) + (k >> 6)) * 8 + 2 * (r & 3) + (r >> 2)) * 1024 + (m & 127) * 8;
+}
+inline int64_t pf_rows(int M) { return (static_cast<int64_t>(M) + kPfTileM - 1) / kPfTileM * kPfTileM; }
+
 // ------------------------------------------------------------------ workspace
 // Byte offsets inside the caller's workspace.  Decode and prefill regions
 // overlap (one call at a time per workspace).
@@ -123,7 +159,7 @@ struct WsLayout {
   int64_t d_cntw;  // u64 [groups]: tagged split-K arrival counters (small-M path)
   int64_t d_end;
   // prefill
-  int64_t p_xr;    // f16 [M_max][K] rotated x scaled by 2^-e per row (or bf16 for dvssq_fwht)
+  int64_t p_xr;    // f16 x_rot tiles of [M_max rounded up to 128][K], scaled by 2^-e per row
   int64_t p_sc;    // fp32 [M_max] 2^e per row
   int64_t p_t;     // fp32 [M_max][nsr_pad] t = x_rot V^T
   int64_t p_tpart; // fp32 [K / block][M_max][nsr_pad] partial t of each Hadamard block
@@ -155,7 +191,7 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
   w.d_cntw = cur; cur = align256(cur + 8 * (decode_groups(L.n_int4) + decode_groups(L.n_int8)));
   w.d_end = cur;
   cur = 0;
-  w.p_xr = cur;   cur = align256(cur + 2 * static_cast<int64_t>(L.M_max) * K);
+  w.p_xr = cur;   cur = align256(cur + 2 * pf_rows(L.M_max) * K);
   w.p_sc = cur;   cur = align256(cur + 4 * static_cast<int64_t>(L.M_max));
   w.p_t = cur;    cur = align256(cur + 4 * static_cast<int64_t>(L.M_max) * nsp);
   w.p_tpart = cur; cur = align256(cur + 4 * (K / L.block) * static_cast<int64_t>(L.M_max) * nsp);
@@ -168,7 +204,7 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
 // ------------------------------------------------------------------ kernel arguments
 struct PrologueArgs {
   const uint16_t *x;   // bf16 [M][K]
-  uint16_t *xr;        // [M][K]: bf16 natural order, or f16 scaled, runs of 8 in order 0,2,4,6,1,3,5,7
+  uint16_t *xr;        // bf16 [M][K] natural order, or f16 scaled prefill tiles (xr_tile_offset)
   float *sc;           // fp32 [M] 2^e per row (f16 output) or null
   const uint16_t *V;   // bf16 [nsr][K] or null (no t)
   float *t;            // fp32 [M][nsr_pad] or null
@@ -226,7 +262,7 @@ struct PrefillArgs {
   const float *s8;
   const uint16_t *U;
   const int32_t *idx;
-  const uint16_t *xr;  // f16 [M][K] scaled per row, runs of 8 in order 0,2,4,6,1,3,5,7
+  const uint16_t *xr;  // f16 tiles (xr_tile_offset) scaled per row, runs of 8 in order 0,2,4,6,1,3,5,7
   const float *sc;     // fp32 [M] 2^e per row
   const float *t;      // fp32 [M][nsr_pad]
   uint16_t *y;         // bf16 [M][N]

@@ -1,189 +1,321 @@
 // Prefill path (large M) of y = (x H) W_hat^T + ((x H) V^T) U^T
 // (MiniCPM5-2B-Hadamard-GSQ model card, Mathematical Foundations 2, runtime
 // equation).  A tiled GEMM on the f16 matrix cores: x_rot tiles (f16, scaled
-// by a power of two per row, from the prologue) and weight tiles dequantized
-// into LDS as exact f16 values -- INT4 rows as (n - 8) s_g (same card, INT4
+// by a power of two per row, from the prologue) times weights dequantized in
+// registers as exact f16 values -- INT4 rows as (n - 8) s_g (same card, INT4
 // equation), INT8 rows as the code q, whose fp32 row scale (Spark-X2.5-4B-
 // Hadamard-GSQ model card, Tier A) is applied to the accumulator afterwards.
 // Both operands hold each run of 8 inputs in the order 0,2,4,6,1,3,5,7, which
 // leaves the K-reduction unchanged.  The epilogue undoes the row scale, then
 // adds the low-rank term as one bf16 MFMA slab of t (bf16) times the U rows.
+#include <type_traits>
+
 #include "dvssq_internal.h"
 
 namespace dvssq {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;          // padded LDS row, f16 elements
+constexpr int BK = kGroup;              // inputs per step: one INT4 group
 constexpr int kThreads = 256;
+constexpr int MF = kPfTileM / 32;        // 32-token fragments of a wavefront
+constexpr int NF = kPfTileN / 4 / 32;    // 32-row weight fragments of a wavefront
+constexpr int kTileA = kPfTileM * BK;    // f16 per x_rot tile
+// s_waitcnt immediates: vmcnt(n), the other counters free
+constexpr int kVmcnt4 = 0x0F74;
+constexpr int kVmcnt8 = 0x0F78;
+// padded LDS row of the staged t (bf16): NS slabs of 16 plus 8, so that the
+// 32 rows one matrix-core operand reads start on different banks
+template <int NS>
+constexpr int TS = NS * 16 + 8;
 
-__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// One workgroup: kPfTileM tokens by kPfTileN weight rows of one tier, the four
+// wavefronts side by side over the weight rows (128 tokens x 64 rows each).
+// x_rot tiles go through LDS (double buffered, one contiguous 16 KB copy per
+// step); each wavefront loads its own weight bytes straight into registers --
+// lane (fr, fh) of fragment j takes row 32 j + fr and inputs 32 fh .. 32 fh + 31
+// of the group, which are contiguous in the packed rows -- and dequantizes
+// them there.  Loads run one step ahead of the matrix cores.
+template <bool T8, int NS>
+__device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0, uint16_t *A1, uint16_t *A2,
+                                             uint16_t *ts, float *scs, int mtile, int tile0) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 31, fh = lane >> 5;
+  const int KG = a.K / BK;
+  const int rows = T8 ? a.n8 : a.n4;
+  const int p0 = tile0 + 64 * wave;   // first weight row (inside the tier) of this wavefront
+  const uint16_t *ag = a.xr + static_cast<int64_t>(mtile) * KG * kTileA;
+  const int m0 = mtile * kPfTileM;
 
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
-  extern __shared__ __align__(16) uint16_t lds[];
-  uint16_t *As = lds;                       // [2][BM][LDK]
-  uint16_t *Bs = lds + 2 * BM * LDK;        // [2][BN][LDK]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int ntile = blockIdx.x / a.m_tiles, mtile = blockIdx.x % a.m_tiles;
-  const bool t8 = ntile >= a.n4_tiles;
-  const int rows = t8 ? a.n8 : a.n4;
-  const int p0l = (t8 ? ntile - a.n4_tiles : ntile) * BN;   // first tile row inside the tier
-  const int m0 = mtile * BM;
-  const int KG = a.K / kGroup;
-  const int nk = KG;
-
-  // global -> register staging assignment
-  const int a_row = tid >> 3, a_seg = tid & 7;         // A: rows a_row + 32 i, 16-byte segment a_seg
-  const int b_row = tid >> 1, b_half = tid & 1;        // B: one row, half of the 64-input step
-  const bool b_ok = p0l + b_row < rows;
-
-  u32x4 ra[4], rb[2];
-  uint32_t rs = 0;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
+  // the epilogue's token-side operands, staged in LDS while the main loop runs:
+  // t rows of the tile as bf16 (padded rows of TS), and the row scales
+  {
+    const auto rt = make_rsrc(a.t, static_cast<uint32_t>(a.M) * (NS * 16) * 4);
+    const int row = tid >> 1, half = tid & 1;
+    const uint32_t base = static_cast<uint32_t>((m0 + row) * (NS * 16) + half * (NS * 8)) * 4;
+    u32x4 tv[2 * NS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + a_row + 32 * i;
-      ra[i] = (m < a.M) ? ld16(a.xr + static_cast<int64_t>(m) * a.K + k0 + 8 * a_seg) : z4;
+    for (int c = 0; c < 2 * NS; ++c) tv[c] = buf_load16(rt, base + 16 * c);
+    const auto rsc = make_rsrc(a.sc, static_cast<uint32_t>(a.M) * 4);
+    const uint32_t sv = buf_load4(rsc, tid < kPfTileM ? static_cast<uint32_t>(m0 + tid) * 4 : kOutOfRange);
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32x4 w = tv[2 * c + q];
+        o[2 * q] = pack_bf16x2(__uint_as_float(w[0]), __uint_as_float(w[1]));
+        o[2 * q + 1] = pack_bf16x2(__uint_as_float(w[2]), __uint_as_float(w[3]));
+      }
+      *reinterpret_cast<u32x4 *>(ts + row * TS<NS> + half * (NS * 8) + 8 * c) = o;
     }
-    if (!t8) {
-      rb[0] = b_ok ? ld16(a.q4 + static_cast<int64_t>(p0l + b_row) * (a.K / 2) + k0 / 2 + 16 * b_half) : z4;
-      rs = b_ok ? a.s4[static_cast<int64_t>(p0l + b_row) * KG + kt] : 0u;
-    } else {
-      const int8_t *src = a.q8 + static_cast<int64_t>(p0l + b_row) * a.K + k0 + 32 * b_half;
-      rb[0] = b_ok ? ld16(src) : z4;
-      rb[1] = b_ok ? ld16(src + 16) : z4;
+    if (tid < kPfTileM) scs[tid] = __uint_as_float(sv);
+  }
+
+  // weight bytes of this workgroup's rows only, so that 32-bit offsets suffice
+  const int64_t rb = T8 ? a.K : a.K / 2;   // packed bytes per row
+  const int nrow = min(kPfTileN, rows - tile0);
+  const auto rq = make_rsrc((T8 ? static_cast<const uint8_t *>(static_cast<const void *>(a.q8)) : a.q4) + tile0 * rb,
+                            static_cast<uint32_t>(nrow * rb));
+  const auto rs = make_rsrc(a.s4 + static_cast<int64_t>(tile0) * KG, static_cast<uint32_t>(T8 ? 0 : nrow * KG * 2));
+  uint32_t oq[NF], os[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int rl = 64 * wave + 32 * j + fr;   // row inside the workgroup's tile
+    const bool ok = rl < nrow;
+    oq[j] = ok ? static_cast<uint32_t>(rl * rb + (T8 ? 32 : 16) * fh) : kOutOfRange;
+    os[j] = ok ? static_cast<uint32_t>(rl * KG * 2) : kOutOfRange;
+  }
+
+  // x_rot tiles: a direct copy into LDS (each wavefront instruction fills 1 KB
+  // of one tile, lane l at byte 16 l)
+  const auto ra = make_rsrc(ag, static_cast<uint32_t>(KG) * kTileA * 2);
+  auto load_a = [&](int g, uint16_t *dst) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void *)(dst + (kThreads * i + 64 * wave) * 8), 16, lane * 16,
+          g * (kTileA * 2) + (kThreads * i + 64 * wave) * 16, 0, 0);
+  };
+  // raw weight bytes of NB steps in flight: INT4 rows (16 bytes + a group
+  // scale per lane) two steps ahead, INT8 rows (32 bytes) one step ahead
+  constexpr int NB = T8 ? 2 : 3;
+  u32x4 Q[NB][NF][T8 ? 2 : 1];
+  uint32_t S[NB][NF];
+  auto load_b = [&](int g, auto set) {
+    constexpr int b = decltype(set)::value;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      if constexpr (T8) {
+        Q[b][j][0] = buf_load16(rq, oq[j] + 64 * g);
+        Q[b][j][1] = buf_load16(rq, oq[j] + 64 * g + 16);
+      } else {
+        Q[b][j][0] = buf_load16(rq, oq[j] + 32 * g);
+        S[b][j] = buf_load2(rs, os[j] + 2 * g);
+      }
     }
   };
-  auto sstore = [&](int buf) {
-    uint16_t *as = As + buf * BM * LDK;
-    uint16_t *bs = Bs + buf * BN * LDK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(as + (a_row + 32 * i) * LDK + 8 * a_seg) = ra[i];
-    uint16_t *dst = bs + b_row * LDK + 32 * b_half;
-    if (!t8) {
-      const float s = bf16_to_f32(rs);
-      const uint32_t s2 = pack_f16x2(s, s), c24 = pack_f16x2(-24.0f * s, -24.0f * s);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4 *>(dst + 8 * d) = int4_to_f16(rb[0][d], s2, c24);
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          *reinterpret_cast<u32x4 *>(dst + 16 * h + 8 * e) = int8_to_f16(rb[h][2 * e], rb[h][2 * e + 1]);
-    }
-  };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MF][NF];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NF; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int fr = lane & 31, fh = lane >> 5;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t *as = As + cur * BM * LDK + (64 * wm + fr) * LDK + 8 * fh;
-    const uint16_t *bs = Bs + cur * BN * LDK + (64 * wn + fr) * LDK + 8 * fh;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4 af[2], bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const u32x4 *>(as + 32 * i * LDK + 16 * ks);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(bs + 32 * j * LDK + 16 * ks);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16_f16(af[i], bf[j], acc[i][j]);
+  // One step of 64 inputs: x_rot tile g sits in LDS buffer cur, tile g + 2
+  // is copied into buffer nx2 (three distinct LDS arrays, so that a copy into
+  // one is never taken to alias reads of another).  Every step issues the
+  // same eight loads (the last steps repeat the last group), so the wait at
+  // the top of a step leaves exactly the next step's loads in flight.
+  auto step = [&](int g, const uint16_t *cur, uint16_t *nx2, auto use, auto fill) {
+    constexpr int bu = decltype(use)::value;
+    // a bare barrier: a workgroup fence here would also wait for the copies
+    // still in flight for the next steps; the asm statements keep the
+    // compiler from moving memory accesses across it
+    __builtin_amdgcn_s_waitcnt(T8 ? kVmcnt4 : kVmcnt8);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if constexpr (T8) {
+      load_b(min(g + 1, KG - 1), fill);
+      load_a(min(g + 2, KG - 1), nx2);
+    } else {
+      load_a(min(g + 2, KG - 1), nx2);
+      load_b(min(g + 2, KG - 1), fill);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    auto dequant = [&](int j, int ks) -> u32x4 {
+      if constexpr (T8) {
+        return int8_to_f16(Q[bu][j][ks >> 1][2 * (ks & 1)], Q[bu][j][ks >> 1][2 * (ks & 1) + 1]);
+      } else {
+        const float sc = bf16_to_f32(S[bu][j]);
+        return int4_to_f16(Q[bu][j][0][ks], pack_f16x2(sc, sc), pack_f16x2(-24.0f * sc, -24.0f * sc));
+      }
+    };
+    // operands of 16-input step ks + 1 are read and dequantized while the
+    // matrix cores work on step ks
+    const uint16_t *as = cur + fh * 1024 + fr * 8;   // chunk 2 ks + fh, row 32 i + fr
+    u32x4 af[2][MF], bf[2][NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i) af[0][i] = *reinterpret_cast<const u32x4 *>(as + i * 256);
+#pragma unroll
+    for (int j = 0; j < NF; ++j) bf[0][j] = dequant(j, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks & 1;
+      if (ks < 3) {
+#pragma unroll
+        for (int i = 0; i < MF; ++i) af[c ^ 1][i] = *reinterpret_cast<const u32x4 *>(as + (ks + 1) * 2048 + i * 256);
+#pragma unroll
+        for (int j = 0; j < NF; ++j) bf[c ^ 1][j] = dequant(j, ks + 1);
+      }
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[i][j] = mfma32x32x16_f16(af[c][i], bf[c][j], acc[i][j]);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using INB1 = std::integral_constant<int, (NB > 2 ? 2 : 0)>;   // set 2 (INT4) or 0 (INT8)
+
+  // pipeline fill in the order the steps issue their loads
+  load_a(0, A0);
+  load_b(0, I0{});
+  if constexpr (T8) {
+    load_a(min(1, KG - 1), A1);
+  } else {
+    load_a(min(1, KG - 1), A1);
+    load_b(min(1, KG - 1), I1{});
   }
+  // six steps per pass: buffers of A rotate by 3, sets of B by NB; the
+  // passes run unconditionally (exact load counts at every wait), the last
+  // fewer than six steps after them
+  auto six = [&](int g, int n) {
+    if constexpr (T8) {
+      if (n > 0) step(g, A0, A2, I0{}, I1{});
+      if (n > 1) step(g + 1, A1, A0, I1{}, I0{});
+      if (n > 2) step(g + 2, A2, A1, I0{}, I1{});
+      if (n > 3) step(g + 3, A0, A2, I1{}, I0{});
+      if (n > 4) step(g + 4, A1, A0, I0{}, I1{});
+      if (n > 5) step(g + 5, A2, A1, I1{}, I0{});
+    } else {
+      if (n > 0) step(g, A0, A2, I0{}, INB1{});
+      if (n > 1) step(g + 1, A1, A0, I1{}, I0{});
+      if (n > 2) step(g + 2, A2, A1, INB1{}, I1{});
+      if (n > 3) step(g + 3, A0, A2, I0{}, INB1{});
+      if (n > 4) step(g + 4, A1, A0, I1{}, I0{});
+      if (n > 5) step(g + 5, A2, A1, INB1{}, I1{});
+    }
+  };
+  int g = 0;
+  for (; g + 6 <= KG; g += 6) six(g, 6);
+  if (g < KG) six(g, KG - g);
 
   // ---- epilogue: row scale 2^e, INT8 row scale, low-rank slab, bf16 scatter through idx
-  float rsc[2][16];
+  // weight-side loads first, all in one batch
+  int pj[NF], col[NF];
+  bool okj[NF];
+  float s8[NF];
+  u32x4 bu[NF][NS];   // U of row pj, slots 16 js + 8 fh .. + 7 of the low-rank vector
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < NF; ++j) {
+    const int pl = p0 + 32 * j + fr;
+    okj[j] = pl < rows;
+    pj[j] = (T8 ? a.n4 : 0) + (okj[j] ? pl : 0);
+    col[j] = a.idx[pj[j]];
+    s8[j] = T8 ? a.s8[okj[j] ? pl : 0] : 1.0f;
+  }
+  const int seg_cols = a.N / a.n_seg;
+  if ((a.r & 7) == 0) {
+    // slots of one segment are whole runs of 8: one 16-byte load each
+    const auto ru = make_rsrc(a.U, static_cast<uint32_t>(a.N) * a.r * 2);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + 64 * wm + 32 * i + 8 * (v / 4) + 4 * fh + (v % 4);
-      rsc[i][v] = (m < a.M) ? a.sc[m] : 0.0f;
-    }
+    for (int j = 0; j < NF; ++j) {
+      const int seg = col[j] / seg_cols;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int pl = p0l + 64 * wn + 32 * j + fr;
-    const bool ok = pl < rows;
-    const int p = (t8 ? a.n4 : 0) + pl;
-    const float s8 = (t8 && ok) ? a.s8[pl] : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] *= rsc[i][v] * s8;
-    const int seg = ok ? a.idx[p] / (a.N / a.n_seg) : 0;
-    for (int js = 0; js < a.nsr_pad / 16; ++js) {
-      u32x4 bv;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t pair = 0;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int ig = 16 * js + 8 * fh + 2 * q + e;
-          const int il = ig - seg * a.r;
-          uint32_t u = 0;
-          if (ok && ig < a.nsr && il >= 0 && il < a.r) u = a.U[static_cast<int64_t>(p) * a.r + il];
-          pair |= u << (16 * e);
-        }
-        bv[q] = pair;
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int m = m0 + 64 * wm + 32 * i + fr;
-        u32x4 av = z4;
-        if (m < a.M) {
-          const float *src = a.t + static_cast<int64_t>(m) * a.nsr_pad + 16 * js + 8 * fh;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) av[q] = pack_bf16x2(src[2 * q], src[2 * q + 1]);
-        }
-        acc[i][j] = mfma32x32x16(av, bv, acc[i][j]);
+      for (int js = 0; js < NS; ++js) {
+        const int il = 16 * js + 8 * fh - seg * a.r;
+        const bool in = okj[j] && il >= 0 && il < a.r;
+        bu[j][js] = buf_load16(ru, in ? static_cast<uint32_t>(pj[j] * a.r + il) * 2 : kOutOfRange);
       }
     }
-    if (!ok) continue;
-    const int col = a.idx[p];
+  } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < NF; ++j) {
+      const int seg = col[j] / seg_cols;
+#pragma unroll
+      for (int js = 0; js < NS; ++js)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t pair = 0;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int il = 16 * js + 8 * fh + 2 * q + e - seg * a.r;
+            uint32_t u = 0;
+            if (okj[j] && il >= 0 && il < a.r) u = a.U[static_cast<int64_t>(pj[j]) * a.r + il];
+            pair |= u << (16 * e);
+          }
+          bu[j][js][q] = pair;
+        }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 sc4 = *reinterpret_cast<const f32x4 *>(scs + 32 * i + 8 * k + 4 * fh);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][4 * k + v] *= sc4[v] * s8[j];
+      }
+#pragma unroll
+    for (int js = 0; js < NS; ++js)
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const u32x4 av = *reinterpret_cast<const u32x4 *>(ts + (32 * i + fr) * TS<NS> + 16 * js + 8 * fh);
+        acc[i][j] = mfma32x32x16(av, bu[j][js], acc[i][j]);
+      }
+    if (!okj[j]) continue;
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + 64 * wm + 32 * i + 8 * (v / 4) + 4 * fh + (v % 4);
-        if (m < a.M) a.y[static_cast<int64_t>(m) * a.N + col] = f32_to_bf16(acc[i][j][v]);
+        const int m = m0 + 32 * i + 8 * (v / 4) + 4 * fh + (v % 4);
+        if (m < a.M) a.y[static_cast<int64_t>(m) * a.N + col[j]] = f32_to_bf16(acc[i][j][v]);
       }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+  __shared__ __align__(16) uint16_t A0[kTileA];
+  __shared__ __align__(16) uint16_t A1[kTileA];
+  __shared__ __align__(16) uint16_t A2[kTileA];
+  __shared__ __align__(16) uint16_t ts[kPfTileM * TS<4>];
+  __shared__ __align__(16) float scs[kPfTileM];
+  // consecutive workgroups share a weight tile (its bytes stay in L2)
+  const int ntile = blockIdx.x / a.m_tiles, mtile = blockIdx.x % a.m_tiles;
+  const bool t8 = ntile >= a.n4_tiles;
+  const int tile0 = (t8 ? ntile - a.n4_tiles : ntile) * kPfTileN;
+  if (a.nsr_pad == 64) {
+    if (t8) prefill_tile<true, 4>(a, A0, A1, A2, ts, scs, mtile, tile0);
+    else prefill_tile<false, 4>(a, A0, A1, A2, ts, scs, mtile, tile0);
+  } else {
+    if (t8) prefill_tile<true, 2>(a, A0, A1, A2, ts, scs, mtile, tile0);
+    else prefill_tile<false, 2>(a, A0, A1, A2, ts, scs, mtile, tile0);
   }
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(2) * (BM + BN) * LDK * 2;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const int grid = (a.n4_tiles + a.n8_tiles) * a.m_tiles;
-  return launch_kernel(reinterpret_cast<const void *>(prefill_kernel), dim3(grid), dim3(kThreads), lds, s, a);
+  return launch_kernel(reinterpret_cast<const void *>(prefill_kernel), dim3(grid), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace dvssq

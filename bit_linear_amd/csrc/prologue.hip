@@ -165,23 +165,30 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
       }
     }
     __syncthreads();
-    // 2. copy out in runs of 8
+    // 2. copy out in runs of 8: f16 into the GEMM's tiles (consecutive threads
+    // take consecutive rows of one run), bf16 row-major
     constexpr int RUNS = B / 8;
-    for (int e = tid; e < mrows * RUNS; e += kThreads) {
-      const int ml = e / RUNS, run = e % RUNS;
-      const float *w = lds + ml * LDR + run * 8;
-      u32x4 o;
-      if (a.out_f16) {
+    if (a.out_f16) {
+      for (int e = tid; e < mrows * RUNS; e += kThreads) {
+        const int run = e / mrows, ml = e - run * mrows;
+        const float *w = lds + ml * LDR + run * 8;
         const float d = ldexpf(1.0f, -rowexp[ml]);
+        u32x4 o;
         o[0] = pack_f16x2(w[0] * d, w[2] * d);
         o[1] = pack_f16x2(w[4] * d, w[6] * d);
         o[2] = pack_f16x2(w[1] * d, w[3] * d);
         o[3] = pack_f16x2(w[5] * d, w[7] * d);
-      } else {
+        *reinterpret_cast<u32x4 *>(a.xr + xr_tile_offset(m0 + ml, kb + run * 8, a.K)) = o;
+      }
+    } else {
+      for (int e = tid; e < mrows * RUNS; e += kThreads) {
+        const int ml = e / RUNS, run = e % RUNS;
+        const float *w = lds + ml * LDR + run * 8;
+        u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
+        *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) = o;
       }
-      *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) = o;
     }
     // 3. t += x_rot(block) V(block)^T on the matrix cores; K-steps of 16 split over the waves
     for (int p0 = 0; p0 < npair; p0 += kVB) {

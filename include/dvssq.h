@@ -125,8 +125,9 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
                         int32_t M, void *ws, uint32_t flags, void *stream);
 
 /*
- * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: two kernel launches
- * (rotation + t, then the GEMM).  Same arguments and ownership rules as
+ * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: three kernel launches
+ * (per-row scales, rotation + t, then the GEMM).  Needs K <= 2^22,
+ * M <= 2^22 and N r <= 2^29 (DVSSQ_EUNSUPPORTED otherwise).  Same arguments and ownership rules as
  * dvssq_linear_decode.  The rotated activations are held in f16 with one
  * power-of-two scale per row, the weights as exact f16 values (same s4 range
  * as decode), t = (x H) V^T in bf16 for the low-rank product; accumulation is
