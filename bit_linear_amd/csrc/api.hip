@@ -305,14 +305,8 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   p.nsr = L->n_seg * L->r;
   p.nsr_pad = nsp;
   // one workgroup column per Hadamard block (the row scale comes from the whole
-  // row in every column); the last column of a row group to finish sums t
+  // row in every column); their partial t are summed by a small kernel after
   p.tpart = reinterpret_cast<float *>(wsb + W.p_tpart);
-  p.cnt = reinterpret_cast<uint64_t *>(wsb + W.p_cnt);
-  {
-    const uint64_t gen = next_generation();
-    p.tag = static_cast<uint32_t>(gen ^ (gen >> 32));
-    if (p.tag == 0) p.tag = 1;
-  }
   p.blocks_per_wg = 1;
   p.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
   p.out_f16 = 1;

@@ -163,7 +163,6 @@ struct WsLayout {
   int64_t p_sc;    // fp32 [M_max] 2^e per row
   int64_t p_t;     // fp32 [M_max][nsr_pad] t = x_rot V^T
   int64_t p_tpart; // fp32 [K / block][M_max][nsr_pad] partial t of each Hadamard block
-  int64_t p_cnt;   // u64 [ceil(M_max / 16)] tagged arrival counters of the prologue's row groups
   int64_t p_end;
   int64_t total;
 };
@@ -195,7 +194,6 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
   w.p_sc = cur;   cur = align256(cur + 4 * static_cast<int64_t>(L.M_max));
   w.p_t = cur;    cur = align256(cur + 4 * static_cast<int64_t>(L.M_max) * nsp);
   w.p_tpart = cur; cur = align256(cur + 4 * (K / L.block) * static_cast<int64_t>(L.M_max) * nsp);
-  w.p_cnt = cur;  cur = align256(cur + 8 * ((static_cast<int64_t>(L.M_max) + 15) / 16));
   w.p_end = cur;
   w.total = w.d_end > w.p_end ? w.d_end : w.p_end;
   return w;
@@ -209,8 +207,6 @@ struct PrologueArgs {
   const uint16_t *V;   // bf16 [nsr][K] or null (no t)
   float *t;            // fp32 [M][nsr_pad] or null
   float *tpart;        // K-split: fp32 [gridDim.y][M][nsr_pad] partial t of each Hadamard block
-  uint64_t *cnt;       // K-split: tagged arrival counters, one per row group
-  uint32_t tag;        // K-split: tag of this call, never 0
   int M, K, nsr, nsr_pad;
   int blocks_per_wg;   // Hadamard blocks handled (and t-accumulated) by one workgroup
   int rotate;          // 0: x is already rotated (copy + t only)

@@ -25,20 +25,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ void st_dev(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_dev(const T *p) {
-  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// wait until every store this thread issued has completed
-__device__ __forceinline__ void drain_stores() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 template <int VPL>  // values per lane = block / 64
 __device__ __forceinline__ void load_row(const uint16_t *src, float (&v)[VPL]) {
   if constexpr (VPL >= 8) {
@@ -63,6 +49,38 @@ __device__ __forceinline__ void load_row(const uint16_t *src, float (&v)[VPL]) {
   }
 }
 
+// value of lane l ^ S (S = 1 .. 32): DPP quad permutes for 1 and 2, row shifts
+// for 4 and 8 (lanes with bit S clear read S lanes up, the others S lanes
+// down), and the permlane swaps of 16-lane rows / 32-lane halves for 16 and 32
+template <int S>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  const int x = __float_as_int(v);
+  if constexpr (S == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (S == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (S == 4 || S == 8) {
+    const int up = __builtin_amdgcn_update_dpp(0, x, 0x100 + S, 0xF, 0xF, false);
+    const int dn = __builtin_amdgcn_update_dpp(0, x, 0x110 + S, 0xF, 0xF, false);
+    return __int_as_float((lane & S) ? dn : up);
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+// one butterfly stage across lanes: lanes with bit S clear keep v + p, the
+// others p - v (p = the partner's value)
+template <int S, int VPL>
+__device__ __forceinline__ void lane_stage(float (&v)[VPL], int lane) {
+  const float sg = (lane & S) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) v[j] = fmaf(sg, v[j], xor_lane<S>(v[j], lane));
+}
+
 template <int VPL>
 __device__ __forceinline__ void fwht_wave(float (&v)[VPL], int lane) {
 #pragma unroll
@@ -74,15 +92,12 @@ __device__ __forceinline__ void fwht_wave(float (&v)[VPL], int lane) {
         v[j] = a + b;
         v[j + s] = a - b;
       }
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const bool upper = (lane & s) != 0;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const float p = __shfl_xor(v[j], s, 64);
-      v[j] = upper ? (p - v[j]) : (v[j] + p);
-    }
-  }
+  lane_stage<1>(v, lane);
+  lane_stage<2>(v, lane);
+  lane_stage<4>(v, lane);
+  lane_stage<8>(v, lane);
+  lane_stage<16>(v, lane);
+  lane_stage<32>(v, lane);
 }
 
 template <int VPL, int MT>
@@ -233,44 +248,34 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
     }
     return;
   }
-  // K split over the workgroup columns: publish this column's partial, count
-  // arrivals on the row group's tagged counter; the last column sums the
-  // partials in column order
+  // K split over the workgroup columns: this column's partial, summed in
+  // column order by treduce_kernel
   for (int e = tid; e < mrows * a.nsr_pad; e += kThreads) {
     const int ml = e / a.nsr_pad, i = e % a.nsr_pad;
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) s += red[((w * 2 + i / 32) * 32 + ml) * 32 + (i % 32)];
-    st_dev(a.tpart + (static_cast<int64_t>(blockIdx.y) * a.M + m0 + ml) * a.nsr_pad + i, s);
+    a.tpart[(static_cast<int64_t>(blockIdx.y) * a.M + m0 + ml) * a.nsr_pad + i] = s;
   }
-  drain_stores();
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t *cnt = a.cnt + blockIdx.x;
-    uint64_t old = ld_dev(cnt), nw;
-    do {
-      nw = (static_cast<uint32_t>(old >> 32) == a.tag) ? old + 1 : ((static_cast<uint64_t>(a.tag) << 32) | 1u);
-    } while (!__hip_atomic_compare_exchange_strong(cnt, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT));
-    rowexp[0] = static_cast<uint32_t>(nw) == gridDim.y;   // LDS flag: this column arrived last
-  }
-  __syncthreads();
-  if (!rowexp[0]) return;
-  constexpr int kPB = 16;
-  const int64_t pstride = static_cast<int64_t>(a.M) * a.nsr_pad;
-  for (int e = tid; e < mrows * a.nsr_pad; e += kThreads) {
-    const int ml = e / a.nsr_pad, i = e % a.nsr_pad;
-    const float *src = a.tpart + static_cast<int64_t>(m0 + ml) * a.nsr_pad + i;
-    float s = 0.0f;
-    for (int c0 = 0; c0 < static_cast<int>(gridDim.y); c0 += kPB) {
-      float v[kPB];
+}
+
+// t = sum over the workgroup columns (Hadamard blocks) of their partial t, in
+// column order; four consecutive t values per thread.
+__global__ __launch_bounds__(kThreads) void treduce_kernel(PrologueArgs a, int ncol) {
+  const int64_t n4 = static_cast<int64_t>(a.M) * a.nsr_pad / 4;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (e >= n4) return;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(a.tpart) + e;
+  constexpr int kB = 8;
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < ncol; c0 += kB) {
+    f32x4 v[kB];
 #pragma unroll
-      for (int j = 0; j < kPB; ++j) v[j] = c0 + j < static_cast<int>(gridDim.y) ? ld_dev(src + (c0 + j) * pstride) : 0.0f;
+    for (int j = 0; j < kB; ++j) v[j] = c0 + j < ncol ? src[(c0 + j) * n4] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < kPB; ++j) s += v[j];
-    }
-    a.t[static_cast<int64_t>(m0 + ml) * a.nsr_pad + i] = s;
+    for (int j = 0; j < kB; ++j) s += v[j];
   }
+  reinterpret_cast<f32x4 *>(a.t)[e] = s;
 }
 
 // Per-row power-of-two scale 2^e of the f16 x_rot: from the bound
@@ -324,15 +329,22 @@ hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hi
                                        dim3((a.M + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, s, a);
     if (e != hipSuccess) return e;
   }
+  hipError_t e;
   switch (block) {
-    case 64: return launch_vpl<1, 32>(a, n_wg_blocks, s);
-    case 128: return launch_vpl<2, 32>(a, n_wg_blocks, s);
-    case 256: return launch_vpl<4, 32>(a, n_wg_blocks, s);
-    case 512: return launch_vpl<8, 32>(a, n_wg_blocks, s);
-    case 1024: return launch_vpl<16, 16>(a, n_wg_blocks, s);
-    case 2048: return launch_vpl<32, 16>(a, n_wg_blocks, s);
+    case 64: e = launch_vpl<1, 32>(a, n_wg_blocks, s); break;
+    case 128: e = launch_vpl<2, 32>(a, n_wg_blocks, s); break;
+    case 256: e = launch_vpl<4, 32>(a, n_wg_blocks, s); break;
+    case 512: e = launch_vpl<8, 32>(a, n_wg_blocks, s); break;
+    case 1024: e = launch_vpl<16, 16>(a, n_wg_blocks, s); break;
+    case 2048: e = launch_vpl<32, 16>(a, n_wg_blocks, s); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess || a.nsr == 0 || n_wg_blocks == 1) return e;
+  const int64_t n4 = static_cast<int64_t>(a.M) * a.nsr_pad / 4;
+  const int ncol = n_wg_blocks;
+  void *args[] = {const_cast<PrologueArgs *>(&a), const_cast<int *>(&ncol)};
+  return hipLaunchKernel(reinterpret_cast<const void *>(treduce_kernel), dim3((n4 + kThreads - 1) / kThreads),
+                         dim3(kThreads), args, 0, s);
 }
 
 }  // namespace dvssq
