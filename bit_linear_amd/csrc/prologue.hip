@@ -104,6 +104,10 @@ template <int VPL, int MT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   constexpr int B = 64 * VPL;
   constexpr int LDR = B + 4;  // padded LDS row (fp32)
+  // blocks of 512 and more stage 16-bit values (the output format: f16 scaled
+  // and permuted, or bf16), so that two workgroups fit in LDS
+  constexpr bool H16 = VPL >= 8;
+  constexpr int LDH = B + 8;  // padded LDS row (16-bit)
   extern __shared__ __align__(16) float lds[];
   __shared__ int rowexp[MT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -164,18 +168,35 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
       for (int j = 0; j < RB; ++j) {
         const int ml = ml0 + 4 * j;
         if (ml >= MT) break;
-        float *row = lds + ml * LDR + lane * VPL;
-        if (ml < mrows) {
-          if (a.rotate) {
-            fwht_wave<VPL>(v[j], lane);
+        if (ml < mrows && a.rotate) {
+          fwht_wave<VPL>(v[j], lane);
 #pragma unroll
-            for (int q = 0; q < VPL; ++q) v[j][q] *= a.hscale;
+          for (int q = 0; q < VPL; ++q) v[j][q] *= a.hscale;
+        }
+        if constexpr (H16) {
+          uint16_t *row = reinterpret_cast<uint16_t *>(lds) + ml * LDH + lane * VPL;
+          const float d = a.out_f16 ? ldexpf(1.0f, -rowexp[ml]) : 1.0f;
+#pragma unroll
+          for (int r = 0; r < VPL / 8; ++r) {
+            const float *w = v[j] + 8 * r;
+            u32x4 o = {0u, 0u, 0u, 0u};
+            if (ml < mrows) {
+              if (a.out_f16) {
+                o[0] = pack_f16x2(w[0] * d, w[2] * d);
+                o[1] = pack_f16x2(w[4] * d, w[6] * d);
+                o[2] = pack_f16x2(w[1] * d, w[3] * d);
+                o[3] = pack_f16x2(w[5] * d, w[7] * d);
+              } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
+              }
+            }
+            *reinterpret_cast<u32x4 *>(row + 8 * r) = o;
           }
-#pragma unroll
-          for (int q = 0; q < VPL; ++q) row[q] = v[j][q];
         } else {
+          float *row = lds + ml * LDR + lane * VPL;
 #pragma unroll
-          for (int q = 0; q < VPL; ++q) row[q] = 0.0f;
+          for (int q = 0; q < VPL; ++q) row[q] = ml < mrows ? v[j][q] : 0.0f;
         }
       }
     }
@@ -183,7 +204,22 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
     // 2. copy out in runs of 8: f16 into the GEMM's tiles (consecutive threads
     // take consecutive rows of one run), bf16 row-major
     constexpr int RUNS = B / 8;
-    if (a.out_f16) {
+    if constexpr (H16) {
+      const uint16_t *h = reinterpret_cast<const uint16_t *>(lds);
+      if (a.out_f16) {
+        for (int e = tid; e < mrows * RUNS; e += kThreads) {
+          const int run = e / mrows, ml = e - run * mrows;
+          *reinterpret_cast<u32x4 *>(a.xr + xr_tile_offset(m0 + ml, kb + run * 8, a.K)) =
+              *reinterpret_cast<const u32x4 *>(h + ml * LDH + run * 8);
+        }
+      } else {
+        for (int e = tid; e < mrows * RUNS; e += kThreads) {
+          const int ml = e / RUNS, run = e % RUNS;
+          *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) =
+              *reinterpret_cast<const u32x4 *>(h + ml * LDH + run * 8);
+        }
+      }
+    } else if (a.out_f16) {
       for (int e = tid; e < mrows * RUNS; e += kThreads) {
         const int run = e / mrows, ml = e - run * mrows;
         const float *w = lds + ml * LDR + run * 8;
@@ -215,9 +251,22 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
         const int st = wave + 4 * (pr >> (n_it - 1)), it = pr & (n_it - 1);
         u32x4 av = {0u, 0u, 0u, 0u};
         if (arow < MT) {
-          const float *w = lds + arow * LDR + 16 * st + 8 * half;
+          if constexpr (H16) {
+            // staged f16 run in the order 0,2,4,6,1,3,5,7, scaled by 2^-e: back
+            // to x_rot, as natural-order bf16 pairs
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(lds) + arow * LDH +
+                                                             16 * st + 8 * half);
+            const float sc = ldexpf(1.0f, rowexp[arow]);
+            auto f = [](uint32_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h))); };
+            av[0] = pack_bf16x2(f(w[0] & 0xFFFFu) * sc, f(w[2] & 0xFFFFu) * sc);
+            av[1] = pack_bf16x2(f(w[0] >> 16) * sc, f(w[2] >> 16) * sc);
+            av[2] = pack_bf16x2(f(w[1] & 0xFFFFu) * sc, f(w[3] & 0xFFFFu) * sc);
+            av[3] = pack_bf16x2(f(w[1] >> 16) * sc, f(w[3] >> 16) * sc);
+          } else {
+            const float *w = lds + arow * LDR + 16 * st + 8 * half;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) av[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
+            for (int q = 0; q < 4; ++q) av[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
+          }
         }
         if (it == 0) acc[0] = mfma32x32x16(av, vb[j], acc[0]);
         else acc[1] = mfma32x32x16(av, vb[j], acc[1]);
@@ -304,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void rowscale_kernel(PrologueArgs a) {
 template <int VPL, int MT>
 hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
   constexpr int B = 64 * VPL;
-  const size_t lds_rows = static_cast<size_t>(MT) * (B + 4) * 4;
+  const size_t lds_rows = VPL >= 8 ? static_cast<size_t>(MT) * (B + 8) * 2 : static_cast<size_t>(MT) * (B + 4) * 4;
   const size_t lds_red = 4 * 2 * 32 * 32 * 4;
   const size_t lds = lds_rows > lds_red ? lds_rows : lds_red;
   if (lds > 65536) {
