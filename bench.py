@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-table", action="store_true", help="skip the secondary shapes")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="time only the prefill shapes (for kernel traces of the prefill path)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 256 MiB device copy (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -166,6 +168,19 @@ def traffic_record():
     return rec.get("traffic_bytes_per_launch")
 
 
+def prefill_table(dv, torch, layers, steps):
+    table = []
+    for name, m in (("spark_gateup", 512), ("spark_gateup", 2048), ("minicpm_gate", 4096),
+                    ("minicpm_down", 4096)):
+        r = Runner(dv, torch, layers[name], m, m, min_bytes=256 << 20, max_copies=16)
+        t, _ = time_calls(torch, r.prefill, steps, 3)
+        tf = r.flops() / (t * 1e-3) / 1e12
+        table.append({"workload": f"{name} prefill M={m}", "us_per_call": round(t * 1e3, 2),
+                      "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
+        r.free()
+    return table
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -179,6 +194,9 @@ def main():
 
     torch.cuda.set_device(0)
     layers = {l.name: l for w in synth.WORKLOADS.values() for l in w.layers}
+    if args.only_prefill:
+        print(json.dumps({"prefill_table": prefill_table(dv, torch, layers, args.prefill_steps)}), flush=True)
+        return
     up = layers["spark_up"]
     M = args.decode_m
     head = Runner(dv, torch, up, M, 32)
@@ -218,14 +236,7 @@ def main():
                 table.append({"workload": f"{name} decode M={m}", "us_per_call": round(t * 1e3, 3),
                               "gbs": round(g, 1), "frac_hbm": round(g / HBM_PEAK_GBS, 4)})
                 r.free()
-        for name, m in (("spark_gateup", 512), ("spark_gateup", 2048), ("minicpm_gate", 4096),
-                        ("minicpm_down", 4096)):
-            r = Runner(dv, torch, layers[name], m, m, min_bytes=256 << 20, max_copies=16)
-            t, _ = time_calls(torch, r.prefill, args.prefill_steps, 3)
-            tf = r.flops() / (t * 1e-3) / 1e12
-            table.append({"workload": f"{name} prefill M={m}", "us_per_call": round(t * 1e3, 2),
-                          "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
-            r.free()
+        table += prefill_table(dv, torch, layers, args.prefill_steps)
         out["table"] = table
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(up, head_blob, head_x, args.cpu_seconds)
