@@ -217,3 +217,60 @@ def quantize_layer(layer, seed: int = 0, power_iters: int = 4, want_diag: bool =
         omega = np.stack([synth.sketch(seed, layer, s, l) for s in range(layer.n_seg)])
     return quantize(W, layer.r, layer.block, layer.n_seg, omega=omega, power_iters=power_iters,
                     full_svd=full, want_diag=want_diag)
+
+
+# ------------------------------------------------------------------ gated MLP block (test infrastructure)
+# The Spark model page describes the feed-forward block as gate, up and down
+# projections with GELU (Spark-X2.5-4B GGUF page, "The model": GELU FFN; ASHQ1
+# page, Architecture: ffn_gate / ffn_up / ffn_down).  Readings: GELU is the
+# exact x * Phi(x); the gate and up projections are the two segments of one
+# fused layer (segment 0 = gate, segment 1 = up); every tensor between the
+# projections is bf16, as in the BF16 model: the layer outputs are rounded to
+# bf16, gelu(gate) * up is computed exactly and rounded to bf16, and that is
+# the down projection's input.
+
+def bf16_round_bits(v: np.ndarray) -> np.ndarray:
+    """Nearest-even bf16 rounding of fp64 values (this module's C rounding), as bits."""
+    f = np.frompyfunc(lambda t: int(lib().orc_bf16_from_double(float(t))), 1, 1)
+    return np.asarray(f(np.asarray(v, dtype=np.float64)), dtype=np.uint16)
+
+
+def bf16_bits_value(bits: np.ndarray) -> np.ndarray:
+    f = np.frompyfunc(lambda h: float(lib().orc_bf16_to_double(int(h))), 1, 1)
+    return np.asarray(f(np.asarray(bits, dtype=np.uint16)), dtype=np.float64)
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """GELU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 (the standard normal CDF Phi)."""
+    import scipy.special
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + scipy.special.erf(x / np.sqrt(2.0)))
+
+
+def mlp_intermediate(y_gate_up: np.ndarray) -> np.ndarray:
+    """bf16 bits of gelu(gate) * up from the fused layer's fp64 output [M][2I]."""
+    I = y_gate_up.shape[1] // 2
+    g = bf16_bits_value(bf16_round_bits(y_gate_up[:, :I]))
+    u = bf16_bits_value(bf16_round_bits(y_gate_up[:, I:]))
+    return bf16_round_bits(gelu(g) * u)
+
+
+def mlp_forward(gu_blob: np.ndarray, gu: tuple, down_blob: np.ndarray, down: tuple, x_bf16: np.ndarray,
+                nthreads: int = 0) -> np.ndarray:
+    """y = down(bf16(gelu(bf16(gate(x))) * bf16(up(x)))) in fp64, with gate and up
+    the two segments of the fused layer gu = (N, K, r, block) and down = (N, K, r, block)."""
+    N, K, r, b = gu
+    y_gu = forward(gu_blob, N, K, r, b, 2, x_bf16, nthreads)
+    h = mlp_intermediate(y_gu)
+    Nd, Kd, rd, bd = down
+    return forward(down_blob, Nd, Kd, rd, bd, 1, h, nthreads)
+
+
+def mlp_forward_cols(gu_blob: np.ndarray, gu: tuple, down_blob: np.ndarray, down: tuple, x_bf16: np.ndarray,
+                     cols, nthreads: int = 0) -> np.ndarray:
+    """mlp_forward restricted to output columns cols of the down projection."""
+    N, K, r, b = gu
+    y_gu = forward(gu_blob, N, K, r, b, 2, x_bf16, nthreads)
+    h = mlp_intermediate(y_gu)
+    Nd, Kd, rd, bd = down
+    return forward_cols(down_blob, Nd, Kd, rd, bd, 1, h, cols, nthreads)

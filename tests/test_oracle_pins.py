@@ -420,3 +420,78 @@ def test_planted_mistakes_are_caught(tiny_case):
         ref = np.zeros_like(y)
         ref[:, idx] = bad
         assert np.abs(y - ref).max() > 1e-6 * np.abs(y).max(), name
+
+
+# ------------------------------------------------------------------ gated MLP block
+
+def test_gelu_closed_forms():
+    """GELU(x) = x Phi(x): tabulated normal-CDF values, the odd-part identity
+    GELU(x) - GELU(-x) = x (Phi(x) + Phi(-x) = 1), its limits, and Phi as the
+    integral of the normal density (a different route than erf)."""
+    import scipy.integrate
+    assert oracle.gelu(np.array([0.0]))[0] == 0.0
+    # Phi(1) = 0.8413447460685429, Phi(2) = 0.9772498680518208, Phi(-1) = 0.15865525393145707
+    np.testing.assert_allclose(oracle.gelu(np.array([1.0, 2.0, -1.0])),
+                               [0.8413447460685429, 2 * 0.9772498680518208, -0.15865525393145707],
+                               rtol=2e-15, atol=0)
+    x = np.random.default_rng(3).normal(0.0, 3.0, 200)
+    np.testing.assert_allclose(oracle.gelu(x) - oracle.gelu(-x), x, rtol=0, atol=1e-14)
+    assert oracle.gelu(np.array([10.0]))[0] == 10.0
+    assert abs(oracle.gelu(np.array([-10.0]))[0]) < 1e-20
+    pdf = lambda t: np.exp(-0.5 * t * t) / np.sqrt(2 * np.pi)
+    for v in (-2.5, -0.3, 0.7, 1.9):
+        phi = 0.5 + scipy.integrate.quad(pdf, 0.0, v, epsabs=1e-15, epsrel=1e-14)[0]
+        assert abs(oracle.gelu(np.array([v]))[0] - v * phi) < 1e-13
+
+
+def _dense_layer(blob, lay, n_seg, x_f64):
+    """y = (x H) (W_hat + U V_seg)^T from the numpy decode of the packed bytes and
+    scipy's Sylvester matrix (block = K), in original output order."""
+    idx, What, U, V = _decode_blob_numpy(blob, lay.N, lay.K, lay.r, n_seg)
+    seg = idx // (lay.N // n_seg)
+    low = np.stack([U[p] @ V[seg[p] * lay.r:(seg[p] + 1) * lay.r] for p in range(lay.N)])
+    H = scipy.linalg.hadamard(lay.K) / np.sqrt(lay.K)
+    y = np.zeros((x_f64.shape[0], lay.N))
+    y[:, idx] = (x_f64 @ H) @ (What + low).T
+    return y
+
+
+@pytest.fixture(scope="module")
+def mlp_case():
+    I, Hd = 128, 128
+    gu = synth.Layer("mlp_gu", N=2 * I, K=Hd, block=Hd, r=4, n_seg=2, n_outlier=2, outlier_tag="mlp")
+    dn = synth.Layer("mlp_dn", N=Hd, K=I, block=I, r=4)
+    bg = oracle.quantize(synth.weights_bf16(0, gu), gu.r, gu.block, n_seg=2, full_svd=True)
+    bd = oracle.quantize(synth.weights_bf16(1, dn), dn.r, dn.block, full_svd=True)
+    return gu, dn, bg, bd
+
+
+def test_mlp_chain_dense_brute_force(mlp_case):
+    """The chained oracle against a dense route: decoded matrices, scipy's
+    Hadamard matrix, GELU through scipy.stats' normal CDF, bf16 rounding by exact
+    rational arithmetic between the projections."""
+    import scipy.stats
+    gu, dn, bg, bd = mlp_case
+    x = synth.activations_bf16(0, "mlp", 3, gu.K)
+    y = oracle.mlp_forward(bg, (gu.N, gu.K, gu.r, gu.block), bd, (dn.N, dn.K, dn.r, dn.block), x)
+    rb = np.vectorize(lambda v: synth.bf16_bits_to_f64(np.array([exact_bf16(float(v))], dtype=np.uint16))[0])
+    ygu = _dense_layer(bg, gu, 2, synth.bf16_bits_to_f64(x))
+    I = gu.N // 2
+    g, u = rb(ygu[:, :I]), rb(ygu[:, I:])
+    h = rb(g * scipy.stats.norm.cdf(g) * u)
+    ref = _dense_layer(bd, dn, 1, h)
+    assert np.abs(y - ref).max() <= 1e-10 * np.abs(ref).max()
+    # planted mistakes (in the dense route): gate and up swapped, GELU dropped
+    for bad in (rb(u * scipy.stats.norm.cdf(u) * g), rb(g * u)):
+        assert np.abs(y - _dense_layer(bd, dn, 1, bad)).max() > 1e-3 * np.abs(ref).max()
+
+
+def test_mlp_chain_columns_and_zero(mlp_case):
+    gu, dn, bg, bd = mlp_case
+    x = synth.activations_bf16(1, "mlp", 2, gu.K)
+    a, b = (gu.N, gu.K, gu.r, gu.block), (dn.N, dn.K, dn.r, dn.block)
+    y = oracle.mlp_forward(bg, a, bd, b, x)
+    cols = np.array([0, 77, 127, 3])
+    np.testing.assert_array_equal(oracle.mlp_forward_cols(bg, a, bd, b, x, cols), y[:, cols])
+    z = oracle.mlp_forward(bg, a, bd, b, np.zeros_like(x))
+    assert np.all(z == 0.0)
