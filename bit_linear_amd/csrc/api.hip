@@ -199,6 +199,17 @@ static int compute_units() {
   return v;
 }
 
+// the decode's shape conditions beyond the argument checks: K a whole number
+// of rotation units, and a plan that fits
+static int decode_supported(const dvssq_layout &L, int32_t M) {
+  if (L.K % decode_unit(L.block) != 0) return DVSSQ_EUNSUPPORTED;
+  SmallPlan sp{};
+  if (M <= kSmallMaxM && plan_decode_small(L, M, compute_units(), &sp)) return sp.S > 0 ? DVSSQ_OK : DVSSQ_EUNSUPPORTED;
+  const int S = decode_split(L.K, decode_groups(L.n_int4) + decode_groups(L.n_int8), M, decode_unit(L.block),
+                             nsr_pad_of(L.n_seg, L.r));
+  return S > 0 ? DVSSQ_OK : DVSSQ_EUNSUPPORTED;
+}
+
 int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M,
                         void *ws, uint32_t flags, void *stream) {
   int rc = check_call(L, blob, x, y, M, ws, DVSSQ_DECODE_MAX_M);
@@ -340,6 +351,68 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   f.m_tiles = (M + kPfTileM - 1) / kPfTileM;
   e = launch_prefill(f, s);
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
+}
+
+// ------------------------------------------------------------------ gated MLP block (decode)
+// workspace: [0, base) shared by the two projections (one after the other on
+// the stream), then the fused gate+up output and the intermediate h
+struct MlpWs {
+  int32_t M_cap;
+  int64_t ygu, h, total;
+};
+
+static MlpWs mlp_ws(const dvssq_layout &gu, const dvssq_layout &down) {
+  MlpWs w{};
+  w.M_cap = std::min(DVSSQ_DECODE_MAX_M, std::min(gu.M_max, down.M_max));
+  w.ygu = align256(std::max(gu.ws_bytes, down.ws_bytes));
+  w.h = align256(w.ygu + 2 * static_cast<int64_t>(w.M_cap) * gu.N);
+  w.total = align256(w.h + 2 * static_cast<int64_t>(w.M_cap) * down.K);
+  return w;
+}
+
+static int check_mlp(const dvssq_layout *gu, const dvssq_layout *down) {
+  if (gu == nullptr || down == nullptr) return DVSSQ_EINVAL;
+  int rc = check_layout(gu);
+  if (rc != DVSSQ_OK) return rc;
+  rc = check_layout(down);
+  if (rc != DVSSQ_OK) return rc;
+  if (gu->n_seg != 2 || down->n_seg != 1 || gu->N != 2 * down->K || down->N != gu->K) return DVSSQ_EINVAL;
+  return DVSSQ_OK;
+}
+
+int dvssq_mlp_ws_bytes(const dvssq_layout *gu, const dvssq_layout *down, int64_t *bytes) {
+  if (bytes == nullptr) return DVSSQ_EINVAL;
+  const int rc = check_mlp(gu, down);
+  if (rc != DVSSQ_OK) return rc;
+  *bytes = mlp_ws(*gu, *down).total;
+  return DVSSQ_OK;
+}
+
+int dvssq_mlp_decode(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down, const void *down_blob,
+                     const void *x, void *y, int32_t M, void *ws, uint32_t flags, void *stream) {
+  int rc = check_mlp(gu, down);
+  if (rc != DVSSQ_OK) return rc;
+  if (!gu_blob || !down_blob || !x || !y || !ws) return DVSSQ_EINVAL;
+  if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
+  if (M < 1 || M > gu->M_max || M > down->M_max) return DVSSQ_EINVAL;
+  if (M > DVSSQ_DECODE_MAX_M) return DVSSQ_EUNSUPPORTED;
+  if (!aligned(ws, 256) || !aligned(y, 16) || !aligned(x, 16)) return DVSSQ_EINVAL;
+  const MlpWs W = mlp_ws(*gu, *down);
+  const size_t yb = static_cast<size_t>(M) * down->N * 2, xb = static_cast<size_t>(M) * gu->K * 2;
+  if (overlap(y, yb, ws, W.total) || overlap(x, xb, ws, W.total) || overlap(x, xb, y, yb) ||
+      overlap(y, yb, gu_blob, gu->blob_bytes) || overlap(y, yb, down_blob, down->blob_bytes))
+    return DVSSQ_EINVAL;
+  if ((rc = decode_supported(*gu, M)) != DVSSQ_OK || (rc = decode_supported(*down, M)) != DVSSQ_OK) return rc;
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  void *ygu = wsb + W.ygu;
+  void *h = wsb + W.h;
+  // every check of the two projection calls has passed above (same M, buffers
+  // disjoint by construction): after the first launch only a launch error can occur
+  rc = dvssq_linear_decode(gu, gu_blob, x, ygu, M, ws, flags, stream);
+  if (rc != DVSSQ_OK) return rc;
+  GegluArgs g{static_cast<const uint16_t *>(ygu), static_cast<uint16_t *>(h), M, down->K};
+  if (launch_geglu(g, static_cast<hipStream_t>(stream)) != hipSuccess) return DVSSQ_EHIP;
+  return dvssq_linear_decode(down, down_blob, h, y, M, ws, 0, stream);
 }
 
 const char *dvssq_status_str(int status) {

@@ -266,7 +266,14 @@ struct PrefillArgs {
   int n4_tiles, n8_tiles, m_tiles;
 };
 
+struct GegluArgs {
+  const uint16_t *ygu;  // bf16 [M][2I]: gate (columns 0 .. I-1) and up (I .. 2I-1)
+  uint16_t *h;          // bf16 [M][I] = gelu(gate) * up
+  int M, I;             // I a multiple of 8
+};
+
 // launchers (return hipError_t of the launch)
+hipError_t launch_geglu(const GegluArgs &a, hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 size_t decode_lds_bytes(int M, int unit, int KW, int nsr_pad);

@@ -136,6 +136,40 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
 int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x, void *y,
                          int32_t M, void *ws, uint32_t flags, void *stream);
 
+/*
+ * Workspace size of dvssq_mlp_decode for the pair (gu, down), into *bytes.
+ * Host-only.  DVSSQ_EINVAL if the pair does not form a gated MLP block (see
+ * dvssq_mlp_decode) or bytes is null.
+ */
+int dvssq_mlp_ws_bytes(const dvssq_layout *gu, const dvssq_layout *down, int64_t *bytes);
+
+/*
+ * Gated MLP block, decode form (Spark-X2.5-4B GGUF page, "The model": a GELU
+ * feed-forward block; ASHQ1 page, Architecture: ffn_gate, ffn_up, ffn_down):
+ *
+ *     y = down( gelu(gate(x)) * up(x) )
+ *
+ * gate and up are the two segments of the fused layer gu (segment 0 = gate,
+ * output columns 0 .. I-1; segment 1 = up, I .. 2I-1), down is a one-segment
+ * layer.  Requires gu->n_seg == 2, down->n_seg == 1, gu->N == 2 down->K (= 2I),
+ * down->N == gu->K (DVSSQ_EINVAL otherwise), 1 <= M <= min(gu->M_max,
+ * down->M_max), M <= 32, and both layers accepted by dvssq_linear_decode.
+ * GELU is the exact v Phi(v) = v (1 + erf(v / sqrt 2)) / 2 in fp32; the tensors
+ * between the projections are bf16 as in a BF16 model: the fused layer's output
+ * is bf16 (as from dvssq_linear_decode), gelu(gate) * up is rounded once to bf16
+ * and is the down projection's input.  Three kernel launches on `stream`: the
+ * fused decode, the GELU product, the down decode.
+ * x: device bf16 [M][gu->K] (x.H when flags has DVSSQ_X_ROTATED; the flag
+ * concerns x only).  y: device bf16 [M][down->N]; x and y 16-byte aligned and
+ * disjoint from each other, from the blobs and from ws.  ws: device,
+ * dvssq_mlp_ws_bytes bytes, 256-byte aligned, no initialization needed, one
+ * call in flight per ws; it holds the fused output and the intermediate.
+ * Same ownership and error rules as dvssq_linear_decode.
+ */
+int dvssq_mlp_decode(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down,
+                     const void *down_blob, const void *x, void *y, int32_t M, void *ws,
+                     uint32_t flags, void *stream);
+
 /* Static text for a return code. */
 const char *dvssq_status_str(int status);
 

@@ -43,6 +43,10 @@ EXTRA = {
                                 outlier_tag="b2048"),
     "seg2_small": synth.Layer("seg2_small", N=2 * 256, K=256, block=256, r=24, n_seg=2,
                               n_outlier=3, outlier_tag="seg2_small"),
+    # a small gated MLP block: fused gate+up (I = 256) and its down projection
+    "mlp_tiny_gu": synth.Layer("mlp_tiny_gu", N=2 * 256, K=256, block=256, r=4, n_seg=2, n_outlier=3,
+                               outlier_tag="mlp_tiny"),
+    "mlp_tiny_dn": synth.Layer("mlp_tiny_dn", N=256, K=256, block=256, r=4),
 }
 LAYERS.update(EXTRA)
 

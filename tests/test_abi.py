@@ -157,3 +157,47 @@ def test_binding_raises_on_error():
     with pytest.raises(dv.DvssqError) as ei:
         dv.pack_info(516, 256, 4, 256)
     assert ei.value.code == dv.DVSSQ_EINVAL
+
+
+# ------------------------------------------------------------------ gated MLP block
+
+def test_mlp_ws_bytes_and_pairing():
+    gu = dv.pack_info(20480, 2560, 24, 256, 2, M_max=32)
+    dn = dv.pack_info(2560, 10240, 16, 256, 1, M_max=32)
+    n = dv.mlp_ws_bytes(gu, dn)
+    assert n % 256 == 0 and n >= max(gu.ws_bytes, dn.ws_bytes) + 2 * 32 * (20480 + 10240)
+    f, out, E = dv.lib().dvssq_mlp_ws_bytes, C.c_int64(0), dv.DVSSQ_EINVAL
+    assert f(C.byref(dn), C.byref(gu), C.byref(out)) == E          # swapped pair
+    assert f(C.byref(gu), C.byref(dn), None) == E
+    assert f(None, C.byref(dn), C.byref(out)) == E
+    one = dv.pack_info(20480, 2560, 24, 256, 1, M_max=32)            # not a two-segment layer
+    assert f(C.byref(one), C.byref(dn), C.byref(out)) == E
+    wrong = dv.pack_info(2560, 5120, 16, 256, 1, M_max=32)           # down K != I
+    assert f(C.byref(gu), C.byref(wrong), C.byref(out)) == E
+
+
+def test_mlp_decode_error_paths():
+    gu = dv.pack_info(512, 256, 4, 256, 2, M_max=64)
+    dn = dv.pack_info(256, 256, 4, 256, 1, M_max=64)
+    GB, DB = 0x10000000, 0x18000000
+    f, E = dv.lib().dvssq_mlp_decode, dv.DVSSQ_EINVAL
+
+    def c(g=gu, gb=GB, d=dn, db=DB, x=X, y=Y, M=1, ws=WS, flags=0):
+        return f(C.byref(g) if g is not None else None, gb, C.byref(d) if d is not None else None, db, x, y, M,
+                 ws, flags, None)
+
+    assert c(g=None) == E and c(d=None) == E
+    assert c(gb=None) == E and c(db=None) == E
+    assert c(x=None) == E and c(y=None) == E and c(ws=None) == E
+    assert c(M=0) == E and c(M=65) == E
+    assert c(M=33) == dv.DVSSQ_EUNSUPPORTED
+    assert c(flags=2) == E
+    assert c(ws=WS + 128) == E and c(x=X + 2) == E and c(y=Y + 8) == E
+    assert c(y=X + 256) == E                                   # y overlaps x
+    assert c(y=WS + 1024) == E                                 # y overlaps ws
+    assert c(g=dn, d=gu) == E                                  # swapped pair
+    # both projections must be decodable (K a multiple of max(block, 256)):
+    # refused before anything is enqueued
+    g2 = dv.pack_info(384, 192, 4, 64, 2, M_max=64)
+    d2 = dv.pack_info(192, 192, 4, 64, 1, M_max=64)
+    assert c(g=g2, d=d2) == dv.DVSSQ_EUNSUPPORTED

@@ -199,3 +199,50 @@ def test_decode_matches_prefill():
     yd = cases.from_device_bf16(lin.forward(x, path="decode"))
     yp = cases.from_device_bf16(lin.forward(x, path="prefill"))
     assert cases.rel_err(yd, yp) <= cases.TOL
+
+
+# ------------------------------------------------------------------ gated MLP block (decode)
+
+MLP_CASES = [("mlp_tiny_gu", "mlp_tiny_dn", 1), ("mlp_tiny_gu", "mlp_tiny_dn", 3), ("mlp_tiny_gu", "mlp_tiny_dn", 32),
+             ("spark_gateup", "spark_down", 1), ("spark_gateup", "spark_down", 4)]
+
+
+def gpu_mlp(gname, dname):
+    g, gb, lg = gpu_layer(gname, 32)
+    d, db, ld = gpu_layer(dname, 32)
+    return g, gb, d, db, dv.MLP(lg, ld)
+
+
+@pytest.mark.parametrize("gname,dname,M", MLP_CASES, ids=[f"{g}-M{m}" for g, _, m in MLP_CASES])
+def test_mlp_decode_parity(gname, dname, M):
+    """y = down(gelu(gate(x)) * up(x)) through dvssq_mlp_decode against the chained oracle."""
+    g, gb, d, db, mlp = gpu_mlp(gname, dname)
+    x_bits = cases.activations(gname, M)
+    y = mlp.forward(cases.to_device_bf16(x_bits, DEV))
+    torch.cuda.synchronize()
+    ref = oracle.mlp_forward(gb, (g.N, g.K, g.r, g.block), db, (d.N, d.K, d.r, d.block), x_bits)
+    err = cases.rel_err(cases.from_device_bf16(y), ref)
+    print(f"{gname}+{dname} M={M} mlp rel_err={err:.3e}")
+    assert err <= cases.TOL
+
+
+def test_mlp_decode_matches_its_parts():
+    """The block equals its three steps run separately: the fused decode, the
+    GELU product on the host (fp32, one bf16 rounding) and the down decode."""
+    g, gb, d, db, mlp = gpu_mlp("mlp_tiny_gu", "mlp_tiny_dn")
+    M = 5
+    x = cases.to_device_bf16(cases.activations("mlp_tiny_gu", M), DEV)
+    y = mlp.forward(x)
+    ygu = mlp.gu.forward(x, path="decode").float()
+    I = g.N // 2
+    h = (torch.nn.functional.gelu(ygu[:, :I]) * ygu[:, I:]).to(torch.bfloat16)
+    y2 = mlp.down.forward(h, path="decode")
+    torch.cuda.synchronize()
+    assert cases.rel_err(cases.from_device_bf16(y), cases.from_device_bf16(y2)) <= 0.2 * cases.TOL
+
+
+def test_mlp_decode_rejects_mismatched_pair():
+    g, gb, lg = gpu_layer("mlp_tiny_gu", 32)
+    d, db, ld = gpu_layer("tiny", 32)
+    with pytest.raises(dv.DvssqError):
+        dv.MLP(lg, ld)
