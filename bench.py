@@ -168,6 +168,35 @@ def traffic_record():
     return rec.get("traffic_bytes_per_launch")
 
 
+class MlpRunner:
+    """The gated MLP block (fused gate+up, then down) through dvssq_mlp_decode,
+    both layers' blobs cycled over replicas like the single-layer runs."""
+
+    def __init__(self, dv, torch, gu, down, M):
+        import synth
+        self.M = M
+        self.Lg, _, self.cg, self.C = make_copies(dv, torch, gu, 32, 1 << 30, 128)
+        self.Ld, _, self.cd, Cd = make_copies(dv, torch, down, 32, 1 << 30, 128)
+        self.C = min(self.C, Cd)
+        x_bits = synth.activations_bf16(0, gu.outlier_tag or gu.name, M, gu.K)
+        self.x = torch.from_numpy(x_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+        self.y = torch.empty((M, down.N), dtype=torch.bfloat16, device="cuda")
+        self.ws = dv.device_buffer(dv.mlp_ws_bytes(self.Lg, self.Ld))
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.dv = dv
+
+    def call(self, i):
+        k = i % self.C
+        self.dv.mlp_decode(self.Lg, self.cg[k].data_ptr(), self.Ld, self.cd[k].data_ptr(), self.x.data_ptr(),
+                           self.y.data_ptr(), self.M, self.ws.data_ptr(), 0, self.stream)
+
+    def algo_bytes(self):
+        return self.Lg.algo_bytes + self.Ld.algo_bytes
+
+    def free(self):
+        del self.cg, self.cd, self.ws
+
+
 def prefill_table(dv, torch, layers, steps):
     table = []
     for name, m in (("spark_gateup", 512), ("spark_gateup", 2048), ("minicpm_gate", 4096),
@@ -236,6 +265,13 @@ def main():
                 table.append({"workload": f"{name} decode M={m}", "us_per_call": round(t * 1e3, 3),
                               "gbs": round(g, 1), "frac_hbm": round(g / HBM_PEAK_GBS, 4)})
                 r.free()
+        for m in (1, 4):
+            r = MlpRunner(dv, torch, layers["spark_gateup"], layers["spark_down"], m)
+            t, _ = time_calls(torch, r.call, args.table_steps, 20)
+            g = r.algo_bytes() / (t * 1e-3) / 1e9
+            table.append({"workload": f"spark MLP block (gate+up, GELU, down) decode M={m}",
+                          "us_per_call": round(t * 1e3, 3), "gbs": round(g, 1), "frac_hbm": round(g / HBM_PEAK_GBS, 4)})
+            r.free()
         table += prefill_table(dv, torch, layers, args.prefill_steps)
         out["table"] = table
     if not args.no_cpu:
