@@ -172,11 +172,13 @@ class MlpRunner:
     """The gated MLP block (fused gate+up, then down) through dvssq_mlp_decode,
     both layers' blobs cycled over replicas like the single-layer runs."""
 
-    def __init__(self, dv, torch, gu, down, M):
+    def __init__(self, dv, torch, gu, down, M, prefill=False):
         import synth
-        self.M = M
-        self.Lg, _, self.cg, self.C = make_copies(dv, torch, gu, 32, 1 << 30, 128)
-        self.Ld, _, self.cd, Cd = make_copies(dv, torch, down, 32, 1 << 30, 128)
+        self.M, self.gu, self.down = M, gu, down
+        mm, nb, nc = (M, 256 << 20, 16) if prefill else (32, 1 << 30, 128)
+        self.fn = dv.mlp_prefill if prefill else dv.mlp_decode
+        self.Lg, _, self.cg, self.C = make_copies(dv, torch, gu, mm, nb, nc)
+        self.Ld, _, self.cd, Cd = make_copies(dv, torch, down, mm, nb, nc)
         self.C = min(self.C, Cd)
         x_bits = synth.activations_bf16(0, gu.outlier_tag or gu.name, M, gu.K)
         self.x = torch.from_numpy(x_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
@@ -187,11 +189,14 @@ class MlpRunner:
 
     def call(self, i):
         k = i % self.C
-        self.dv.mlp_decode(self.Lg, self.cg[k].data_ptr(), self.Ld, self.cd[k].data_ptr(), self.x.data_ptr(),
-                           self.y.data_ptr(), self.M, self.ws.data_ptr(), 0, self.stream)
+        self.fn(self.Lg, self.cg[k].data_ptr(), self.Ld, self.cd[k].data_ptr(), self.x.data_ptr(),
+                self.y.data_ptr(), self.M, self.ws.data_ptr(), 0, self.stream)
 
     def algo_bytes(self):
         return self.Lg.algo_bytes + self.Ld.algo_bytes
+
+    def flops(self):
+        return 2.0 * self.M * (self.gu.N * self.gu.K + self.down.N * self.down.K)
 
     def free(self):
         del self.cg, self.cd, self.ws
@@ -207,6 +212,12 @@ def prefill_table(dv, torch, layers, steps):
         table.append({"workload": f"{name} prefill M={m}", "us_per_call": round(t * 1e3, 2),
                       "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
         r.free()
+    r = MlpRunner(dv, torch, layers["spark_gateup"], layers["spark_down"], 2048, prefill=True)
+    t, _ = time_calls(torch, r.call, steps, 3)
+    tf = r.flops() / (t * 1e-3) / 1e12
+    table.append({"workload": "spark MLP block (gate+up, GELU, down) prefill M=2048", "us_per_call": round(t * 1e3, 2),
+                  "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
+    r.free()
     return table
 
 

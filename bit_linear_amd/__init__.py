@@ -26,7 +26,7 @@ DVSSQ_X_ROTATED = 1
 DECODE_MAX_M = 32
 
 EXPORTS = ("dvssq_pack_info", "dvssq_fwht", "dvssq_linear_decode", "dvssq_linear_prefill",
-           "dvssq_mlp_ws_bytes", "dvssq_mlp_decode", "dvssq_status_str")
+           "dvssq_mlp_ws_bytes", "dvssq_mlp_decode", "dvssq_mlp_prefill", "dvssq_status_str")
 
 
 class Layout(C.Structure):
@@ -69,9 +69,9 @@ for _n in ("dvssq_linear_decode", "dvssq_linear_prefill"):
     getattr(_lib, _n).argtypes = [C.POINTER(Layout), _P, _P, _P, C.c_int32, _P, C.c_uint32, _P]
 _lib.dvssq_mlp_ws_bytes.restype = C.c_int
 _lib.dvssq_mlp_ws_bytes.argtypes = [C.POINTER(Layout), C.POINTER(Layout), C.POINTER(C.c_int64)]
-_lib.dvssq_mlp_decode.restype = C.c_int
-_lib.dvssq_mlp_decode.argtypes = [C.POINTER(Layout), _P, C.POINTER(Layout), _P, _P, _P, C.c_int32, _P, C.c_uint32,
-                                  _P]
+for _n in ("dvssq_mlp_decode", "dvssq_mlp_prefill"):
+    getattr(_lib, _n).restype = C.c_int
+    getattr(_lib, _n).argtypes = [C.POINTER(Layout), _P, C.POINTER(Layout), _P, _P, _P, C.c_int32, _P, C.c_uint32, _P]
 _lib.dvssq_status_str.restype = C.c_char_p
 _lib.dvssq_status_str.argtypes = [C.c_int]
 
@@ -139,6 +139,12 @@ def mlp_decode(gu: Layout, gu_blob, down: Layout, down_blob, x, y, M: int, ws, f
                                  _ptr(ws), flags, _stream(stream)), "dvssq_mlp_decode")
 
 
+def mlp_prefill(gu: Layout, gu_blob, down: Layout, down_blob, x, y, M: int, ws, flags: int = 0,
+                stream=None) -> None:
+    _check(_lib.dvssq_mlp_prefill(C.byref(gu), _ptr(gu_blob), C.byref(down), _ptr(down_blob), _ptr(x), _ptr(y), M,
+                                  _ptr(ws), flags, _stream(stream)), "dvssq_mlp_prefill")
+
+
 def pack_blob(layout: Layout, parts: dict) -> np.ndarray:
     """Place given sub-arrays (idx, q4, s4, q8, s8, U, V) at the layout's offsets."""
     blob = np.zeros(layout.blob_bytes, dtype=np.uint8)
@@ -188,17 +194,20 @@ class Linear:
 
 
 class MLP:
-    """Gated MLP block (fused gate+up layer, then down) resident on a GPU; decode
-    form through dvssq_mlp_decode."""
+    """Gated MLP block (fused gate+up layer, then down) resident on a GPU:
+    dvssq_mlp_decode for M <= 32, dvssq_mlp_prefill above (or as `path` says)."""
 
     def __init__(self, gu: Linear, down: Linear):
         self.gu, self.down = gu, down
         self.ws = device_buffer(mlp_ws_bytes(gu.layout, down.layout), gu.device)
 
-    def forward(self, x, y=None, flags: int = 0, stream=None):
+    def forward(self, x, y=None, flags: int = 0, stream=None, path: str | None = None):
         import torch
         M = x.shape[0]
         if y is None:
             y = torch.empty((M, self.down.layout.N), dtype=torch.bfloat16, device=x.device)
-        mlp_decode(self.gu.layout, self.gu.blob, self.down.layout, self.down.blob, x, y, M, self.ws, flags, stream)
+        if path is None:
+            path = "decode" if M <= DECODE_MAX_M else "prefill"
+        fn = mlp_decode if path == "decode" else mlp_prefill
+        fn(self.gu.layout, self.gu.blob, self.down.layout, self.down.blob, x, y, M, self.ws, flags, stream)
         return y

@@ -292,13 +292,19 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
+// the prefill's own limits (32-bit offsets in the GEMM)
+static int prefill_supported(const dvssq_layout &L, int32_t M) {
+  if (L.K > (1 << 22) || M > (1 << 22) || static_cast<int64_t>(L.N) * L.r > (1 << 29)) return DVSSQ_EUNSUPPORTED;
+  return DVSSQ_OK;
+}
+
 int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M,
                          void *ws, uint32_t flags, void *stream) {
   int rc = check_call(L, blob, x, y, M, ws, L ? L->M_max : 0);
   if (rc != DVSSQ_OK) return rc;
   if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
   // the GEMM addresses one workgroup's weight rows, t and U with 32-bit byte offsets
-  if (L->K > (1 << 22) || M > (1 << 22) || static_cast<int64_t>(L->N) * L->r > (1 << 29)) return DVSSQ_EUNSUPPORTED;
+  if ((rc = prefill_supported(*L, M)) != DVSSQ_OK) return rc;
   const WsLayout W = ws_layout(*L);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   const Blob B{static_cast<const uint8_t *>(blob), L};
@@ -353,9 +359,10 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
-// ------------------------------------------------------------------ gated MLP block (decode)
+// ------------------------------------------------------------------ gated MLP block
 // workspace: [0, base) shared by the two projections (one after the other on
-// the stream), then the fused gate+up output and the intermediate h
+// the stream), then the fused gate+up output and the intermediate h, for up
+// to min(gu.M_max, down.M_max) rows
 struct MlpWs {
   int32_t M_cap;
   int64_t ygu, h, total;
@@ -363,7 +370,7 @@ struct MlpWs {
 
 static MlpWs mlp_ws(const dvssq_layout &gu, const dvssq_layout &down) {
   MlpWs w{};
-  w.M_cap = std::min(DVSSQ_DECODE_MAX_M, std::min(gu.M_max, down.M_max));
+  w.M_cap = std::min(gu.M_max, down.M_max);
   w.ygu = align256(std::max(gu.ws_bytes, down.ws_bytes));
   w.h = align256(w.ygu + 2 * static_cast<int64_t>(w.M_cap) * gu.N);
   w.total = align256(w.h + 2 * static_cast<int64_t>(w.M_cap) * down.K);
@@ -388,21 +395,31 @@ int dvssq_mlp_ws_bytes(const dvssq_layout *gu, const dvssq_layout *down, int64_t
   return DVSSQ_OK;
 }
 
-int dvssq_mlp_decode(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down, const void *down_blob,
-                     const void *x, void *y, int32_t M, void *ws, uint32_t flags, void *stream) {
-  int rc = check_mlp(gu, down);
+// argument checks shared by the decode and prefill forms of the block
+static int check_mlp_call(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down,
+                          const void *down_blob, const void *x, void *y, int32_t M, void *ws, uint32_t flags) {
+  const int rc = check_mlp(gu, down);
   if (rc != DVSSQ_OK) return rc;
   if (!gu_blob || !down_blob || !x || !y || !ws) return DVSSQ_EINVAL;
   if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
   if (M < 1 || M > gu->M_max || M > down->M_max) return DVSSQ_EINVAL;
-  if (M > DVSSQ_DECODE_MAX_M) return DVSSQ_EUNSUPPORTED;
-  if (!aligned(ws, 256) || !aligned(y, 16) || !aligned(x, 16)) return DVSSQ_EINVAL;
+  if (!aligned(ws, 256) || !aligned(y, 16) || !aligned(x, 16) || !aligned(gu_blob, 256) || !aligned(down_blob, 256))
+    return DVSSQ_EINVAL;
   const MlpWs W = mlp_ws(*gu, *down);
   const size_t yb = static_cast<size_t>(M) * down->N * 2, xb = static_cast<size_t>(M) * gu->K * 2;
   if (overlap(y, yb, ws, W.total) || overlap(x, xb, ws, W.total) || overlap(x, xb, y, yb) ||
       overlap(y, yb, gu_blob, gu->blob_bytes) || overlap(y, yb, down_blob, down->blob_bytes))
     return DVSSQ_EINVAL;
+  return DVSSQ_OK;
+}
+
+int dvssq_mlp_decode(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down, const void *down_blob,
+                     const void *x, void *y, int32_t M, void *ws, uint32_t flags, void *stream) {
+  int rc = check_mlp_call(gu, gu_blob, down, down_blob, x, y, M, ws, flags);
+  if (rc != DVSSQ_OK) return rc;
+  if (M > DVSSQ_DECODE_MAX_M) return DVSSQ_EUNSUPPORTED;
   if ((rc = decode_supported(*gu, M)) != DVSSQ_OK || (rc = decode_supported(*down, M)) != DVSSQ_OK) return rc;
+  const MlpWs W = mlp_ws(*gu, *down);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   void *ygu = wsb + W.ygu;
   void *h = wsb + W.h;
@@ -413,6 +430,22 @@ int dvssq_mlp_decode(const dvssq_layout *gu, const void *gu_blob, const dvssq_la
   GegluArgs g{static_cast<const uint16_t *>(ygu), static_cast<uint16_t *>(h), M, down->K};
   if (launch_geglu(g, static_cast<hipStream_t>(stream)) != hipSuccess) return DVSSQ_EHIP;
   return dvssq_linear_decode(down, down_blob, h, y, M, ws, 0, stream);
+}
+
+int dvssq_mlp_prefill(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down, const void *down_blob,
+                      const void *x, void *y, int32_t M, void *ws, uint32_t flags, void *stream) {
+  int rc = check_mlp_call(gu, gu_blob, down, down_blob, x, y, M, ws, flags);
+  if (rc != DVSSQ_OK) return rc;
+  if ((rc = prefill_supported(*gu, M)) != DVSSQ_OK || (rc = prefill_supported(*down, M)) != DVSSQ_OK) return rc;
+  const MlpWs W = mlp_ws(*gu, *down);
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  void *ygu = wsb + W.ygu;
+  void *h = wsb + W.h;
+  rc = dvssq_linear_prefill(gu, gu_blob, x, ygu, M, ws, flags, stream);
+  if (rc != DVSSQ_OK) return rc;
+  GegluArgs g{static_cast<const uint16_t *>(ygu), static_cast<uint16_t *>(h), M, down->K};
+  if (launch_geglu(g, static_cast<hipStream_t>(stream)) != hipSuccess) return DVSSQ_EHIP;
+  return dvssq_linear_prefill(down, down_blob, h, y, M, ws, 0, stream);
 }
 
 const char *dvssq_status_str(int status) {

@@ -137,8 +137,9 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
                          int32_t M, void *ws, uint32_t flags, void *stream);
 
 /*
- * Workspace size of dvssq_mlp_decode for the pair (gu, down), into *bytes.
- * Host-only.  DVSSQ_EINVAL if the pair does not form a gated MLP block (see
+ * Workspace size of dvssq_mlp_decode / dvssq_mlp_prefill for the pair (gu,
+ * down) and up to min(gu->M_max, down->M_max) rows, into *bytes.  Host-only.
+ * DVSSQ_EINVAL if the pair does not form a gated MLP block (see
  * dvssq_mlp_decode) or bytes is null.
  */
 int dvssq_mlp_ws_bytes(const dvssq_layout *gu, const dvssq_layout *down, int64_t *bytes);
@@ -153,7 +154,8 @@ int dvssq_mlp_ws_bytes(const dvssq_layout *gu, const dvssq_layout *down, int64_t
  * output columns 0 .. I-1; segment 1 = up, I .. 2I-1), down is a one-segment
  * layer.  Requires gu->n_seg == 2, down->n_seg == 1, gu->N == 2 down->K (= 2I),
  * down->N == gu->K (DVSSQ_EINVAL otherwise), 1 <= M <= min(gu->M_max,
- * down->M_max), M <= 32, and both layers accepted by dvssq_linear_decode.
+ * down->M_max), M <= 32, and both layers accepted by dvssq_linear_decode;
+ * gu_blob and down_blob 256-byte aligned.
  * GELU is the exact v Phi(v) = v (1 + erf(v / sqrt 2)) / 2 in fp32; the tensors
  * between the projections are bf16 as in a BF16 model: the fused layer's output
  * is bf16 (as from dvssq_linear_decode), gelu(gate) * up is rounded once to bf16
@@ -169,6 +171,16 @@ int dvssq_mlp_ws_bytes(const dvssq_layout *gu, const dvssq_layout *down, int64_t
 int dvssq_mlp_decode(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down,
                      const void *down_blob, const void *x, void *y, int32_t M, void *ws,
                      uint32_t flags, void *stream);
+
+/*
+ * Gated MLP block, prefill form: the same block and arguments as
+ * dvssq_mlp_decode, with both projections on the prefill path
+ * (dvssq_linear_prefill) and 1 <= M <= min(gu->M_max, down->M_max) (no limit
+ * of 32); the limits of dvssq_linear_prefill apply to both layers.
+ */
+int dvssq_mlp_prefill(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down,
+                      const void *down_blob, const void *x, void *y, int32_t M, void *ws,
+                      uint32_t flags, void *stream);
 
 /* Static text for a return code. */
 const char *dvssq_status_str(int status);

@@ -10,6 +10,13 @@ import oracle
 import synth
 
 TOL = 5e-3          # max|y_gpu - y_ref| / max|y_ref|
+# The gated MLP block applies two projections in sequence; each is held to TOL
+# of its own output scale.  The gate+up error reaches the down projection
+# through h = bf16(gelu(gate) up): a gate/up element's absolute error is scaled
+# by its partner factor, and a bf16 rounding of g, u or h that lands on the
+# other side of a tie moves that element by one bf16 unit (2^-8 relative).
+# The block is therefore held to twice the layer tolerance.
+TOL_BLOCK = 2 * TOL
 
 
 def all_layers():

@@ -201,3 +201,16 @@ def test_mlp_decode_error_paths():
     g2 = dv.pack_info(384, 192, 4, 64, 2, M_max=64)
     d2 = dv.pack_info(192, 192, 4, 64, 1, M_max=64)
     assert c(g=g2, d=d2) == dv.DVSSQ_EUNSUPPORTED
+
+
+def test_mlp_prefill_error_paths():
+    gu = dv.pack_info(512, 256, 4, 256, 2, M_max=64)
+    dn = dv.pack_info(256, 256, 4, 256, 1, M_max=64)
+    f, E = dv.lib().dvssq_mlp_prefill, dv.DVSSQ_EINVAL
+    GB, DB = 0x10000000, 0x18000000
+    assert f(C.byref(gu), None, C.byref(dn), DB, X, Y, 40, WS, 0, None) == E
+    assert f(C.byref(gu), GB, C.byref(dn), DB, X, Y, 65, WS, 0, None) == E      # above M_max
+    assert f(C.byref(gu), GB, C.byref(dn), DB, X, Y, 0, WS, 0, None) == E
+    assert f(C.byref(dn), GB, C.byref(gu), DB, X, Y, 40, WS, 0, None) == E      # swapped pair
+    assert f(C.byref(gu), GB + 64, C.byref(dn), DB, X, Y, 40, WS, 0, None) == E  # blob alignment
+    assert f(C.byref(gu), GB, C.byref(dn), DB, X, WS + 4096, 40, WS, 0, None) == E  # y inside ws

@@ -223,7 +223,26 @@ def test_mlp_decode_parity(gname, dname, M):
     ref = oracle.mlp_forward(gb, (g.N, g.K, g.r, g.block), db, (d.N, d.K, d.r, d.block), x_bits)
     err = cases.rel_err(cases.from_device_bf16(y), ref)
     print(f"{gname}+{dname} M={M} mlp rel_err={err:.3e}")
-    assert err <= cases.TOL
+    assert err <= cases.TOL_BLOCK
+
+
+MLP_PREFILL_CASES = [("mlp_tiny_gu", "mlp_tiny_dn", 40), ("mlp_tiny_gu", "mlp_tiny_dn", 130),
+                     ("spark_gateup", "spark_down", 48)]
+
+
+@pytest.mark.parametrize("gname,dname,M", MLP_PREFILL_CASES, ids=[f"{g}-M{m}" for g, _, m in MLP_PREFILL_CASES])
+def test_mlp_prefill_parity(gname, dname, M):
+    """The prefill form of the block (dvssq_mlp_prefill) against the chained oracle."""
+    g, gb, lg = gpu_layer(gname, 256)
+    d, db, ld = gpu_layer(dname, 256)
+    mlp = dv.MLP(lg, ld)
+    x_bits = cases.activations(gname, M)
+    y = mlp.forward(cases.to_device_bf16(x_bits, DEV), path="prefill")
+    torch.cuda.synchronize()
+    ref = oracle.mlp_forward(gb, (g.N, g.K, g.r, g.block), db, (d.N, d.K, d.r, d.block), x_bits)
+    err = cases.rel_err(cases.from_device_bf16(y), ref)
+    print(f"{gname}+{dname} M={M} mlp prefill rel_err={err:.3e}")
+    assert err <= cases.TOL_BLOCK
 
 
 def test_mlp_decode_matches_its_parts():
