@@ -274,3 +274,20 @@ def mlp_forward_cols(gu_blob: np.ndarray, gu: tuple, down_blob: np.ndarray, down
     h = mlp_intermediate(y_gu)
     Nd, Kd, rd, bd = down
     return forward_cols(down_blob, Nd, Kd, rd, bd, 1, h, cols, nthreads)
+
+
+# ------------------------------------------------------------------ dense materialization (test infrastructure)
+# The MiniCPM card's usage section offers to materialize the quantized MLP
+# weights into plain BF16 for generation.  Reading: the dense weight of the
+# layer in the original input domain, W = (W_hat + U V_seg) H^T (H symmetric,
+# so H^T = H), so that x W^T is the layer's forward; rows in original output
+# order, rounded once to bf16.
+
+def materialize(blob: np.ndarray, N, K, r, block, n_seg=1) -> np.ndarray:
+    """fp64 dense weight [N][K] (original output order, original input domain)."""
+    idx, What, U, V = unpack(blob, N, K, r, n_seg)
+    seg = idx // (N // n_seg)
+    Wr = What + np.einsum("pi,pik->pk", U, V.reshape(n_seg, r, K)[seg])
+    W = np.empty_like(Wr)
+    W[idx] = fwht_rows(Wr, block)
+    return W

@@ -495,3 +495,34 @@ def test_mlp_chain_columns_and_zero(mlp_case):
     np.testing.assert_array_equal(oracle.mlp_forward_cols(bg, a, bd, b, x, cols), y[:, cols])
     z = oracle.mlp_forward(bg, a, bd, b, np.zeros_like(x))
     assert np.all(z == 0.0)
+
+
+# ------------------------------------------------------------------ dense materialization
+
+def test_materialize_reproduces_forward(tiny_case):
+    """x W^T with the materialized weight equals the layer's forward (which
+    rotates x instead), and matches a dense route from the numpy decode and
+    scipy's Hadamard matrix."""
+    lay, W, blob, _ = tiny_case
+    Wm = oracle.materialize(blob, lay.N, lay.K, lay.r, lay.block)
+    x = synth.activations_bf16(2, "tiny", 5, lay.K)
+    y = oracle.forward(blob, lay.N, lay.K, lay.r, lay.block, 1, x)
+    yd = synth.bf16_bits_to_f64(x) @ Wm.T
+    assert np.abs(y - yd).max() <= 1e-12 * np.abs(y).max()
+    idx, What, U, V = _decode_blob_numpy(blob, lay.N, lay.K, lay.r, 1)
+    H = scipy.linalg.hadamard(lay.K) / np.sqrt(lay.K)
+    ref = np.zeros_like(Wm)
+    ref[idx] = (What + U @ V) @ H
+    assert np.abs(Wm - ref).max() <= 1e-12 * np.abs(ref).max()
+    # and it approximates the weight the layer was quantized from
+    Wt = synth.bf16_bits_to_f64(W)
+    assert np.linalg.norm(Wm - Wt) <= 0.1 * np.linalg.norm(Wt)     # INT4 grid of Gaussian rows: ~7 %
+
+
+def test_materialize_two_segments():
+    lay = synth.Layer("seg2m", N=2 * 128, K=128, block=64, r=3, n_seg=2, n_outlier=2, outlier_tag="seg2m")
+    blob = oracle.quantize(synth.weights_bf16(4, lay), lay.r, lay.block, n_seg=2, full_svd=True)
+    Wm = oracle.materialize(blob, lay.N, lay.K, lay.r, lay.block, 2)
+    x = synth.activations_bf16(4, "seg2m", 3, lay.K)
+    y = oracle.forward(blob, lay.N, lay.K, lay.r, lay.block, 2, x)
+    assert np.abs(y - synth.bf16_bits_to_f64(x) @ Wm.T).max() <= 1e-12 * np.abs(y).max()
