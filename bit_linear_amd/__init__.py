@@ -26,7 +26,8 @@ DVSSQ_X_ROTATED = 1
 DECODE_MAX_M = 32
 
 EXPORTS = ("dvssq_pack_info", "dvssq_fwht", "dvssq_linear_decode", "dvssq_linear_prefill",
-           "dvssq_mlp_ws_bytes", "dvssq_mlp_decode", "dvssq_mlp_prefill", "dvssq_status_str")
+           "dvssq_materialize", "dvssq_mlp_ws_bytes", "dvssq_mlp_decode", "dvssq_mlp_prefill",
+           "dvssq_status_str")
 
 
 class Layout(C.Structure):
@@ -67,6 +68,8 @@ _lib.dvssq_fwht.argtypes = [_P, _P, C.c_int32, C.c_int32, C.c_int32, _P]
 for _n in ("dvssq_linear_decode", "dvssq_linear_prefill"):
     getattr(_lib, _n).restype = C.c_int
     getattr(_lib, _n).argtypes = [C.POINTER(Layout), _P, _P, _P, C.c_int32, _P, C.c_uint32, _P]
+_lib.dvssq_materialize.restype = C.c_int
+_lib.dvssq_materialize.argtypes = [C.POINTER(Layout), _P, _P, _P]
 _lib.dvssq_mlp_ws_bytes.restype = C.c_int
 _lib.dvssq_mlp_ws_bytes.argtypes = [C.POINTER(Layout), C.POINTER(Layout), C.POINTER(C.c_int64)]
 for _n in ("dvssq_mlp_decode", "dvssq_mlp_prefill"):
@@ -125,6 +128,10 @@ def linear_decode(layout: Layout, blob, x, y, M: int, ws, flags: int = 0, stream
 def linear_prefill(layout: Layout, blob, x, y, M: int, ws, flags: int = 0, stream=None) -> None:
     _check(_lib.dvssq_linear_prefill(C.byref(layout), _ptr(blob), _ptr(x), _ptr(y), M, _ptr(ws),
                                      flags, _stream(stream)), "dvssq_linear_prefill")
+
+
+def materialize(layout: Layout, blob, w, stream=None) -> None:
+    _check(_lib.dvssq_materialize(C.byref(layout), _ptr(blob), _ptr(w), _stream(stream)), "dvssq_materialize")
 
 
 def mlp_ws_bytes(gu: Layout, down: Layout) -> int:

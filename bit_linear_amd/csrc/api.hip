@@ -359,6 +359,32 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
+// ------------------------------------------------------------------ dense materialization
+int dvssq_materialize(const dvssq_layout *L, const void *blob, void *w, void *stream) {
+  const int rc = check_layout(L);
+  if (rc != DVSSQ_OK) return rc;
+  if (!blob || !w) return DVSSQ_EINVAL;
+  if (!aligned(blob, 256) || !aligned(w, 16)) return DVSSQ_EINVAL;
+  if (overlap(w, static_cast<size_t>(L->N) * L->K * 2, blob, L->blob_bytes)) return DVSSQ_EINVAL;
+  const Blob B{static_cast<const uint8_t *>(blob), L};
+  DenseArgs a{};
+  a.q4 = B.q4();
+  a.s4 = B.s4();
+  a.q8 = B.q8();
+  a.s8 = B.s8();
+  a.U = B.U();
+  a.V = B.V();
+  a.idx = B.idx();
+  a.w = static_cast<uint16_t *>(w);
+  a.N = L->N;
+  a.K = L->K;
+  a.r = L->r;
+  a.n_seg = L->n_seg;
+  a.n4 = L->n_int4;
+  a.hscale = inv_sqrt_block(L->block);
+  return launch_materialize(a, L->block, static_cast<hipStream_t>(stream)) == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
+}
+
 // ------------------------------------------------------------------ gated MLP block
 // workspace: [0, base) shared by the two projections (one after the other on
 // the stream), then the fused gate+up output and the intermediate h, for up

@@ -125,6 +125,61 @@ __device__ __forceinline__ u32x4 int8_to_f16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// ------------------------------------------------------------------ register FWHT
+// Fast Walsh-Hadamard transform of one block of 64 VPL values held by a
+// wavefront, VPL consecutive values per lane (Sylvester order, unnormalized):
+// log2(VPL) butterfly stages in registers, then the six stages across lanes.
+// value of lane l ^ S (S = 1 .. 32): DPP quad permutes for 1 and 2, row shifts
+// for 4 and 8 (lanes with bit S clear read S lanes up, the others S lanes
+// down), and the permlane swaps of 16-lane rows / 32-lane halves for 16 and 32
+template <int S>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  const int x = __float_as_int(v);
+  if constexpr (S == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (S == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (S == 4 || S == 8) {
+    const int up = __builtin_amdgcn_update_dpp(0, x, 0x100 + S, 0xF, 0xF, false);
+    const int dn = __builtin_amdgcn_update_dpp(0, x, 0x110 + S, 0xF, 0xF, false);
+    return __int_as_float((lane & S) ? dn : up);
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+// one butterfly stage across lanes: lanes with bit S clear keep v + p, the
+// others p - v (p = the partner's value)
+template <int S, int VPL>
+__device__ __forceinline__ void lane_stage(float (&v)[VPL], int lane) {
+  const float sg = (lane & S) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) v[j] = fmaf(sg, v[j], xor_lane<S>(v[j], lane));
+}
+
+template <int VPL>
+__device__ __forceinline__ void fwht_wave(float (&v)[VPL], int lane) {
+#pragma unroll
+  for (int s = 1; s < VPL; s <<= 1)
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (!(j & s)) {
+        const float a = v[j], b = v[j + s];
+        v[j] = a + b;
+        v[j + s] = a - b;
+      }
+  lane_stage<1>(v, lane);
+  lane_stage<2>(v, lane);
+  lane_stage<4>(v, lane);
+  lane_stage<8>(v, lane);
+  lane_stage<16>(v, lane);
+  lane_stage<32>(v, lane);
+}
+
 // ------------------------------------------------------------------ prefill tiles
 // The prefill GEMM takes kPfTileM tokens by kPfTileN weight rows per workgroup
 // and one INT4 group (64 inputs) per step.  Its x_rot operand is stored as
@@ -272,7 +327,21 @@ struct GegluArgs {
   int M, I;             // I a multiple of 8
 };
 
+struct DenseArgs {
+  const uint8_t *q4;
+  const uint16_t *s4;
+  const int8_t *q8;
+  const float *s8;
+  const uint16_t *U;
+  const uint16_t *V;
+  const int32_t *idx;
+  uint16_t *w;      // bf16 [N][K], original output order
+  int N, K, r, n_seg, n4;
+  float hscale;     // 1/sqrt(block)
+};
+
 // launchers (return hipError_t of the launch)
+hipError_t launch_materialize(const DenseArgs &a, int block, hipStream_t s);
 hipError_t launch_geglu(const GegluArgs &a, hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);

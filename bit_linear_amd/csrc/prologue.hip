@@ -49,57 +49,6 @@ __device__ __forceinline__ void load_row(const uint16_t *src, float (&v)[VPL]) {
   }
 }
 
-// value of lane l ^ S (S = 1 .. 32): DPP quad permutes for 1 and 2, row shifts
-// for 4 and 8 (lanes with bit S clear read S lanes up, the others S lanes
-// down), and the permlane swaps of 16-lane rows / 32-lane halves for 16 and 32
-template <int S>
-__device__ __forceinline__ float xor_lane(float v, int lane) {
-  const int x = __float_as_int(v);
-  if constexpr (S == 1) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
-  } else if constexpr (S == 2) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
-  } else if constexpr (S == 4 || S == 8) {
-    const int up = __builtin_amdgcn_update_dpp(0, x, 0x100 + S, 0xF, 0xF, false);
-    const int dn = __builtin_amdgcn_update_dpp(0, x, 0x110 + S, 0xF, 0xF, false);
-    return __int_as_float((lane & S) ? dn : up);
-  } else if constexpr (S == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
-    return __uint_as_float((lane & 16) ? r[0] : r[1]);
-  } else {
-    const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
-    return __uint_as_float((lane & 32) ? r[0] : r[1]);
-  }
-}
-
-// one butterfly stage across lanes: lanes with bit S clear keep v + p, the
-// others p - v (p = the partner's value)
-template <int S, int VPL>
-__device__ __forceinline__ void lane_stage(float (&v)[VPL], int lane) {
-  const float sg = (lane & S) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) v[j] = fmaf(sg, v[j], xor_lane<S>(v[j], lane));
-}
-
-template <int VPL>
-__device__ __forceinline__ void fwht_wave(float (&v)[VPL], int lane) {
-#pragma unroll
-  for (int s = 1; s < VPL; s <<= 1)
-#pragma unroll
-    for (int j = 0; j < VPL; ++j)
-      if (!(j & s)) {
-        const float a = v[j], b = v[j + s];
-        v[j] = a + b;
-        v[j + s] = a - b;
-      }
-  lane_stage<1>(v, lane);
-  lane_stage<2>(v, lane);
-  lane_stage<4>(v, lane);
-  lane_stage<8>(v, lane);
-  lane_stage<16>(v, lane);
-  lane_stage<32>(v, lane);
-}
-
 template <int VPL, int MT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   constexpr int B = 64 * VPL;

@@ -137,6 +137,18 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
                          int32_t M, void *ws, uint32_t flags, void *stream);
 
 /*
+ * Dense materialization of a packed layer (MiniCPM5-2B-Hadamard-GSQ model card,
+ * usage section: the quantized MLP weights materialized as plain BF16):
+ *     w[idx[p]][k] = bf16( sum_j (W_hat[p] + U[p] V_seg(p))[j] H[j][k] ),
+ * the layer's weight in the original input domain (H symmetric, H^T = H), so
+ * that x w^T is the layer's forward up to the bf16 rounding of w.
+ * w: device bf16 [N][K] row-major, original output order, 16-byte aligned,
+ * disjoint from the blob; every row is written.  fp32 arithmetic, one bf16
+ * rounding (nearest-even).  One kernel launch on `stream`.
+ */
+int dvssq_materialize(const dvssq_layout *L, const void *blob, void *w, void *stream);
+
+/*
  * Workspace size of dvssq_mlp_decode / dvssq_mlp_prefill for the pair (gu,
  * down) and up to min(gu->M_max, down->M_max) rows, into *bytes.  Host-only.
  * DVSSQ_EINVAL if the pair does not form a gated MLP block (see

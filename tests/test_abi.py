@@ -214,3 +214,17 @@ def test_mlp_prefill_error_paths():
     assert f(C.byref(dn), GB, C.byref(gu), DB, X, Y, 40, WS, 0, None) == E      # swapped pair
     assert f(C.byref(gu), GB + 64, C.byref(dn), DB, X, Y, 40, WS, 0, None) == E  # blob alignment
     assert f(C.byref(gu), GB, C.byref(dn), DB, X, WS + 4096, 40, WS, 0, None) == E  # y inside ws
+
+
+def test_materialize_error_paths():
+    L = dv.pack_info(512, 256, 4, 256, 1, M_max=8)
+    f, E = dv.lib().dvssq_materialize, dv.DVSSQ_EINVAL
+    assert f(None, BLOB, Y, None) == E
+    assert f(C.byref(L), None, Y, None) == E
+    assert f(C.byref(L), BLOB, None, None) == E
+    assert f(C.byref(L), BLOB + 16, Y, None) == E        # blob not 256-aligned
+    assert f(C.byref(L), BLOB, Y + 2, None) == E         # w not 16-aligned
+    assert f(C.byref(L), BLOB, BLOB + 4096, None) == E   # w overlaps the blob
+    bad = dv.pack_info(512, 256, 4, 256, 1, M_max=8)
+    bad.off_U += 256
+    assert f(C.byref(bad), BLOB, Y, None) == E

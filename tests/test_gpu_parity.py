@@ -265,3 +265,39 @@ def test_mlp_decode_rejects_mismatched_pair():
     d, db, ld = gpu_layer("tiny", 32)
     with pytest.raises(dv.DvssqError):
         dv.MLP(lg, ld)
+
+
+# ------------------------------------------------------------------ dense materialization
+
+DENSE_CASES = ["tiny", "ragged_b64_r1", "b128_r64", "seg2_b512_r32", "b1024_tail", "b2048_ragged", "seg2_small",
+               "spark_up"]
+
+
+@pytest.mark.parametrize("name", DENSE_CASES)
+def test_materialize_parity(name):
+    """dvssq_materialize against the oracle's (W_hat + U V_seg) H, element by
+    element: one bf16 rounding of an fp32 value."""
+    lay, blob, lin = gpu_layer(name, 8)
+    w = torch.empty((lay.N, lay.K), dtype=torch.bfloat16, device=DEV)
+    dv.materialize(lin.layout, lin.blob, w)
+    torch.cuda.synchronize()
+    got = cases.from_device_bf16(w)
+    ref = oracle.materialize(blob, lay.N, lay.K, lay.r, lay.block, lay.n_seg)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max()
+    worst = float((np.abs(got - ref) / bound).max())
+    print(f"{name} materialize worst/bound={worst:.3f}")
+    assert worst <= 1.0
+
+
+def test_materialized_dense_gemm_matches_layer():
+    """x W^T on the materialized weights (a plain bf16 GEMM, fp32 accumulation)
+    reproduces the layer's forward."""
+    lay, blob, lin = gpu_layer("spark_up", 8)
+    w = torch.empty((lay.N, lay.K), dtype=torch.bfloat16, device=DEV)
+    dv.materialize(lin.layout, lin.blob, w)
+    x_bits = cases.activations("spark_up", 8)
+    x = cases.to_device_bf16(x_bits, DEV)
+    y = torch.matmul(x.float(), w.float().t())
+    torch.cuda.synchronize()
+    ref = oracle.forward(blob, lay.N, lay.K, lay.r, lay.block, 1, x_bits)
+    assert cases.rel_err(y.cpu().double().numpy(), ref) <= cases.TOL
