@@ -202,6 +202,31 @@ class MlpRunner:
         del self.cg, self.cd, self.ws
 
 
+def dense_table(dv, torch, layers, steps):
+    """Materialization of the fused gate+up layer into dense bf16, and a plain
+    bf16 GEMM (torch's library GEMM) on that dense weight at M = 2048, beside
+    this library's prefill of the packed layer."""
+    import torch.nn.functional as F
+    lay = layers["spark_gateup"]
+    r = Runner(dv, torch, lay, 2048, 2048, min_bytes=256 << 20, max_copies=16)
+    w = torch.empty((lay.N, lay.K), dtype=torch.bfloat16, device="cuda")
+
+    def mat(i):
+        dv.materialize(r.L, r.ptrs[i % r.C], w, r.stream)
+    t, _ = time_calls(torch, mat, steps, 3)
+    out = [{"workload": f"spark_gateup materialize to dense bf16 (N={lay.N}, K={lay.K})",
+            "us_per_call": round(t * 1e3, 2), "gbs_written": round(2.0 * lay.N * lay.K / (t * 1e-3) / 1e9, 1)}]
+    y = torch.empty((2048, lay.N), dtype=torch.bfloat16, device="cuda")
+    t, _ = time_calls(torch, lambda i: torch.matmul(r.x, w.t(), out=y), steps, 3)
+    tf = 2.0 * 2048 * lay.N * lay.K / (t * 1e-3) / 1e12
+    out.append({"workload": "dense bf16 GEMM (torch.matmul) on the materialized spark_gateup, M=2048",
+                "us_per_call": round(t * 1e3, 2), "tflops": round(tf, 1),
+                "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
+    del w, y
+    r.free()
+    return out
+
+
 def prefill_table(dv, torch, layers, steps):
     table = []
     for name, m in (("spark_gateup", 512), ("spark_gateup", 2048), ("minicpm_gate", 4096),
@@ -212,6 +237,7 @@ def prefill_table(dv, torch, layers, steps):
         table.append({"workload": f"{name} prefill M={m}", "us_per_call": round(t * 1e3, 2),
                       "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
         r.free()
+    table += dense_table(dv, torch, layers, steps)
     r = MlpRunner(dv, torch, layers["spark_gateup"], layers["spark_down"], 2048, prefill=True)
     t, _ = time_calls(torch, r.call, steps, 3)
     tf = r.flops() / (t * 1e-3) / 1e12
