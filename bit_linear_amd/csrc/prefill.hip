@@ -22,6 +22,7 @@ constexpr int MF = kPfTileM / 32;        // 32-token fragments of a wavefront
 constexpr int NF = kPfTileN / 4 / 32;    // 32-row weight fragments of a wavefront
 constexpr int kTileA = kPfTileM * BK;    // f16 per x_rot tile
 // s_waitcnt immediates: vmcnt(n), the other counters free
+constexpr int kVmcnt0 = 0x0F70;
 constexpr int kVmcnt4 = 0x0F74;
 constexpr int kVmcnt8 = 0x0F78;
 // padded LDS row of the staged t (bf16): NS slabs of 16 plus 8, so that the
@@ -215,6 +216,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0,
   int g = 0;
   for (; g + 6 <= KG; g += 6) six(g, 6);
   if (g < KG) six(g, KG - g);
+  // the last steps' repeated copies into LDS are never read: let them land
+  // before the workgroup can end
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
   // ---- epilogue: row scale 2^e, INT8 row scale, low-rank slab, bf16 scatter through idx
   // weight-side loads first, all in one batch
