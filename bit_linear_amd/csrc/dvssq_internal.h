@@ -200,6 +200,7 @@ inline int64_t pf_rows(int M) { return (static_cast<int64_t>(M) + kPfTileM - 1) 
 // Byte offsets inside the caller's workspace.  Decode and prefill regions
 // overlap (one call at a time per workspace).
 constexpr int kMaxSplit = 16;   // largest decode split-K factor
+constexpr int kTSplitMax = 16;  // largest number of K-ranges of the prefill's t product
 
 struct WsLayout {
   // decode
@@ -217,7 +218,7 @@ struct WsLayout {
   int64_t p_xr;    // f16 x_rot tiles of [M_max rounded up to 128][K], scaled by 2^-e per row
   int64_t p_sc;    // fp32 [M_max] 2^e per row
   int64_t p_t;     // fp32 [M_max][nsr_pad] t = x_rot V^T
-  int64_t p_tpart; // fp32 [K / block][M_max][nsr_pad] partial t of each Hadamard block
+  int64_t p_tpart; // fp32 [kTSplitMax][M_max][nsr_pad] partial t of each K-range
   int64_t p_end;
   int64_t total;
 };
@@ -248,7 +249,7 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
   w.p_xr = cur;   cur = align256(cur + 2 * pf_rows(L.M_max) * K);
   w.p_sc = cur;   cur = align256(cur + 4 * static_cast<int64_t>(L.M_max));
   w.p_t = cur;    cur = align256(cur + 4 * static_cast<int64_t>(L.M_max) * nsp);
-  w.p_tpart = cur; cur = align256(cur + 4 * (K / L.block) * static_cast<int64_t>(L.M_max) * nsp);
+  w.p_tpart = cur; cur = align256(cur + 4 * kTSplitMax * static_cast<int64_t>(L.M_max) * nsp);
   w.p_end = cur;
   w.total = w.d_end > w.p_end ? w.d_end : w.p_end;
   return w;
@@ -261,7 +262,7 @@ struct PrologueArgs {
   float *sc;           // fp32 [M] 2^e per row (f16 output) or null
   const uint16_t *V;   // bf16 [nsr][K] or null (no t)
   float *t;            // fp32 [M][nsr_pad] or null
-  float *tpart;        // K-split: fp32 [gridDim.y][M][nsr_pad] partial t of each Hadamard block
+  float *tpart;        // prefill: fp32 [ranges][M][nsr_pad] partial t of each K-range
   int M, K, nsr, nsr_pad;
   int blocks_per_wg;   // Hadamard blocks handled (and t-accumulated) by one workgroup
   int rotate;          // 0: x is already rotated (copy + t only)
@@ -343,7 +344,7 @@ struct DenseArgs {
 // launchers (return hipError_t of the launch)
 hipError_t launch_materialize(const DenseArgs &a, int block, hipStream_t s);
 hipError_t launch_geglu(const GegluArgs &a, hipStream_t s);
-hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hipStream_t s);
+hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, int cus, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 size_t decode_lds_bytes(int M, int unit, int KW, int nsr_pad);
 int decode_max_spans();   // most 128-input spans one decode workgroup takes

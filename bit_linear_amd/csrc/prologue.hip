@@ -8,15 +8,14 @@
 //
 // One workgroup = 4 wavefronts handles MT activation rows and a run of
 // Hadamard blocks.  Each row of a block is rotated by one wavefront with the
-// fast Walsh-Hadamard transform: VPL = block/64 consecutive values per lane,
-// log2(VPL) butterfly stages in registers, then the stages across lanes (xor
-// 1..32).  The fp32 block is staged in LDS and copied out either as bf16 in
-// natural order (dvssq_fwht), or -- for the prefill GEMM -- as f16 scaled by
-// a power of two per row and stored in runs of 8 in the order 0,2,4,6,1,3,5,7
-// (the order the weight decoder produces).  The row's exponent comes from the
-// bound max|x H| <= sqrt(block) max|x|, so the scaled values stay below 2^15.
-// t is accumulated on the matrix cores (32x32x16 bf16 MFMA) over the
-// workgroup's blocks.
+// register FWHT.  The block is staged in LDS and copied out either as bf16 in
+// natural order (dvssq_fwht), or -- for the prefill GEMM -- as f16 scaled by a
+// power of two per row, in the GEMM's tile layout, runs of 8 in the order
+// 0,2,4,6,1,3,5,7 (the order the weight decoder produces).  The row's exponent
+// comes from the bound max|x H| <= sqrt(block) max|x| (rowscale_kernel), so the
+// scaled values stay below 2^15.  For the prefill, t = x_rot V^T is then
+// computed from those f16 tiles on the matrix cores (tgemm_kernel), its K-ranges
+// summed in order by treduce_kernel.
 #include "dvssq_internal.h"
 
 namespace dvssq {
@@ -65,8 +64,6 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   const int b0 = blockIdx.y * a.blocks_per_wg;
   const int b1 = min(nblk, b0 + a.blocks_per_wg);
   const int mrows = min(MT, a.M - m0);
-  const bool want_t = a.nsr > 0;
-  const int n_it = (a.nsr_pad + 31) / 32;
 
   // 0. per-row power-of-two scale (f16 output only), written by rowscale_kernel
   if (a.out_f16) {
@@ -74,37 +71,11 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
     __syncthreads();
   }
 
-  f32x16 acc[2];
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[it][e] = 0.0f;
-
-  // t pairs of this wavefront per block: K-steps s = wave, wave + 4, ... (of
-  // 16 inputs) times the n_it column tiles of 32; V is loaded in batches of
-  // kVB pairs, the first batch of a block before its rows are rotated
-  constexpr int SN = B / 64;
-  constexpr int kVB = 8;
-  const int npair = want_t ? SN * n_it : 0;
-  const int arow = lane & 31, half = lane >> 5;
-  u32x4 vb[kVB];
-  auto vload = [&](int kb, int p0) {
-#pragma unroll
-    for (int j = 0; j < kVB; ++j) {
-      const int pr = min(p0 + j, max(npair - 1, 0));
-      const int st = wave + 4 * (pr >> (n_it - 1)), it = pr & (n_it - 1);
-      const int i = 32 * it + arow;
-      vb[j] = (want_t && i < a.nsr)
-                  ? *reinterpret_cast<const u32x4 *>(a.V + static_cast<int64_t>(i) * a.K + kb + 16 * st + 8 * half)
-                  : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
   // rows of this wavefront rotated together: their loads are issued at once
   constexpr int RB = VPL <= 4 ? 8 : VPL <= 8 ? 4 : VPL <= 16 ? 2 : 1;
 
   for (int blk = b0; blk < b1; ++blk) {
     const int kb = blk * B;
-    if (npair > 0) vload(kb, 0);
     // 1. rotate each row of this block (one wavefront per row), stage fp32 in LDS
     for (int ml0 = wave; ml0 < MT; ml0 += 4 * RB) {
       float v[RB][VPL];
@@ -190,75 +161,71 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
         *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) = o;
       }
     }
-    // 3. t += x_rot(block) V(block)^T on the matrix cores; K-steps of 16 split over the waves
-    for (int p0 = 0; p0 < npair; p0 += kVB) {
-      if (p0 > 0) vload(kb, p0);
-#pragma unroll
-      for (int j = 0; j < kVB; ++j) {
-        if (p0 + j >= npair) break;
-        const int pr = p0 + j;
-        const int st = wave + 4 * (pr >> (n_it - 1)), it = pr & (n_it - 1);
-        u32x4 av = {0u, 0u, 0u, 0u};
-        if (arow < MT) {
-          if constexpr (H16) {
-            // staged f16 run in the order 0,2,4,6,1,3,5,7, scaled by 2^-e: back
-            // to x_rot, as natural-order bf16 pairs
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(lds) + arow * LDH +
-                                                             16 * st + 8 * half);
-            const float sc = ldexpf(1.0f, rowexp[arow]);
-            auto f = [](uint32_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h))); };
-            av[0] = pack_bf16x2(f(w[0] & 0xFFFFu) * sc, f(w[2] & 0xFFFFu) * sc);
-            av[1] = pack_bf16x2(f(w[0] >> 16) * sc, f(w[2] >> 16) * sc);
-            av[2] = pack_bf16x2(f(w[1] & 0xFFFFu) * sc, f(w[3] & 0xFFFFu) * sc);
-            av[3] = pack_bf16x2(f(w[1] >> 16) * sc, f(w[3] >> 16) * sc);
-          } else {
-            const float *w = lds + arow * LDR + 16 * st + 8 * half;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) av[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
-          }
-        }
-        if (it == 0) acc[0] = mfma32x32x16(av, vb[j], acc[0]);
-        else acc[1] = mfma32x32x16(av, vb[j], acc[1]);
-      }
-    }
     __syncthreads();
-  }
-  if (!want_t) return;
-  // 4. reduce the four waves' partial t and write it out
-  float *red = lds;  // [4 waves][2 it][32 m][32 i]
-  {
-    const int col = lane & 31, half = lane >> 5;
-    for (int it = 0; it < n_it; ++it)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = 8 * (v / 4) + 4 * half + (v % 4);
-        red[((wave * 2 + it) * 32 + m) * 32 + col] = acc[it][v];
-      }
-  }
-  __syncthreads();
-  if (gridDim.y == 1) {
-    for (int e = tid; e < mrows * a.nsr_pad; e += kThreads) {
-      const int ml = e / a.nsr_pad, i = e % a.nsr_pad;
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) s += red[((w * 2 + i / 32) * 32 + ml) * 32 + (i % 32)];
-      a.t[static_cast<int64_t>(m0 + ml) * a.nsr_pad + i] = s;
-    }
-    return;
-  }
-  // K split over the workgroup columns: this column's partial, summed in
-  // column order by treduce_kernel
-  for (int e = tid; e < mrows * a.nsr_pad; e += kThreads) {
-    const int ml = e / a.nsr_pad, i = e % a.nsr_pad;
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) s += red[((w * 2 + i / 32) * 32 + ml) * 32 + (i % 32)];
-    a.tpart[(static_cast<int64_t>(blockIdx.y) * a.M + m0 + ml) * a.nsr_pad + i] = s;
   }
 }
 
-// t = sum over the workgroup columns (Hadamard blocks) of their partial t, in
-// column order; four consecutive t values per thread.
+// t = x_rot V^T for the prefill from the GEMM's f16 x_rot tiles: one workgroup
+// per 128-row tile and K-range (grid y splits K), wavefront w on rows
+// 32 w .. 32 w + 31, 32x32x16 f16 MFMAs against V converted to f16 in the
+// tiles' input order (step s, chunk 2 ks + h: inputs 64 s + 32 h + 8 ks + 0,2,4,6,1,3,5,7);
+// each row's partial is scaled back by its 2^e.  One K-range writes t directly,
+// several write partials that treduce_kernel sums in range order.
+template <int NI>   // column tiles of 32 in t (nsr_pad / 32)
+__global__ __launch_bounds__(kThreads) void tgemm_kernel(PrologueArgs a, int spw) {
+  const int lane = threadIdx.x & 63, fr = lane & 31, fh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int KG = a.K / kGroup;
+  const int mt = blockIdx.x, s0 = blockIdx.y * spw, s1 = min(KG, s0 + spw);
+  const uint16_t *tile0 = a.xr + static_cast<int64_t>(mt) * KG * (kPfTileM * kGroup) + (2 * 0 + fh) * 1024 +
+                          (32 * wave + fr) * 8;
+  const auto rv = make_rsrc(a.V, static_cast<uint32_t>(a.nsr) * a.K * 2);
+  f32x16 acc[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[ni][e] = 0.0f;
+  auto f16of = [](uint32_t bf) { return static_cast<_Float16>(__uint_as_float(bf << 16)); };
+  for (int s = s0; s < s1; ++s) {
+    u32x4 af[4], vb[4][NI];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      af[ks] = *reinterpret_cast<const u32x4 *>(tile0 + static_cast<int64_t>(s) * (kPfTileM * kGroup) + ks * 2048);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int i = 32 * ni + fr;
+        const uint32_t off = i < a.nsr ? (static_cast<uint32_t>(i) * a.K + 64 * s + 32 * fh + 8 * ks) * 2 : kOutOfRange;
+        vb[ks][ni] = buf_load16(rv, off);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        // natural-order bf16 pairs (k0,k1) .. (k6,k7) -> f16 in the order 0,2,4,6,1,3,5,7
+        const u32x4 w = vb[ks][ni];
+        f16x8 h;
+        h[0] = f16of(w[0] & 0xFFFFu); h[1] = f16of(w[1] & 0xFFFFu);
+        h[2] = f16of(w[2] & 0xFFFFu); h[3] = f16of(w[3] & 0xFFFFu);
+        h[4] = f16of(w[0] >> 16);     h[5] = f16of(w[1] >> 16);
+        h[6] = f16of(w[2] >> 16);     h[7] = f16of(w[3] >> 16);
+        acc[ni] = mfma32x32x16_f16(af[ks], __builtin_bit_cast(u32x4, h), acc[ni]);
+      }
+  }
+  // lane (fr, fh), acc[ni][v]: row 32 w + 8 (v / 4) + 4 fh + v % 4, column 32 ni + fr
+  float *dst = gridDim.y == 1 ? a.t : a.tpart + static_cast<int64_t>(blockIdx.y) * a.M * a.nsr_pad;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = mt * kPfTileM + 32 * wave + 8 * (v / 4) + 4 * fh + (v % 4);
+    if (m >= a.M) continue;
+    const float sc = a.sc[m];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) dst[static_cast<int64_t>(m) * a.nsr_pad + 32 * ni + fr] = acc[ni][v] * sc;
+  }
+}
+
+// t = sum over the K-ranges of their partial t, in range order; four
+// consecutive t values per thread.
 __global__ __launch_bounds__(kThreads) void treduce_kernel(PrologueArgs a, int ncol) {
   const int64_t n4 = static_cast<int64_t>(a.M) * a.nsr_pad / 4;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -302,9 +269,7 @@ __global__ __launch_bounds__(kThreads) void rowscale_kernel(PrologueArgs a) {
 template <int VPL, int MT>
 hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
   constexpr int B = 64 * VPL;
-  const size_t lds_rows = VPL >= 8 ? static_cast<size_t>(MT) * (B + 8) * 2 : static_cast<size_t>(MT) * (B + 4) * 4;
-  const size_t lds_red = 4 * 2 * 32 * 32 * 4;
-  const size_t lds = lds_rows > lds_red ? lds_rows : lds_red;
+  const size_t lds = VPL >= 8 ? static_cast<size_t>(MT) * (B + 8) * 2 : static_cast<size_t>(MT) * (B + 4) * 4;
   if (lds > 65536) {
     static bool attr_set = false;
     if (!attr_set) {
@@ -321,7 +286,7 @@ hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hipStream_t s) {
+hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, int cus, hipStream_t s) {
   if (a.out_f16) {
     const hipError_t e = launch_kernel(reinterpret_cast<const void *>(rowscale_kernel),
                                        dim3((a.M + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, s, a);
@@ -337,10 +302,24 @@ hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, hi
     case 2048: e = launch_vpl<32, 16>(a, n_wg_blocks, s); break;
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || a.nsr == 0 || n_wg_blocks == 1) return e;
+  if (e != hipSuccess || !a.out_f16 || a.nsr == 0) return e;
+  // t from the f16 tiles: K split so that the grid has about two workgroups
+  // per compute unit, at most kTSplitMax ranges
+  const int KG = a.K / kGroup, mtiles = (a.M + kPfTileM - 1) / kPfTileM;
+  const int want = std::max(1, std::min(kTSplitMax, (2 * cus + mtiles - 1) / mtiles));
+  const int spw = (KG + want - 1) / want;
+  const int nsplit = (KG + spw - 1) / spw;
+  {
+    int spw_arg = spw;
+    void *args[] = {const_cast<PrologueArgs *>(&a), &spw_arg};
+    const void *fn = a.nsr_pad > 32 ? reinterpret_cast<const void *>(tgemm_kernel<2>)
+                                    : reinterpret_cast<const void *>(tgemm_kernel<1>);
+    e = hipLaunchKernel(fn, dim3(mtiles, nsplit), dim3(kThreads), args, 0, s);
+    if (e != hipSuccess || nsplit == 1) return e;
+  }
   const int64_t n4 = static_cast<int64_t>(a.M) * a.nsr_pad / 4;
-  const int ncol = n_wg_blocks;
-  void *args[] = {const_cast<PrologueArgs *>(&a), const_cast<int *>(&ncol)};
+  int ncol = nsplit;
+  void *args[] = {const_cast<PrologueArgs *>(&a), &ncol};
   return hipLaunchKernel(reinterpret_cast<const void *>(treduce_kernel), dim3((n4 + kThreads - 1) / kThreads),
                          dim3(kThreads), args, 0, s);
 }
