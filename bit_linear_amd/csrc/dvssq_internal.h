@@ -125,6 +125,82 @@ __device__ __forceinline__ u32x4 int8_to_f16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// ------------------------------------------------------------------ Hadamard blocks on the matrix cores
+typedef int16_t s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16_bf16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                   0, 0);
+}
+
+// bf16 entry (a, b) of the 16x16 block-diagonal matrix with Sylvester blocks H_R
+__device__ __forceinline__ uint32_t sylvester_bf16(int a, int b, int R) {
+  if ((a / R) != (b / R)) return 0u;
+  return (__popc(a & b & (R - 1)) & 1) ? 0xBF80u : 0x3F80u;
+}
+
+// bf16 entries (4q + j, n), j < 4, of H_16 (Sylvester, +-1) as two packed
+// pairs.  The sign is the parity of (4q + j) & n = parity(q & (n >> 2)) xor
+// parity(j & (n & 3)); the second term, as a 4-bit mask over j, is 0x0, 0xA,
+// 0xC, 0x6 for n & 3 = 0 .. 3.
+__device__ __forceinline__ u32x2 sylvester_h16(int n, int q) {
+  uint32_t t = (0x6CA0u >> (4 * (n & 3))) & 0xFu;
+  t ^= (__popc(q & (n >> 2)) & 1) ? 0xFu : 0u;
+  u32x2 h;
+  h[0] = 0x3F803F80u | ((t & 1u) << 15) | ((t & 2u) << 30);
+  h[1] = 0x3F803F80u | ((t & 4u) << 13) | ((t & 8u) << 28);
+  return h;
+}
+
+// Rotation of C blocks of 256 inputs (or one block of b < 256 inputs, C = 1)
+// of one row by one wavefront: lane (n, q) = (lane % 16, lane / 16) holds, for
+// every 256-block c, the inputs 256 c + 16 n + 4 q + j, j < 4 (xw: bf16 pairs),
+// and gets x H at the same positions, scaled by hscale = 1/sqrt(block).  A
+// Sylvester block of 256 is H_16 (x) H_16, so a block viewed as a 16x16 matrix X
+// becomes Hs X H_16 (Hs = H_16, or I (x) H_{b/16} for b < 256): one bf16 MFMA for
+// X H_16 (exact products, fp32 sums) and two for the second factor on that fp32
+// result split into bf16 high and low parts; blocks of 512 .. 2048 combine
+// their 256-blocks with butterflies in registers.
+template <int C>
+__device__ __forceinline__ void rotate_blocks(const u32x2 (&xw)[C], float (&y)[C][4], int block, float hscale) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const u32x2 h1 = sylvester_h16(n, q);
+  u32x2 h2 = h1;
+  if (block < 256) {
+    const int Rb = block / 16;
+    h2[0] = sylvester_bf16(4 * q, n, Rb) | (sylvester_bf16(4 * q + 1, n, Rb) << 16);
+    h2[1] = sylvester_bf16(4 * q + 2, n, Rb) | (sylvester_bf16(4 * q + 3, n, Rb) << 16);
+  }
+  const f32x4 zf = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const f32x4 F = mfma16_bf16(xw[c], h1, zf);  // X H_16, lane: rows 4q+j, column n
+    u32x2 hi, lo;
+    hi[0] = pack_bf16x2(F[0], F[1]);
+    hi[1] = pack_bf16x2(F[2], F[3]);
+    lo[0] = pack_bf16x2(F[0] - __uint_as_float(hi[0] << 16), F[1] - __uint_as_float(hi[0] & 0xFFFF0000u));
+    lo[1] = pack_bf16x2(F[2] - __uint_as_float(hi[1] << 16), F[3] - __uint_as_float(hi[1] & 0xFFFF0000u));
+    f32x4 D = mfma16_bf16(hi, h2, zf);             // (Hs X H_16)^T, high part ...
+    D = mfma16_bf16(lo, h2, D);                    // ... plus low part
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[c][j] = D[j];
+  }
+#pragma unroll
+  for (int sft = 1; sft < C; sft <<= 1)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      if (!(c & sft))
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = y[c][j], p1 = y[c + sft][j];
+          y[c][j] = p0 + p1;
+          y[c + sft][j] = p0 - p1;
+        }
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[c][j] *= hscale;
+}
+
 // ------------------------------------------------------------------ register FWHT
 // Fast Walsh-Hadamard transform of one block of 64 VPL values held by a
 // wavefront, VPL consecutive values per lane (Sylvester order, unnormalized):

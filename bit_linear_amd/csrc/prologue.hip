@@ -78,6 +78,62 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
     const int kb = blk * B;
     // 1. rotate each row of this block (one wavefront per row), stage fp32 in LDS
     for (int ml0 = wave; ml0 < MT; ml0 += 4 * RB) {
+      if constexpr (B >= 256) {
+        if (a.out_f16) {
+          // prefill: the rotation on the matrix cores (rotate_blocks), each lane
+          // holding inputs 256 c + 16 n + 4 q + j of the row's block
+          constexpr int C = B / 256;
+          const int n = lane & 15, q = lane >> 4;
+          u32x2 xw[RB][C];
+#pragma unroll
+          for (int j = 0; j < RB; ++j) {
+            const int ml = min(ml0 + 4 * j, mrows - 1);
+            const uint16_t *src = a.x + static_cast<int64_t>(m0 + ml) * a.K + kb + 16 * n + 4 * q;
+#pragma unroll
+            for (int c = 0; c < C; ++c) xw[j][c] = *reinterpret_cast<const u32x2 *>(src + 256 * c);
+          }
+#pragma unroll
+          for (int j = 0; j < RB; ++j) {
+            const int ml = ml0 + 4 * j;
+            if (ml < MT) {
+              float y[C][4];
+              if (a.rotate) {
+                rotate_blocks<C>(xw[j], y, B, a.hscale);
+              } else {
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                  y[c][0] = __uint_as_float(xw[j][c][0] << 16);
+                  y[c][1] = __uint_as_float(xw[j][c][0] & 0xFFFF0000u);
+                  y[c][2] = __uint_as_float(xw[j][c][1] << 16);
+                  y[c][3] = __uint_as_float(xw[j][c][1] & 0xFFFF0000u);
+                }
+              }
+              const bool live = ml < mrows;
+              if constexpr (H16) {
+                // f16 x 2^-e; inputs 4 h + j (h = q % 2) of run r fill slots
+                // (j even) h, ... and (j odd) 4 + h, ... of the order 0,2,4,6,1,3,5,7
+                uint16_t *row = reinterpret_cast<uint16_t *>(lds) + ml * LDH;
+                const float d = ldexpf(1.0f, -rowexp[ml]);
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                  const int r = 32 * c + 2 * n + (q >> 1), h = q & 1;
+                  *reinterpret_cast<uint32_t *>(row + 8 * r + 2 * h) = live ? pack_f16x2(y[c][0] * d, y[c][2] * d) : 0u;
+                  *reinterpret_cast<uint32_t *>(row + 8 * r + 4 + 2 * h) = live ? pack_f16x2(y[c][1] * d, y[c][3] * d) : 0u;
+                }
+              } else {
+                float *row = lds + ml * LDR;
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                  const f32x4 o = {live ? y[c][0] : 0.0f, live ? y[c][1] : 0.0f, live ? y[c][2] : 0.0f,
+                                   live ? y[c][3] : 0.0f};
+                  *reinterpret_cast<f32x4 *>(row + 256 * c + 16 * n + 4 * q) = o;
+                }
+              }
+            }
+          }
+          continue;
+        }
+      }
       float v[RB][VPL];
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
