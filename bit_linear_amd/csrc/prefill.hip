@@ -164,6 +164,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0,
     for (int i = 0; i < MF; ++i) af[0][i] = *reinterpret_cast<const u32x4 *>(as + i * 256);
 #pragma unroll
     for (int j = 0; j < NF; ++j) bf[0][j] = dequant(j, 0);
+    // let the scheduler interleave the operand reads with the matrix-core
+    // instructions (it helps most where one wavefront runs per SIMD)
+    __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c = ks & 1;
