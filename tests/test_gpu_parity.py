@@ -245,6 +245,25 @@ def test_mlp_prefill_parity(gname, dname, M):
     assert err <= cases.TOL_BLOCK
 
 
+def test_mlp_prefill_full_size_sampled():
+    """The Spark block at M=2048 tokens (the shape and launch the benchmark times),
+    checked on sampled tokens: each token's output depends on its own row of x
+    only, so the chained oracle runs on those rows.  The rows cover the first and
+    last 128-token tiles, a tile boundary and the middle."""
+    M = 2048
+    g, gb, lg = gpu_layer("spark_gateup", M)
+    d, db, ld = gpu_layer("spark_down", M)
+    mlp = dv.MLP(lg, ld)
+    x_bits = cases.activations("spark_gateup", M)
+    y = cases.from_device_bf16(mlp.forward(cases.to_device_bf16(x_bits, DEV), path="prefill"))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 1000, 1919, 2047])
+    ref = oracle.mlp_forward(gb, (g.N, g.K, g.r, g.block), db, (d.N, d.K, d.r, d.block), x_bits[rows])
+    err = cases.rel_err(y[rows], ref)
+    print(f"spark MLP block M={M} prefill sampled({rows.size} tokens) rel_err={err:.3e}")
+    assert err <= cases.TOL_BLOCK
+
+
 def test_mlp_decode_matches_its_parts():
     """The block equals its three steps run separately: the fused decode, the
     GELU product on the host (fp32, one bf16 rounding) and the down decode."""
