@@ -227,8 +227,27 @@ def dense_table(dv, torch, layers, steps):
     return out
 
 
+def fwht_table(dv, torch, steps):
+    """dvssq_fwht alone (bf16 in, bf16 out) on the prefill activation shapes:
+    HBM-bound, 2MK bytes read + 2MK written per call."""
+    import synth
+    out = []
+    src = torch.from_numpy(synth.activations_bf16(0, "fwht", 4096, 6144).view(np.int16)).cuda().view(torch.bfloat16)
+    for M, K, b in ((2048, 2560, 256), (4096, 2048, 2048), (4096, 6144, 2048)):
+        x = src[:M, :K].contiguous()
+        xr = torch.empty_like(x)
+        st = torch.cuda.current_stream().cuda_stream
+        t, _ = time_calls(torch, lambda i: dv.fwht(x, xr, M, K, b, st), steps, 3)
+        g = 4.0 * M * K / (t * 1e-3) / 1e9
+        out.append({"workload": f"fwht M={M} K={K} H_{b}", "us_per_call": round(t * 1e3, 2), "gbs": round(g, 1),
+                    "frac_hbm": round(g / HBM_PEAK_GBS, 4)})
+        del x, xr
+    del src
+    return out
+
+
 def prefill_table(dv, torch, layers, steps):
-    table = []
+    table = fwht_table(dv, torch, steps)
     for name, m in (("spark_gateup", 512), ("spark_gateup", 2048), ("minicpm_gate", 4096),
                     ("minicpm_down", 4096)):
         r = Runner(dv, torch, layers[name], m, m, min_bytes=256 << 20, max_copies=16)
