@@ -181,9 +181,8 @@ int dvssq_fwht(const void *x, void *xrot, int32_t M, int32_t K, int32_t block, v
   a.K = K;
   a.blocks_per_wg = 1;
   a.rotate = 1;
-  a.out_f16 = 0;
   a.hscale = inv_sqrt_block(block);
-  const hipError_t e = launch_prologue(a, block, K / block, 256, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_fwht(a, block, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
@@ -326,7 +325,6 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   p.tpart = reinterpret_cast<float *>(wsb + W.p_tpart);
   p.blocks_per_wg = 1;
   p.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
-  p.out_f16 = 1;
   p.hscale = inv_sqrt_block(L->block);
   p.exp_bias = (p.rotate ? (__builtin_ctz(static_cast<unsigned>(L->block)) + 1) / 2 : 0) + 1 - 15;
   hipError_t e = launch_prologue(p, L->block, L->K / L->block, compute_units(), s);

@@ -334,17 +334,16 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
 // ------------------------------------------------------------------ kernel arguments
 struct PrologueArgs {
   const uint16_t *x;   // bf16 [M][K]
-  uint16_t *xr;        // bf16 [M][K] natural order, or f16 scaled prefill tiles (xr_tile_offset)
-  float *sc;           // fp32 [M] 2^e per row (f16 output) or null
+  uint16_t *xr;        // dvssq_fwht: bf16 [M][K]; prefill: f16 x_rot 2^-e in the GEMM tiles (xr_tile_offset)
+  float *sc;           // prefill: fp32 [M] 2^e per row
   const uint16_t *V;   // bf16 [nsr][K] or null (no t)
   float *t;            // fp32 [M][nsr_pad] or null
   float *tpart;        // prefill: fp32 [ranges][M][nsr_pad] partial t of each K-range
   int M, K, nsr, nsr_pad;
-  int blocks_per_wg;   // Hadamard blocks handled (and t-accumulated) by one workgroup
+  int blocks_per_wg;   // prefill: Hadamard blocks rotated by one workgroup
   int rotate;          // 0: x is already rotated (copy + t only)
-  int out_f16;         // 1: f16 scaled permuted output and sc; 0: bf16 natural
   float hscale;        // 1/sqrt(block)
-  int exp_bias;        // f16 output: row exponent = ilogb(max |x|) + exp_bias (log2 sqrt(block) if rotating, + 1 - 15)
+  int exp_bias;        // prefill: row exponent = ilogb(max |x|) + exp_bias (log2 sqrt(block) if rotating, + 1 - 15)
 };
 
 struct DecodeArgs {
@@ -420,6 +419,7 @@ struct DenseArgs {
 // launchers (return hipError_t of the launch)
 hipError_t launch_materialize(const DenseArgs &a, int block, hipStream_t s);
 hipError_t launch_geglu(const GegluArgs &a, hipStream_t s);
+hipError_t launch_fwht(const PrologueArgs &a, int block, hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, int cus, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 size_t decode_lds_bytes(int M, int unit, int KW, int nsr_pad);

@@ -6,12 +6,15 @@
 // equation (block-diagonal H_K).  t: MiniCPM card, Mathematical Foundations 2,
 // runtime equation (the X B^T factor).
 //
-// One workgroup = 4 wavefronts handles MT activation rows and a run of
-// Hadamard blocks.  Each row of a block is rotated by one wavefront with the
-// register FWHT.  The block is staged in LDS and copied out either as bf16 in
-// natural order (dvssq_fwht), or -- for the prefill GEMM -- as f16 scaled by a
-// power of two per row, in the GEMM's tile layout, runs of 8 in the order
-// 0,2,4,6,1,3,5,7 (the order the weight decoder produces).  The row's exponent
+// dvssq_fwht (fwht_kernel): one wavefront per (row, block), the register FWHT,
+// bf16 stored in natural order straight from registers.
+//
+// Prefill (prologue_kernel): one workgroup = 4 wavefronts handles MT activation
+// rows and a run of Hadamard blocks, each row of a block rotated by one
+// wavefront (on the matrix cores for blocks of 256 and more, else with the
+// register FWHT), staged in LDS and copied out as f16 scaled by a power of two
+// per row, in the GEMM's tile layout, runs of 8 in the order 0,2,4,6,1,3,5,7
+// (the order the weight decoder produces).  The row's exponent
 // comes from the bound max|x H| <= sqrt(block) max|x| (rowscale_kernel), so the
 // scaled values stay below 2^15.  For the prefill, t = x_rot V^T is then
 // computed from those f16 tiles on the matrix cores (tgemm_kernel), its K-ranges
@@ -48,12 +51,72 @@ __device__ __forceinline__ void load_row(const uint16_t *src, float (&v)[VPL]) {
   }
 }
 
+template <int VPL>
+__device__ __forceinline__ void store_row(uint16_t *dst, const float (&v)[VPL]) {
+  if constexpr (VPL >= 8) {
+#pragma unroll
+    for (int q = 0; q < VPL / 8; ++q) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[8 * q + 2 * e], v[8 * q + 2 * e + 1]);
+      *reinterpret_cast<u32x4 *>(dst + 8 * q) = w;
+    }
+  } else if constexpr (VPL == 4) {
+    u32x2 w;
+    w[0] = pack_bf16x2(v[0], v[1]);
+    w[1] = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2 *>(dst) = w;
+  } else if constexpr (VPL == 2) {
+    *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(v[0], v[1]);
+  } else {
+    dst[0] = f32_to_bf16(v[0]);
+  }
+}
+
+// rows of one block that a wavefront rotates together: their loads are issued at once
+template <int VPL>
+constexpr int kRowBatch = VPL <= 4 ? 8 : VPL <= 8 ? 4 : VPL <= 16 ? 2 : 1;
+
+// dvssq_fwht: [M][K] is M·K/B consecutive blocks of B values; wavefront w takes
+// blocks w·RB .. w·RB + RB - 1, loads them all, then rotates and stores each
+// (in place allowed: a wavefront reads its blocks before it writes them, and
+// no other wavefront touches them).
+template <int VPL>
+__global__ __launch_bounds__(kThreads) void fwht_kernel(PrologueArgs a) {
+  constexpr int B = 64 * VPL, RB = kRowBatch<VPL>;
+  const int lane = threadIdx.x & 63;
+  const int64_t nitem = static_cast<int64_t>(a.M) * (a.K / B);
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6)) * RB;
+  if (i0 >= nitem) return;
+  float v[RB][VPL];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) load_row<VPL>(a.x + min(i0 + j, nitem - 1) * B + lane * VPL, v[j]);
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    if (i0 + j < nitem) {
+      fwht_wave<VPL>(v[j], lane);
+#pragma unroll
+      for (int q = 0; q < VPL; ++q) v[j][q] *= a.hscale;
+      store_row<VPL>(a.xr + (i0 + j) * B + lane * VPL, v[j]);
+    }
+  }
+}
+
+template <int VPL>
+hipError_t launch_fwht_vpl(const PrologueArgs &a, hipStream_t s) {
+  constexpr int B = 64 * VPL;
+  const int64_t waves = (static_cast<int64_t>(a.M) * (a.K / B) + kRowBatch<VPL> - 1) / kRowBatch<VPL>;
+  const int64_t wgs = (waves + kThreads / 64 - 1) / (kThreads / 64);
+  return launch_kernel(reinterpret_cast<const void *>(fwht_kernel<VPL>), dim3(static_cast<unsigned>(wgs)),
+                       dim3(kThreads), 0, s, a);
+}
+
 template <int VPL, int MT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   constexpr int B = 64 * VPL;
   constexpr int LDR = B + 4;  // padded LDS row (fp32)
   // blocks of 512 and more stage 16-bit values (the output format: f16 scaled
-  // and permuted, or bf16), so that two workgroups fit in LDS
+  // and permuted), so that two workgroups fit in LDS
   constexpr bool H16 = VPL >= 8;
   constexpr int LDH = B + 8;  // padded LDS row (16-bit)
   extern __shared__ __align__(16) float lds[];
@@ -65,111 +128,84 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   const int b1 = min(nblk, b0 + a.blocks_per_wg);
   const int mrows = min(MT, a.M - m0);
 
-  // 0. per-row power-of-two scale (f16 output only), written by rowscale_kernel
-  if (a.out_f16) {
-    for (int ml = tid; ml < MT; ml += kThreads) rowexp[ml] = ml < mrows ? ilogbf(a.sc[m0 + ml]) : 0;
-    __syncthreads();
-  }
+  // 0. per-row power-of-two scale, written by rowscale_kernel
+  for (int ml = tid; ml < MT; ml += kThreads) rowexp[ml] = ml < mrows ? ilogbf(a.sc[m0 + ml]) : 0;
+  __syncthreads();
 
-  // rows of this wavefront rotated together: their loads are issued at once
-  constexpr int RB = VPL <= 4 ? 8 : VPL <= 8 ? 4 : VPL <= 16 ? 2 : 1;
+  constexpr int RB = kRowBatch<VPL>;
 
   for (int blk = b0; blk < b1; ++blk) {
     const int kb = blk * B;
-    // 1. rotate each row of this block (one wavefront per row), stage fp32 in LDS
+    // 1. rotate each row of this block (one wavefront per row) and stage it in LDS
     for (int ml0 = wave; ml0 < MT; ml0 += 4 * RB) {
       if constexpr (B >= 256) {
-        if (a.out_f16) {
-          // prefill: the rotation on the matrix cores (rotate_blocks), each lane
-          // holding inputs 256 c + 16 n + 4 q + j of the row's block
-          constexpr int C = B / 256;
-          const int n = lane & 15, q = lane >> 4;
-          u32x2 xw[RB][C];
+        // on the matrix cores (rotate_blocks): lane (n, q) holds inputs
+        // 256 c + 16 n + 4 q + j of the row's block
+        constexpr int C = B / 256;
+        const int n = lane & 15, q = lane >> 4;
+        u32x2 xw[RB][C];
 #pragma unroll
-          for (int j = 0; j < RB; ++j) {
-            const int ml = min(ml0 + 4 * j, mrows - 1);
-            const uint16_t *src = a.x + static_cast<int64_t>(m0 + ml) * a.K + kb + 16 * n + 4 * q;
+        for (int j = 0; j < RB; ++j) {
+          const int ml = min(ml0 + 4 * j, mrows - 1);
+          const uint16_t *src = a.x + static_cast<int64_t>(m0 + ml) * a.K + kb + 16 * n + 4 * q;
 #pragma unroll
-            for (int c = 0; c < C; ++c) xw[j][c] = *reinterpret_cast<const u32x2 *>(src + 256 * c);
-          }
+          for (int c = 0; c < C; ++c) xw[j][c] = *reinterpret_cast<const u32x2 *>(src + 256 * c);
+        }
 #pragma unroll
-          for (int j = 0; j < RB; ++j) {
-            const int ml = ml0 + 4 * j;
-            if (ml < MT) {
-              float y[C][4];
-              if (a.rotate) {
-                rotate_blocks<C>(xw[j], y, B, a.hscale);
-              } else {
+        for (int j = 0; j < RB; ++j) {
+          const int ml = ml0 + 4 * j;
+          if (ml >= MT) continue;
+          float y[C][4];
+          if (a.rotate) {
+            rotate_blocks<C>(xw[j], y, B, a.hscale);
+          } else {
 #pragma unroll
-                for (int c = 0; c < C; ++c) {
-                  y[c][0] = __uint_as_float(xw[j][c][0] << 16);
-                  y[c][1] = __uint_as_float(xw[j][c][0] & 0xFFFF0000u);
-                  y[c][2] = __uint_as_float(xw[j][c][1] << 16);
-                  y[c][3] = __uint_as_float(xw[j][c][1] & 0xFFFF0000u);
-                }
-              }
-              const bool live = ml < mrows;
-              if constexpr (H16) {
-                // f16 x 2^-e; inputs 4 h + j (h = q % 2) of run r fill slots
-                // (j even) h, ... and (j odd) 4 + h, ... of the order 0,2,4,6,1,3,5,7
-                uint16_t *row = reinterpret_cast<uint16_t *>(lds) + ml * LDH;
-                const float d = ldexpf(1.0f, -rowexp[ml]);
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                  const int r = 32 * c + 2 * n + (q >> 1), h = q & 1;
-                  *reinterpret_cast<uint32_t *>(row + 8 * r + 2 * h) = live ? pack_f16x2(y[c][0] * d, y[c][2] * d) : 0u;
-                  *reinterpret_cast<uint32_t *>(row + 8 * r + 4 + 2 * h) = live ? pack_f16x2(y[c][1] * d, y[c][3] * d) : 0u;
-                }
-              } else {
-                float *row = lds + ml * LDR;
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                  const f32x4 o = {live ? y[c][0] : 0.0f, live ? y[c][1] : 0.0f, live ? y[c][2] : 0.0f,
-                                   live ? y[c][3] : 0.0f};
-                  *reinterpret_cast<f32x4 *>(row + 256 * c + 16 * n + 4 * q) = o;
-                }
-              }
+            for (int c = 0; c < C; ++c) {
+              y[c][0] = __uint_as_float(xw[j][c][0] << 16);
+              y[c][1] = __uint_as_float(xw[j][c][0] & 0xFFFF0000u);
+              y[c][2] = __uint_as_float(xw[j][c][1] << 16);
+              y[c][3] = __uint_as_float(xw[j][c][1] & 0xFFFF0000u);
             }
           }
-          continue;
-        }
-      }
-      float v[RB][VPL];
+          const bool live = ml < mrows;
+          if constexpr (H16) {
+            // f16 x 2^-e; inputs 4 h + j (h = q % 2) of run r fill slots
+            // (j even) h, ... and (j odd) 4 + h, ... of the order 0,2,4,6,1,3,5,7
+            uint16_t *row = reinterpret_cast<uint16_t *>(lds) + ml * LDH;
+            const float d = ldexpf(1.0f, -rowexp[ml]);
 #pragma unroll
-      for (int j = 0; j < RB; ++j) {
-        const int ml = min(ml0 + 4 * j, mrows - 1);
-        load_row<VPL>(a.x + static_cast<int64_t>(m0 + ml) * a.K + kb + lane * VPL, v[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < RB; ++j) {
-        const int ml = ml0 + 4 * j;
-        if (ml >= MT) break;
-        if (ml < mrows && a.rotate) {
-          fwht_wave<VPL>(v[j], lane);
-#pragma unroll
-          for (int q = 0; q < VPL; ++q) v[j][q] *= a.hscale;
-        }
-        if constexpr (H16) {
-          uint16_t *row = reinterpret_cast<uint16_t *>(lds) + ml * LDH + lane * VPL;
-          const float d = a.out_f16 ? ldexpf(1.0f, -rowexp[ml]) : 1.0f;
-#pragma unroll
-          for (int r = 0; r < VPL / 8; ++r) {
-            const float *w = v[j] + 8 * r;
-            u32x4 o = {0u, 0u, 0u, 0u};
-            if (ml < mrows) {
-              if (a.out_f16) {
-                o[0] = pack_f16x2(w[0] * d, w[2] * d);
-                o[1] = pack_f16x2(w[4] * d, w[6] * d);
-                o[2] = pack_f16x2(w[1] * d, w[3] * d);
-                o[3] = pack_f16x2(w[5] * d, w[7] * d);
-              } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
-              }
+            for (int c = 0; c < C; ++c) {
+              const int r = 32 * c + 2 * n + (q >> 1), h = q & 1;
+              *reinterpret_cast<uint32_t *>(row + 8 * r + 2 * h) = live ? pack_f16x2(y[c][0] * d, y[c][2] * d) : 0u;
+              *reinterpret_cast<uint32_t *>(row + 8 * r + 4 + 2 * h) = live ? pack_f16x2(y[c][1] * d, y[c][3] * d) : 0u;
             }
-            *reinterpret_cast<u32x4 *>(row + 8 * r) = o;
+          } else {
+            float *row = lds + ml * LDR;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+              const f32x4 o = {live ? y[c][0] : 0.0f, live ? y[c][1] : 0.0f, live ? y[c][2] : 0.0f,
+                               live ? y[c][3] : 0.0f};
+              *reinterpret_cast<f32x4 *>(row + 256 * c + 16 * n + 4 * q) = o;
+            }
           }
-        } else {
+        }
+      } else {
+        // blocks of 64 and 128: the register FWHT, fp32 in LDS
+        float v[RB][VPL];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          const int ml = min(ml0 + 4 * j, mrows - 1);
+          load_row<VPL>(a.x + static_cast<int64_t>(m0 + ml) * a.K + kb + lane * VPL, v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          const int ml = ml0 + 4 * j;
+          if (ml >= MT) continue;
+          if (ml < mrows && a.rotate) {
+            fwht_wave<VPL>(v[j], lane);
+#pragma unroll
+            for (int q = 0; q < VPL; ++q) v[j][q] *= a.hscale;
+          }
           float *row = lds + ml * LDR + lane * VPL;
 #pragma unroll
           for (int q = 0; q < VPL; ++q) row[q] = ml < mrows ? v[j][q] : 0.0f;
@@ -177,25 +213,17 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
       }
     }
     __syncthreads();
-    // 2. copy out in runs of 8: f16 into the GEMM's tiles (consecutive threads
-    // take consecutive rows of one run), bf16 row-major
+    // 2. copy out in runs of 8 into the GEMM's tiles (consecutive threads take
+    // consecutive rows of one run): f16 as staged, or fp32 scaled by 2^-e and permuted
     constexpr int RUNS = B / 8;
     if constexpr (H16) {
       const uint16_t *h = reinterpret_cast<const uint16_t *>(lds);
-      if (a.out_f16) {
-        for (int e = tid; e < mrows * RUNS; e += kThreads) {
-          const int run = e / mrows, ml = e - run * mrows;
-          *reinterpret_cast<u32x4 *>(a.xr + xr_tile_offset(m0 + ml, kb + run * 8, a.K)) =
-              *reinterpret_cast<const u32x4 *>(h + ml * LDH + run * 8);
-        }
-      } else {
-        for (int e = tid; e < mrows * RUNS; e += kThreads) {
-          const int ml = e / RUNS, run = e % RUNS;
-          *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) =
-              *reinterpret_cast<const u32x4 *>(h + ml * LDH + run * 8);
-        }
+      for (int e = tid; e < mrows * RUNS; e += kThreads) {
+        const int run = e / mrows, ml = e - run * mrows;
+        *reinterpret_cast<u32x4 *>(a.xr + xr_tile_offset(m0 + ml, kb + run * 8, a.K)) =
+            *reinterpret_cast<const u32x4 *>(h + ml * LDH + run * 8);
       }
-    } else if (a.out_f16) {
+    } else {
       for (int e = tid; e < mrows * RUNS; e += kThreads) {
         const int run = e / mrows, ml = e - run * mrows;
         const float *w = lds + ml * LDR + run * 8;
@@ -206,15 +234,6 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
         o[2] = pack_f16x2(w[1] * d, w[3] * d);
         o[3] = pack_f16x2(w[5] * d, w[7] * d);
         *reinterpret_cast<u32x4 *>(a.xr + xr_tile_offset(m0 + ml, kb + run * 8, a.K)) = o;
-      }
-    } else {
-      for (int e = tid; e < mrows * RUNS; e += kThreads) {
-        const int ml = e / RUNS, run = e % RUNS;
-        const float *w = lds + ml * LDR + run * 8;
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
-        *reinterpret_cast<u32x4 *>(a.xr + static_cast<int64_t>(m0 + ml) * a.K + kb + run * 8) = o;
       }
     }
     __syncthreads();
@@ -342,13 +361,22 @@ hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, int cus, hipStream_t s) {
-  if (a.out_f16) {
-    const hipError_t e = launch_kernel(reinterpret_cast<const void *>(rowscale_kernel),
-                                       dim3((a.M + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, s, a);
-    if (e != hipSuccess) return e;
+hipError_t launch_fwht(const PrologueArgs &a, int block, hipStream_t s) {
+  switch (block) {
+    case 64: return launch_fwht_vpl<1>(a, s);
+    case 128: return launch_fwht_vpl<2>(a, s);
+    case 256: return launch_fwht_vpl<4>(a, s);
+    case 512: return launch_fwht_vpl<8>(a, s);
+    case 1024: return launch_fwht_vpl<16>(a, s);
+    case 2048: return launch_fwht_vpl<32>(a, s);
+    default: return hipErrorInvalidValue;
   }
-  hipError_t e;
+}
+
+hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, int cus, hipStream_t s) {
+  hipError_t e = launch_kernel(reinterpret_cast<const void *>(rowscale_kernel),
+                               dim3((a.M + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, s, a);
+  if (e != hipSuccess) return e;
   switch (block) {
     case 64: e = launch_vpl<1, 32>(a, n_wg_blocks, s); break;
     case 128: e = launch_vpl<2, 32>(a, n_wg_blocks, s); break;
@@ -358,7 +386,7 @@ hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, in
     case 2048: e = launch_vpl<32, 16>(a, n_wg_blocks, s); break;
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || !a.out_f16 || a.nsr == 0) return e;
+  if (e != hipSuccess || a.nsr == 0) return e;
   // t from the f16 tiles: K split so that the grid has about two workgroups
   // per compute unit, at most kTSplitMax ranges
   const int KG = a.K / kGroup, mtiles = (a.M + kPfTileM - 1) / kPfTileM;
