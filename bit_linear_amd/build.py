@@ -16,6 +16,8 @@ FLAGS = [
     # no packed-FP32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # host symbols hidden: only the C ABI of include/dvssq.h is exported
+    "-Xarch_host", "-fvisibility=hidden",
 ]
 
 

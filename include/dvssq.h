@@ -57,6 +57,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbols; the entry points below are its
+   only exports. */
+#pragma GCC visibility push(default)
+
 #define DVSSQ_OK 0
 #define DVSSQ_EINVAL (-1)       /* null pointer, bad shape, misalignment, M out of range */
 #define DVSSQ_EUNSUPPORTED (-2) /* a valid request with no kernel (e.g. block not a power of two in [64, 2048]) */
@@ -114,10 +118,12 @@ int dvssq_fwht(const void *x, void *xrot, int32_t M, int32_t K, int32_t block, v
  * [M][N] in original column order; y must not overlap x, blob or ws.
  * ws: device workspace of L->ws_bytes, 256-byte aligned, contents need no
  * initialization; one ws must not be used by two calls in flight at once.
- * The rotated activations are held in f16 with a power-of-two scale per row
- * and per max(block, 256) inputs (no overflow for finite fp32 values), the
- * weights as exact f16 values; accumulation is fp32.  Decode needs the INT4
- * scales s4 to lie in [2^-14, 63] for exact f16 weights.
+ * Each (row, max(block, 256) inputs) of the rotated activations is held as a
+ * 15-bit integer with a power-of-two scale and multiplied exactly against the
+ * integer codes (int32 products, fp32 group sums); where that kernel's plan does
+ * not fit (per-wavefront load count, LDS, 32-bit offsets) a second kernel holds
+ * it in f16 with the same scales against exact f16 weights, which needs the
+ * INT4 scales s4 to lie in [2^-14, 63].  No overflow for finite fp32 values.
  * x and y must be 16-byte aligned.  Accumulation is fp32; y is rounded once to
  * bf16 (nearest-even).
  */
@@ -125,8 +131,9 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
                         int32_t M, void *ws, uint32_t flags, void *stream);
 
 /*
- * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: three kernel launches
- * (per-row scales, rotation + t, then the GEMM).  Needs K <= 2^22,
+ * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: four or five kernel
+ * launches (per-row scales, rotation, t and, when t is split over K-ranges, their
+ * ordered sum, then the GEMM).  Needs K <= 2^22,
  * M <= 2^22 and N r <= 2^29 (DVSSQ_EUNSUPPORTED otherwise).  Same arguments and ownership rules as
  * dvssq_linear_decode.  The rotated activations are held in f16 with one
  * power-of-two scale per row, the weights as exact f16 values (same s4 range
@@ -196,6 +203,8 @@ int dvssq_mlp_prefill(const dvssq_layout *gu, const void *gu_blob, const dvssq_l
 
 /* Static text for a return code. */
 const char *dvssq_status_str(int status);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,19 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_library_exports_nothing_else():
+    """Internal host symbols are hidden: the text symbols of the dynamic symbol
+    table are exactly the declared entry points."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", dv.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    text = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] in "TW"}
+    assert text == set(declared_functions())
+
+
 def test_layout_struct_size_matches_header():
     # 10 int32 + 10 int64 fields, no padding
     assert C.sizeof(dv.Layout) == 10 * 4 + 10 * 8
