@@ -2,7 +2,10 @@
 // launch (MiniCPM5-2B-Hadamard-GSQ model card, Mathematical Foundations 2,
 // runtime equation; rotation: same card, Mathematical Foundations 1 and
 // Spark-X2.5-4B-Hadamard-GSQ model card, Tier B equation; tiers: MiniCPM card
-// INT4 equation and Spark card Tier A).
+// INT4 equation and Spark card Tier A).  It serves the calls for which the
+// small-M kernel (decode_small.hip) finds no plan: per-wavefront load counts,
+// LDS for the activation planes (e.g. blocks of 2048 at M = 32) or 32-bit
+// offsets out of its range.
 //
 // Roles inside the launch (workgroups of four wavefronts):
 //  * producer workgroups (the lowest block indices, one per "unit" of

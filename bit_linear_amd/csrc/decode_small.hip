@@ -1,12 +1,14 @@
-// Small-M decode path (1 <= M <= 4) of y = (x H) W_hat^T + ((x H) V^T) U^T in
+// Small-M decode path (1 <= M <= 32) of y = (x H) W_hat^T + ((x H) V^T) U^T in
 // one kernel launch (MiniCPM5-2B-Hadamard-GSQ model card, Mathematical
 // Foundations 2, runtime equation; rotation: same card, Mathematical
 // Foundations 1, and Spark-X2.5-4B-Hadamard-GSQ model card, Tier B equation;
 // tiers: MiniCPM card INT4 equation and Spark card Tier A).
 //
 // t producers (the lowest block indices, one per rotation unit of max(block,
-// 256) inputs) rotate their unit of x and store the partial t = x_rot V^T with
-// device-scope stores, then publish a 64-bit generation flag.
+// 256) inputs and 16 rows) rotate their unit of x and store the partial
+// t = x_rot V^T with device-scope stores, then publish a 64-bit generation
+// flag.  For M > 4 they also publish the quantized planes below, which the
+// consumers then copy instead of rotating every (row, unit) themselves.
 //
 // Consumers are 16-wavefront workgroups (about one per compute unit): RT tiles
 // of 16 packed rows, each served by KQ wavefronts that split the K-range, plus
