@@ -249,7 +249,7 @@ def fwht_table(dv, torch, steps):
 def prefill_table(dv, torch, layers, steps):
     table = fwht_table(dv, torch, steps)
     for name, m in (("spark_gateup", 512), ("spark_gateup", 2048), ("minicpm_gate", 4096),
-                    ("minicpm_down", 4096)):
+                    ("minicpm_down", 4096), ("spark_down", 512)):
         r = Runner(dv, torch, layers[name], m, m, min_bytes=256 << 20, max_copies=16)
         t, _ = time_calls(torch, r.prefill, steps, 3)
         tf = r.flops() / (t * 1e-3) / 1e12

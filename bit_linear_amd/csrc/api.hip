@@ -353,6 +353,8 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   f.n4_tiles = (L->n_int4 + kPfTileN - 1) / kPfTileN;
   f.n8_tiles = (L->n_int8 + kPfTileN - 1) / kPfTileN;
   f.m_tiles = (M + kPfTileM - 1) / kPfTileM;
+  f.ksplit = pf_ksplit(f.m_tiles * (f.n4_tiles + f.n8_tiles), L->K / kGroup, &f.kspw);
+  f.part = reinterpret_cast<float *>(wsb + W.p_part);
   e = launch_prefill(f, s);
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }

@@ -295,6 +295,7 @@ struct WsLayout {
   int64_t p_sc;    // fp32 [M_max] 2^e per row
   int64_t p_t;     // fp32 [M_max][nsr_pad] t = x_rot V^T
   int64_t p_tpart; // fp32 [kTSplitMax][M_max][nsr_pad] partial t of each K-range
+  int64_t p_part;  // fp32 [ksplit][M][N] partial sums of a split GEMM (pf_part_bytes)
   int64_t p_end;
   int64_t total;
 };
@@ -304,6 +305,42 @@ inline int nsr_pad_of(int n_seg, int r) { return (n_seg * r + 31) / 32 * 32; }
 inline int decode_unit(int block) { return block > 256 ? block : 256; }
 inline int decode_groups(int n) { return (n + 15) / 16; }   // 16 packed rows per consumer group
 inline int decode_producers(int nunit, int M) { return nunit * ((M + 7) / 8); }
+
+// Prefill K split: a GEMM of fewer tiles than kPfSplitTiles (half the compute
+// units of an MI355X) runs each tile as up to kPfSplitMax workgroups over
+// K-ranges of at least kPfSplitMinSteps steps, aiming at one workgroup per
+// compute unit (from one per compute unit on, a split no longer paid for its
+// partial sums: measured).  Returns the number of ranges (1: no split); *spw =
+// steps per range.
+constexpr int kPfSplitTiles = 128, kPfSplitMax = 4, kPfSplitMinSteps = 2;
+inline int pf_ksplit(int tiles, int KG, int *spw) {
+  int want = 1;
+  if (tiles < kPfSplitTiles) {
+    want = (2 * kPfSplitTiles) / tiles;
+    want = want < kPfSplitMax ? want : kPfSplitMax;
+    const int most = KG / kPfSplitMinSteps;
+    want = want < most ? want : most;
+    want = want > 1 ? want : 1;
+  }
+  const int w = (KG + want - 1) / want;
+  if (spw) *spw = w;
+  return (KG + w - 1) / w;
+}
+
+// fp32 partial sums of a split prefill GEMM, largest over 1 <= M <= M_max
+inline int64_t pf_part_bytes(const dvssq_layout &L) {
+  const int nt = (L.n_int4 + kPfTileN - 1) / kPfTileN + (L.n_int8 + kPfTileN - 1) / kPfTileN;
+  const int mt_max = (L.M_max + kPfTileM - 1) / kPfTileM;
+  int64_t best = 0;
+  for (int mt = 1; mt <= mt_max && mt * nt < kPfSplitTiles; ++mt) {
+    const int ns = pf_ksplit(mt * nt, L.K / kGroup, nullptr);
+    if (ns < 2) continue;
+    const int64_t rows = L.M_max < mt * kPfTileM ? L.M_max : mt * kPfTileM;
+    const int64_t b = 4 * ns * rows * L.N;
+    best = b > best ? b : best;
+  }
+  return best;
+}
 
 inline WsLayout ws_layout(const dvssq_layout &L) {
   WsLayout w{};
@@ -326,6 +363,7 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
   w.p_sc = cur;   cur = align256(cur + 4 * static_cast<int64_t>(L.M_max));
   w.p_t = cur;    cur = align256(cur + 4 * static_cast<int64_t>(L.M_max) * nsp);
   w.p_tpart = cur; cur = align256(cur + 4 * kTSplitMax * static_cast<int64_t>(L.M_max) * nsp);
+  w.p_part = cur; cur = align256(cur + pf_part_bytes(L));
   w.p_end = cur;
   w.total = w.d_end > w.p_end ? w.d_end : w.p_end;
   return w;
@@ -393,8 +431,10 @@ struct PrefillArgs {
   const float *sc;     // fp32 [M] 2^e per row
   const float *t;      // fp32 [M][nsr_pad]
   uint16_t *y;         // bf16 [M][N]
+  float *part;         // K split: fp32 [ksplit][M][N] partial sums per packed row
   int N, K, r, n_seg, n4, n8, M, nsr, nsr_pad;
   int n4_tiles, n8_tiles, m_tiles;
+  int ksplit, kspw;    // K-ranges per tile (1: no split) and GEMM steps per range
 };
 
 struct GegluArgs {

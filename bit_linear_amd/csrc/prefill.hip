@@ -37,21 +37,27 @@ constexpr int TS = NS * 16 + 8;
 // lane (fr, fh) of fragment j takes row 32 j + fr and inputs 32 fh .. 32 fh + 31
 // of the group, which are contiguous in the packed rows -- and dequantizes
 // them there.  Loads run one step ahead of the matrix cores.
-template <bool T8, int NS>
+template <bool T8, int NS, bool SPLIT>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0, uint16_t *A1, uint16_t *A2,
-                                             uint16_t *ts, float *scs, int mtile, int tile0) {
+                                             uint16_t *ts, float *scs, int mtile, int tile0, int split) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, fh = lane >> 5;
-  const int KG = a.K / BK;
+  const int KGa = a.K / BK;                                   // steps of the whole K
+  const int s0 = split * a.kspw;                              // this workgroup's K-range
+  const int KG = min(KGa, s0 + a.kspw) - s0;                  // its steps
   const int rows = T8 ? a.n8 : a.n4;
   const int p0 = tile0 + 64 * wave;   // first weight row (inside the tier) of this wavefront
-  const uint16_t *ag = a.xr + static_cast<int64_t>(mtile) * KG * kTileA;
+  const uint16_t *ag = a.xr + (static_cast<int64_t>(mtile) * KGa + s0) * kTileA;
   const int m0 = mtile * kPfTileM;
 
   // the epilogue's token-side operands, staged in LDS while the main loop runs:
-  // t rows of the tile as bf16 (padded rows of TS), and the row scales
-  {
+  // t rows of the tile as bf16 (padded rows of TS) and the row scales.  With a
+  // K split, the first range alone adds the low-rank term.
+  const bool lowrank = !SPLIT || split == 0;
+  if (!lowrank) {
+    if (tid < kPfTileM) scs[tid] = m0 + tid < a.M ? a.sc[m0 + tid] : 0.0f;
+  } else {
     const auto rt = make_rsrc(a.t, static_cast<uint32_t>(a.M) * (NS * 16) * 4);
     const int row = tid >> 1, half = tid & 1;
     const uint32_t base = static_cast<uint32_t>((m0 + row) * (NS * 16) + half * (NS * 8)) * 4;
@@ -79,14 +85,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0,
   const int nrow = min(kPfTileN, rows - tile0);
   const auto rq = make_rsrc((T8 ? static_cast<const uint8_t *>(static_cast<const void *>(a.q8)) : a.q4) + tile0 * rb,
                             static_cast<uint32_t>(nrow * rb));
-  const auto rs = make_rsrc(a.s4 + static_cast<int64_t>(tile0) * KG, static_cast<uint32_t>(T8 ? 0 : nrow * KG * 2));
+  const auto rs = make_rsrc(a.s4 + static_cast<int64_t>(tile0) * KGa, static_cast<uint32_t>(T8 ? 0 : nrow * KGa * 2));
   uint32_t oq[NF], os[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     const int rl = 64 * wave + 32 * j + fr;   // row inside the workgroup's tile
     const bool ok = rl < nrow;
-    oq[j] = ok ? static_cast<uint32_t>(rl * rb + (T8 ? 32 : 16) * fh) : kOutOfRange;
-    os[j] = ok ? static_cast<uint32_t>(rl * KG * 2) : kOutOfRange;
+    oq[j] = ok ? static_cast<uint32_t>(rl * rb + (T8 ? 32 : 16) * fh + (T8 ? 64 : 32) * s0) : kOutOfRange;
+    os[j] = ok ? static_cast<uint32_t>((rl * KGa + s0) * 2) : kOutOfRange;
   }
 
   // x_rot tiles: a direct copy into LDS (each wavefront instruction fills 1 KB
@@ -223,8 +229,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0,
   // before the workgroup can end
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
-  // ---- epilogue: row scale 2^e, INT8 row scale, low-rank slab, bf16 scatter through idx
-  // weight-side loads first, all in one batch
+  // ---- epilogue: row scale 2^e, INT8 row scale, low-rank slab, bf16 scatter
+  // through idx -- or, with a K split, this range's result as fp32 at
+  // [split][m][packed row] for psum_kernel.  Weight-side loads first, in one batch
   int pj[NF], col[NF];
   bool okj[NF];
   float s8[NF];
@@ -238,7 +245,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0,
     s8[j] = T8 ? a.s8[okj[j] ? pl : 0] : 1.0f;
   }
   const int seg_cols = a.N / a.n_seg;
-  if ((a.r & 7) == 0) {
+  if (!lowrank) {
+    // no low-rank term in this K-range
+  } else if ((a.r & 7) == 0) {
     // slots of one segment are whole runs of 8: one 16-byte load each
     const auto ru = make_rsrc(a.U, static_cast<uint32_t>(a.N) * a.r * 2);
 #pragma unroll
@@ -281,21 +290,33 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0,
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[i][j][4 * k + v] *= sc4[v] * s8[j];
       }
+    if (lowrank)
 #pragma unroll
-    for (int js = 0; js < NS; ++js)
+      for (int js = 0; js < NS; ++js)
 #pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        const u32x4 av = *reinterpret_cast<const u32x4 *>(ts + (32 * i + fr) * TS<NS> + 16 * js + 8 * fh);
-        acc[i][j] = mfma32x32x16(av, bu[j][js], acc[i][j]);
-      }
+        for (int i = 0; i < MF; ++i) {
+          const u32x4 av = *reinterpret_cast<const u32x4 *>(ts + (32 * i + fr) * TS<NS> + 16 * js + 8 * fh);
+          acc[i][j] = mfma32x32x16(av, bu[j][js], acc[i][j]);
+        }
     if (!okj[j]) continue;
+    if constexpr (SPLIT) {
+      float *dst = a.part + static_cast<int64_t>(split) * a.M * a.N + pj[j];
 #pragma unroll
-    for (int i = 0; i < MF; ++i)
+      for (int i = 0; i < MF; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + 32 * i + 8 * (v / 4) + 4 * fh + (v % 4);
-        if (m < a.M) a.y[static_cast<int64_t>(m) * a.N + col[j]] = f32_to_bf16(acc[i][j][v]);
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + 32 * i + 8 * (v / 4) + 4 * fh + (v % 4);
+          if (m < a.M) dst[static_cast<int64_t>(m) * a.N] = acc[i][j][v];
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + 32 * i + 8 * (v / 4) + 4 * fh + (v % 4);
+          if (m < a.M) a.y[static_cast<int64_t>(m) * a.N + col[j]] = f32_to_bf16(acc[i][j][v]);
+        }
+    }
   }
 }
 
@@ -305,24 +326,61 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __align__(16) uint16_t A2[kTileA];
   __shared__ __align__(16) uint16_t ts[kPfTileM * TS<4>];
   __shared__ __align__(16) float scs[kPfTileM];
-  // consecutive workgroups share a weight tile (its bytes stay in L2)
-  const int ntile = blockIdx.x / a.m_tiles, mtile = blockIdx.x % a.m_tiles;
+  // consecutive workgroups share a weight tile (its bytes stay in L2); with a
+  // K split, the ranges of one tile sit m_tiles workgroups apart
+  const int mtile = blockIdx.x % a.m_tiles, rest = blockIdx.x / a.m_tiles;
+  const int split = rest % a.ksplit, ntile = rest / a.ksplit;
   const bool t8 = ntile >= a.n4_tiles;
   const int tile0 = (t8 ? ntile - a.n4_tiles : ntile) * kPfTileN;
-  if (a.nsr_pad == 64) {
-    if (t8) prefill_tile<true, 4>(a, A0, A1, A2, ts, scs, mtile, tile0);
-    else prefill_tile<false, 4>(a, A0, A1, A2, ts, scs, mtile, tile0);
+  if (a.ksplit > 1) {
+    if (a.nsr_pad == 64) {
+      if (t8) prefill_tile<true, 4, true>(a, A0, A1, A2, ts, scs, mtile, tile0, split);
+      else prefill_tile<false, 4, true>(a, A0, A1, A2, ts, scs, mtile, tile0, split);
+    } else {
+      if (t8) prefill_tile<true, 2, true>(a, A0, A1, A2, ts, scs, mtile, tile0, split);
+      else prefill_tile<false, 2, true>(a, A0, A1, A2, ts, scs, mtile, tile0, split);
+    }
+  } else if (a.nsr_pad == 64) {
+    if (t8) prefill_tile<true, 4, false>(a, A0, A1, A2, ts, scs, mtile, tile0, 0);
+    else prefill_tile<false, 4, false>(a, A0, A1, A2, ts, scs, mtile, tile0, 0);
   } else {
-    if (t8) prefill_tile<true, 2>(a, A0, A1, A2, ts, scs, mtile, tile0);
-    else prefill_tile<false, 2>(a, A0, A1, A2, ts, scs, mtile, tile0);
+    if (t8) prefill_tile<true, 2, false>(a, A0, A1, A2, ts, scs, mtile, tile0, 0);
+    else prefill_tile<false, 2, false>(a, A0, A1, A2, ts, scs, mtile, tile0, 0);
   }
+}
+
+// After a K split: y[m][idx[p]] = bf16(the ranges' results summed in range
+// order; the first range carries the low-rank term).  Four consecutive packed
+// rows of one token per thread.
+__global__ __launch_bounds__(kThreads) void psum_kernel(PrefillArgs a) {
+  const int nq = a.N / 4;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (e >= static_cast<int64_t>(a.M) * nq) return;
+  const int m = static_cast<int>(e / nq), p0 = static_cast<int>(e - static_cast<int64_t>(m) * nq) * 4;
+  const int64_t plane4 = static_cast<int64_t>(a.M) * a.N / 4;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(a.part + static_cast<int64_t>(m) * a.N + p0);
+  f32x4 v[kPfSplitMax];
+#pragma unroll
+  for (int k = 0; k < kPfSplitMax; ++k) v[k] = k < a.ksplit ? src[k * plane4] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const u32x4 col = *reinterpret_cast<const u32x4 *>(a.idx + p0);
+  f32x4 acc = v[0];
+#pragma unroll
+  for (int k = 1; k < kPfSplitMax; ++k)
+    if (k < a.ksplit) acc += v[k];
+  uint16_t *yr = a.y + static_cast<int64_t>(m) * a.N;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) yr[static_cast<int>(col[q])] = f32_to_bf16(acc[q]);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
-  const int grid = (a.n4_tiles + a.n8_tiles) * a.m_tiles;
-  return launch_kernel(reinterpret_cast<const void *>(prefill_kernel), dim3(grid), dim3(kThreads), 0, s, a);
+  const int grid = (a.n4_tiles + a.n8_tiles) * a.m_tiles * a.ksplit;
+  const hipError_t e = launch_kernel(reinterpret_cast<const void *>(prefill_kernel), dim3(grid), dim3(kThreads), 0, s, a);
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  const int64_t n = static_cast<int64_t>(a.M) * (a.N / 4);
+  return launch_kernel(reinterpret_cast<const void *>(psum_kernel), dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, a);
 }
 
 }  // namespace dvssq

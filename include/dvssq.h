@@ -131,9 +131,10 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
                         int32_t M, void *ws, uint32_t flags, void *stream);
 
 /*
- * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: four or five kernel
+ * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: four to six kernel
  * launches (per-row scales, rotation, t and, when t is split over K-ranges, their
- * ordered sum, then the GEMM).  Needs K <= 2^22,
+ * ordered sum, then the GEMM and, when a GEMM of few tiles is split over
+ * K-ranges, the ordered sum of their results).  Needs K <= 2^22,
  * M <= 2^22 and N r <= 2^29 (DVSSQ_EUNSUPPORTED otherwise).  Same arguments and ownership rules as
  * dvssq_linear_decode.  The rotated activations are held in f16 with one
  * power-of-two scale per row, the weights as exact f16 values (same s4 range
