@@ -106,6 +106,8 @@ PREFILL_CASES = [
     ("tiny", 1), ("tiny", 4), ("tiny", 33), ("tiny", 130), ("tiny", 257),
     ("ragged_b64_r1", 45), ("k192_b64", 19), ("b128_r64", 200), ("seg2_b512_r32", 129), ("b1024_tail", 64),
     ("b2048_ragged", 100), ("seg2_small", 77), ("spark_up", 40),
+    # 120 GEMM tiles (K split in two) and 160 tiles (no split), element by element
+    ("spark_up", 384), ("spark_up", 512),
 ]
 
 
