@@ -806,10 +806,12 @@ hipError_t launch_m(const DecodeArgs &a, hipStream_t s) {
 // wavefront (the register file holds 16 wavefronts of at most 128 registers)
 // and the LDS within 160 KB.  Every workgroup, a t producer included, holds a
 // whole compute unit.  The plan minimises an estimated cost fitted to
-// measured runs: the rounds of workgroups, each weighted by the activation
-// planes a workgroup copies per byte of its weights (M > 4), plus 0.4 + 0.05 S
-// for a split (it adds a reduction), minus 0.2 x the share of compute units
-// kept busy; ties go to more workgroups.
+// measured runs (every feasible plan timed on spark_up, spark_down, gate+up
+// and the MiniCPM layers at M = 1 .. 32): the rounds of workgroups, each
+// weighted by the activation planes a workgroup copies per byte of its weights
+// (M > 4), plus 0.4 + 0.05 S for a split (it adds a reduction) and 4 x the
+// bytes of its fp32 partials per byte of the packed layer, minus 0.2 x the
+// share of compute units kept busy; ties go to more workgroups.
 bool plan_decode_small(const dvssq_layout &L, int M, int cus, SmallPlan *plan) {
   if (M < 1 || M > 32) return false;
   // byte offsets of the buffer loads stay below 2^31
@@ -842,8 +844,11 @@ bool plan_decode_small(const dvssq_layout &L, int M, int cus, SmallPlan *plan) {
       const int rounds = (wgs + cus - 1) / cus;
       // activation planes a workgroup copies (M > 4) per byte of its weights
       const double planes = M >= 5 ? 2.0 * M / (RT * kTile * (0.5 + 2.0 / kGroup)) : 0.0;
+      // split-K partials written and read back (fp32 [S][M][N]) per byte of the packed layer
+      const double part = S > 1 ? 4.0 * S * M * static_cast<double>(L.N) / static_cast<double>(L.blob_bytes) : 0.0;
       const double util = static_cast<double>(wgs) / (static_cast<double>(cus) * rounds);
-      const double cost = rounds * (1.0 + 0.5 * planes) + (S > 1 ? 0.4 + 0.05 * S : 0.0) - 0.2 * util;
+      const double cost =
+          rounds * (1.0 + 0.3 * planes) + (S > 1 ? 0.4 + 0.05 * S : 0.0) + 4.0 * part - 0.2 * util;
       const double score = -cost;
       if (score > best + 1e-9 || (score > best - 1e-9 && wgs > best_wgs)) {
         best = score;

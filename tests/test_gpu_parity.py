@@ -79,7 +79,7 @@ def test_fwht_exact_special_cases():
 DECODE_CASES = [
     ("tiny", 1), ("tiny", 4), ("tiny", 3), ("tiny", 8), ("tiny", 9), ("tiny", 16), ("tiny", 17),
     ("tiny", 32),
-    ("spark_up", 1), ("spark_up", 4), ("spark_up", 16),
+    ("spark_up", 1), ("spark_up", 4), ("spark_up", 16), ("spark_up", 32),
     ("spark_down", 1), ("spark_down", 8), ("spark_down", 32),
     ("minicpm_gate", 1), ("minicpm_up", 1), ("minicpm_down", 1),
     ("minicpm_gate_r32", 1), ("minicpm_down_r32", 1),
