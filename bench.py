@@ -312,7 +312,7 @@ def main():
 
     if not args.no_table:
         table = []
-        for name, Ms in (("spark_up", (4, 16)), ("spark_down", (1, 8, 32)), ("minicpm_gate", (1,)),
+        for name, Ms in (("spark_up", (4, 16, 32)), ("spark_down", (1, 8, 32)), ("minicpm_gate", (1,)),
                          ("minicpm_down", (1,)), ("spark_gateup", (1,))):
             for m in Ms:
                 r = Runner(dv, torch, layers[name], m, 32)
