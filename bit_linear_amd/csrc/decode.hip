@@ -549,11 +549,9 @@ __global__ __launch_bounds__(kThreads) void decode_prologue_kernel(DecodeArgs a)
   produce_any<kModeSplit>(a, blockIdx.x, smem);
 }
 
-hipError_t set_lds(const void *fn, size_t lds, bool &done) {
-  if (lds <= 65536 || done) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (e == hipSuccess) done = true;
-  return e;
+hipError_t set_lds(const void *fn, size_t lds, std::atomic<uint64_t> &done) {
+  if (lds <= 65536) return hipSuccess;
+  return ensure_lds_limit(fn, 160 * 1024, done);
 }
 
 size_t prologue_lds_bytes(int unit) {
@@ -566,7 +564,7 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = decode_lds_bytes(a.M, a.unit, a.KW, a.nsr_pad);
   const int groups = (a.g4 + a.g8) * a.S;
   if (a.fused) {
-    static bool done = false;
+    static std::atomic<uint64_t> done{0};
     const hipError_t e = set_lds(reinterpret_cast<const void *>(decode_kernel<MSUB, MAXS, true>), lds, done);
     if (e != hipSuccess) return e;
     return launch_kernel(reinterpret_cast<const void *>(decode_kernel<MSUB, MAXS, true>), dim3(a.nprod + groups),
@@ -575,7 +573,7 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
   hipError_t e = launch_kernel(reinterpret_cast<const void *>(decode_prologue_kernel), dim3(a.nprod), dim3(kThreads),
                                prologue_lds_bytes(a.unit), s, a);
   if (e != hipSuccess) return e;
-  static bool done = false;
+  static std::atomic<uint64_t> done{0};
   e = set_lds(reinterpret_cast<const void *>(decode_kernel<MSUB, MAXS, false>), lds, done);
   if (e != hipSuccess) return e;
   return launch_kernel(reinterpret_cast<const void *>(decode_kernel<MSUB, MAXS, false>), dim3(groups), dim3(kThreads),

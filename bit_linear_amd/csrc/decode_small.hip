@@ -769,13 +769,10 @@ template <int MT, int C, int MAXG>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = small_lds(a.M, a.unit, a.KW, a.nsr_pad);
   if (lds > 65536) {
-    static bool done = false;
-    if (!done) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_small_kernel<MT, C, MAXG>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      done = true;
-    }
+    static std::atomic<uint64_t> done{0};
+    const hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void *>(decode_small_kernel<MT, C, MAXG>), 160 * 1024, done);
+    if (e != hipSuccess) return e;
   }
   const int grid = a.nprod + (a.g4 + a.g8) * a.S;
   return launch_kernel(reinterpret_cast<const void *>(decode_small_kernel<MT, C, MAXG>), dim3(grid), dim3(kThreads), lds,

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/dvssq.h"
 
@@ -123,6 +124,21 @@ __device__ __forceinline__ u32x4 int8_to_f16(uint32_t lo, uint32_t hi) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = pk_add(__builtin_amdgcn_perm(hi, lo, sel[i]) ^ 0x64806480u, m1152);
   return r;
+}
+
+// ------------------------------------------------------------------ launch set-up
+// Allow a kernel more than 64 KB of dynamic LDS (up to `bytes`), once per
+// device: the attribute belongs to the current device.  `done` holds one bit
+// per device id already set up (ids >= 64 are set up on every call).
+inline hipError_t ensure_lds_limit(const void *fn, int bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
 }
 
 // ------------------------------------------------------------------ Hadamard blocks on the matrix cores

@@ -346,14 +346,10 @@ hipError_t launch_vpl(const PrologueArgs &a, int n_wg_blocks, hipStream_t s) {
   constexpr int B = 64 * VPL;
   const size_t lds = VPL >= 8 ? static_cast<size_t>(MT) * (B + 8) * 2 : static_cast<size_t>(MT) * (B + 4) * 4;
   if (lds > 65536) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prologue_kernel<VPL, MT>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static std::atomic<uint64_t> done{0};
+    const hipError_t e =
+        ensure_lds_limit(reinterpret_cast<const void *>(prologue_kernel<VPL, MT>), static_cast<int>(lds), done);
+    if (e != hipSuccess) return e;
   }
   dim3 grid((a.M + MT - 1) / MT, n_wg_blocks);
   return launch_kernel(reinterpret_cast<const void *>(prologue_kernel<VPL, MT>), grid, dim3(kThreads), lds, s, a);
