@@ -327,6 +327,8 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   p.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
   p.hscale = inv_sqrt_block(L->block);
   p.exp_bias = (p.rotate ? (__builtin_ctz(static_cast<unsigned>(L->block)) + 1) / 2 : 0) + 1 - 15;
+  // a single Hadamard block of 256 or more: its rotation kernel sees whole rows
+  p.fuse_scale = (L->K == L->block && L->block >= 256) ? 1 : 0;
   hipError_t e = launch_prologue(p, L->block, L->K / L->block, compute_units(), s);
   if (e != hipSuccess) return DVSSQ_EHIP;
 

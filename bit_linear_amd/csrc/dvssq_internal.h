@@ -398,6 +398,7 @@ struct PrologueArgs {
   int rotate;          // 0: x is already rotated (copy + t only)
   float hscale;        // 1/sqrt(block)
   int exp_bias;        // prefill: row exponent = ilogb(max |x|) + exp_bias (log2 sqrt(block) if rotating, + 1 - 15)
+  int fuse_scale;      // prefill with K == block >= 256: the rotation kernel finds the row exponents itself
 };
 
 struct DecodeArgs {

@@ -128,9 +128,12 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
   const int b1 = min(nblk, b0 + a.blocks_per_wg);
   const int mrows = min(MT, a.M - m0);
 
-  // 0. per-row power-of-two scale, written by rowscale_kernel
-  for (int ml = tid; ml < MT; ml += kThreads) rowexp[ml] = ml < mrows ? ilogbf(a.sc[m0 + ml]) : 0;
-  __syncthreads();
+  // 0. per-row power-of-two scale, written by rowscale_kernel (or, when a
+  // block is the whole row, found below by the wavefront that rotates the row)
+  if (!a.fuse_scale) {
+    for (int ml = tid; ml < MT; ml += kThreads) rowexp[ml] = ml < mrows ? ilogbf(a.sc[m0 + ml]) : 0;
+    __syncthreads();
+  }
 
   constexpr int RB = kRowBatch<VPL>;
 
@@ -155,6 +158,28 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
         for (int j = 0; j < RB; ++j) {
           const int ml = ml0 + 4 * j;
           if (ml >= MT) continue;
+          const bool live = ml < mrows;
+          int ex;   // the row's exponent e
+          if (a.fuse_scale) {
+            // as rowscale_kernel: e from max |x| of the row (this block)
+            float mx = 0.0f;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(xw[j][c][h] << 16)),
+                                     fabsf(__uint_as_float(xw[j][c][h] & 0xFFFF0000u))));
+#pragma unroll
+            for (int sft = 1; sft < 64; sft <<= 1) mx = fmaxf(mx, __shfl_xor(mx, sft, 64));
+            ex = 0;
+            if (mx > 0.0f && mx <= 3.0e38f) ex = max(-120, min(120, ilogbf(mx) + a.exp_bias));
+            if (lane == 0) {
+              rowexp[ml] = live ? ex : 0;
+              if (live) a.sc[m0 + ml] = ldexpf(1.0f, ex);
+            }
+          } else {
+            ex = rowexp[ml];
+          }
           float y[C][4];
           if (a.rotate) {
             rotate_blocks<C>(xw[j], y, B, a.hscale);
@@ -167,12 +192,11 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
               y[c][3] = __uint_as_float(xw[j][c][1] & 0xFFFF0000u);
             }
           }
-          const bool live = ml < mrows;
           if constexpr (H16) {
             // f16 x 2^-e; inputs 4 h + j (h = q % 2) of run r fill slots
             // (j even) h, ... and (j odd) 4 + h, ... of the order 0,2,4,6,1,3,5,7
             uint16_t *row = reinterpret_cast<uint16_t *>(lds) + ml * LDH;
-            const float d = ldexpf(1.0f, -rowexp[ml]);
+            const float d = ldexpf(1.0f, -ex);
 #pragma unroll
             for (int c = 0; c < C; ++c) {
               const int r = 32 * c + 2 * n + (q >> 1), h = q & 1;
@@ -370,9 +394,13 @@ hipError_t launch_fwht(const PrologueArgs &a, int block, hipStream_t s) {
 }
 
 hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, int cus, hipStream_t s) {
-  hipError_t e = launch_kernel(reinterpret_cast<const void *>(rowscale_kernel),
-                               dim3((a.M + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, s, a);
-  if (e != hipSuccess) return e;
+  if (a.fuse_scale && (a.K != block || block < 256)) return hipErrorInvalidValue;
+  hipError_t e = hipSuccess;
+  if (!a.fuse_scale) {
+    e = launch_kernel(reinterpret_cast<const void *>(rowscale_kernel),
+                      dim3((a.M + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, s, a);
+    if (e != hipSuccess) return e;
+  }
   switch (block) {
     case 64: e = launch_vpl<1, 32>(a, n_wg_blocks, s); break;
     case 128: e = launch_vpl<2, 32>(a, n_wg_blocks, s); break;
