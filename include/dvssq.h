@@ -131,10 +131,11 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
                         int32_t M, void *ws, uint32_t flags, void *stream);
 
 /*
- * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: four to six kernel
- * launches (per-row scales, rotation, t and, when t is split over K-ranges, their
- * ordered sum, then the GEMM and, when a GEMM of few tiles is split over
- * K-ranges, the ordered sum of their results).  Needs K <= 2^22,
+ * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: three to six kernel
+ * launches (per-row scales, unless K == block >= 256, where the rotation finds
+ * them; rotation; t and, when t is split over K-ranges, their ordered sum; the
+ * GEMM and, when a GEMM of few tiles is split over K-ranges, the ordered sum of
+ * their results).  Needs K <= 2^22,
  * M <= 2^22 and N r <= 2^29 (DVSSQ_EUNSUPPORTED otherwise).  Same arguments and ownership rules as
  * dvssq_linear_decode.  The rotated activations are held in f16 with one
  * power-of-two scale per row, the weights as exact f16 values (same s4 range
