@@ -241,10 +241,12 @@ def bf16_bits_value(bits: np.ndarray) -> np.ndarray:
 
 
 def gelu(x: np.ndarray) -> np.ndarray:
-    """GELU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 (the standard normal CDF Phi)."""
+    """GELU(x) = x Phi(x) with the standard normal CDF Phi(x) = erfc(-x / sqrt 2) / 2
+    (the same function as (1 + erf(x / sqrt 2)) / 2, without its cancellation for
+    negative x, where 1 + erf loses every digit below Phi ~ 1e-16)."""
     import scipy.special
     x = np.asarray(x, dtype=np.float64)
-    return 0.5 * x * (1.0 + scipy.special.erf(x / np.sqrt(2.0)))
+    return 0.5 * x * scipy.special.erfc(-x / np.sqrt(2.0))
 
 
 def mlp_intermediate(y_gate_up: np.ndarray) -> np.ndarray:
@@ -277,8 +279,8 @@ def mlp_forward_cols(gu_blob: np.ndarray, gu: tuple, down_blob: np.ndarray, down
 
 
 # ------------------------------------------------------------------ dense materialization (test infrastructure)
-# The MiniCPM card's usage section offers to materialize the quantized MLP
-# weights into plain BF16 for generation.  Reading: the dense weight of the
+# The Spark card's Quickstart & Inference Guide offers materialize_weights(),
+# which turns the quantized MLP weights into plain BF16 for generation.  Reading: the dense weight of the
 # layer in the original input domain, W = (W_hat + U V_seg) H^T (H symmetric,
 # so H^T = H), so that x W^T is the layer's forward; rows in original output
 # order, rounded once to bf16.

@@ -438,6 +438,11 @@ def test_gelu_closed_forms():
     np.testing.assert_allclose(oracle.gelu(x) - oracle.gelu(-x), x, rtol=0, atol=1e-14)
     assert oracle.gelu(np.array([10.0]))[0] == 10.0
     assert abs(oracle.gelu(np.array([-10.0]))[0]) < 1e-20
+    # the far negative tail, relatively: Phi(-5) = 2.866515718791939e-07,
+    # Phi(-8) = 6.220960574271784e-16, Phi(-10) = 7.619853024160470e-24
+    np.testing.assert_allclose(oracle.gelu(np.array([-5.0, -8.0, -10.0])),
+                               [-5 * 2.866515718791939e-07, -8 * 6.220960574271784e-16,
+                                -10 * 7.619853024160470e-24], rtol=1e-12, atol=0)
     pdf = lambda t: np.exp(-0.5 * t * t) / np.sqrt(2 * np.pi)
     for v in (-2.5, -0.3, 0.7, 1.9):
         phi = 0.5 + scipy.integrate.quad(pdf, 0.0, v, epsabs=1e-15, epsrel=1e-14)[0]
