@@ -23,11 +23,14 @@ DVSSQ_EINVAL = -1
 DVSSQ_EUNSUPPORTED = -2
 DVSSQ_EHIP = -3
 DVSSQ_X_ROTATED = 1
+DVSSQ_TEST_NO_PUBLISH = 0x80000000
+DVSSQ_WS_STATUS_BYTES = 256
+DVSSQ_STATUS_WAIT_TIMEOUT = 1
 DECODE_MAX_M = 32
 
 EXPORTS = ("dvssq_pack_info", "dvssq_fwht", "dvssq_linear_decode", "dvssq_linear_prefill",
-           "dvssq_materialize", "dvssq_mlp_ws_bytes", "dvssq_mlp_decode", "dvssq_mlp_prefill",
-           "dvssq_status_str")
+           "dvssq_materialize", "dvssq_mlp_ws_bytes", "dvssq_mlp_ws_offsets", "dvssq_mlp_decode",
+           "dvssq_mlp_prefill", "dvssq_stream_read", "dvssq_status_str")
 
 
 class Layout(C.Structure):
@@ -72,9 +75,14 @@ _lib.dvssq_materialize.restype = C.c_int
 _lib.dvssq_materialize.argtypes = [C.POINTER(Layout), _P, _P, _P]
 _lib.dvssq_mlp_ws_bytes.restype = C.c_int
 _lib.dvssq_mlp_ws_bytes.argtypes = [C.POINTER(Layout), C.POINTER(Layout), C.POINTER(C.c_int64)]
+_lib.dvssq_mlp_ws_offsets.restype = C.c_int
+_lib.dvssq_mlp_ws_offsets.argtypes = [C.POINTER(Layout), C.POINTER(Layout), C.POINTER(C.c_int64),
+                                      C.POINTER(C.c_int64)]
 for _n in ("dvssq_mlp_decode", "dvssq_mlp_prefill"):
     getattr(_lib, _n).restype = C.c_int
     getattr(_lib, _n).argtypes = [C.POINTER(Layout), _P, C.POINTER(Layout), _P, _P, _P, C.c_int32, _P, C.c_uint32, _P]
+_lib.dvssq_stream_read.restype = C.c_int
+_lib.dvssq_stream_read.argtypes = [_P, C.c_int64, _P, _P]
 _lib.dvssq_status_str.restype = C.c_char_p
 _lib.dvssq_status_str.argtypes = [C.c_int]
 
@@ -140,6 +148,13 @@ def mlp_ws_bytes(gu: Layout, down: Layout) -> int:
     return int(out.value)
 
 
+def mlp_ws_offsets(gu: Layout, down: Layout) -> tuple[int, int]:
+    """(off_ygu, off_h): byte offsets of the block's intermediates in its workspace."""
+    a, b = C.c_int64(0), C.c_int64(0)
+    _check(_lib.dvssq_mlp_ws_offsets(C.byref(gu), C.byref(down), C.byref(a), C.byref(b)), "dvssq_mlp_ws_offsets")
+    return int(a.value), int(b.value)
+
+
 def mlp_decode(gu: Layout, gu_blob, down: Layout, down_blob, x, y, M: int, ws, flags: int = 0,
                stream=None) -> None:
     _check(_lib.dvssq_mlp_decode(C.byref(gu), _ptr(gu_blob), C.byref(down), _ptr(down_blob), _ptr(x), _ptr(y), M,
@@ -150,6 +165,11 @@ def mlp_prefill(gu: Layout, gu_blob, down: Layout, down_blob, x, y, M: int, ws, 
                 stream=None) -> None:
     _check(_lib.dvssq_mlp_prefill(C.byref(gu), _ptr(gu_blob), C.byref(down), _ptr(down_blob), _ptr(x), _ptr(y), M,
                                   _ptr(ws), flags, _stream(stream)), "dvssq_mlp_prefill")
+
+
+def stream_read(buf, nbytes: int, sink, stream=None) -> None:
+    """Measurement aid: a plain streaming read of nbytes of buf (no computation)."""
+    _check(_lib.dvssq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "dvssq_stream_read")
 
 
 def pack_blob(layout: Layout, parts: dict) -> np.ndarray:

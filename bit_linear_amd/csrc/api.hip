@@ -86,33 +86,14 @@ uint64_t next_generation() {
   return g;
 }
 
-// Split-K factor of the decode kernel: S equal parts of K, each a multiple of
-// 128 inputs (so no 128-input span crosses a rotation unit) and at most
-// decode_max_spans() spans, whose on-chip staging fits in LDS.  The smallest
-// such S that gives >= 512 consumer workgroups within 80 KB of LDS (two
-// workgroups per compute unit); failing that, the largest such S (LDS use
-// falls as S grows).  0 when no S fits.
-// Largest M decoded by the small-M kernel (int8 matrix cores, 16-wavefront
-// consumer workgroups).
+// Largest M decoded by the single-launch kernel (int8 matrix cores,
+// 16-wavefront consumer workgroups).
 constexpr int kSmallMaxM = 32;
 constexpr int kPlanesMinM = 5;   // from this M on, producers quantize x_rot once for all consumers
-
-// Largest M decoded in one launch (producers and consumers together); larger
-// M uses a separate rotation launch first.
-constexpr int kDecodeFusedMaxM = 32;
-
-int decode_split(int K, int groups, int M, int unit, int nsr_pad) {
-  const int nspan = K / 128;
-  int best = 0;
-  for (int S = 1; S <= kMaxSplit && S <= nspan; ++S) {
-    if (nspan % S || nspan / S > decode_max_spans()) continue;
-    const size_t lds = decode_lds_bytes(M, unit, K / S, nsr_pad);
-    if (lds > 160 * 1024) continue;
-    if (lds <= 80 * 1024 && static_cast<int64_t>(groups) * S >= 512) return S;
-    best = S;
-  }
-  return best;
-}
+// Polls of a producer flag before a consumer's wait gives up: about 0.1 s at
+// the sleep of one poll; under DVSSQ_TEST_NO_PUBLISH a few polls only.
+constexpr int kSpinLimit = 1 << 22;
+constexpr int kTestSpinLimit = 64;
 
 float inv_sqrt_block(int block) {
   // 1/sqrt(b) rounded once to fp32: b = 2^e
@@ -198,29 +179,29 @@ static int compute_units() {
   return v;
 }
 
-// the decode's shape conditions beyond the argument checks: K a whole number
-// of rotation units, and a plan that fits
-static int decode_supported(const dvssq_layout &L, int32_t M) {
-  if (L.K % decode_unit(L.block) != 0) return DVSSQ_EUNSUPPORTED;
-  SmallPlan sp{};
-  if (M <= kSmallMaxM && plan_decode_small(L, M, compute_units(), &sp)) return sp.S > 0 ? DVSSQ_OK : DVSSQ_EUNSUPPORTED;
-  const int S = decode_split(L.K, decode_groups(L.n_int4) + decode_groups(L.n_int8), M, decode_unit(L.block),
-                             nsr_pad_of(L.n_seg, L.r));
-  return S > 0 ? DVSSQ_OK : DVSSQ_EUNSUPPORTED;
+// The single-launch decode kernel takes the call when K is a whole number of
+// rotation units of max(block, 256) inputs and one of its plans fits;
+// otherwise the call runs the prefill path.
+static bool decode_single_launch(const dvssq_layout &L, int32_t M, SmallPlan *sp) {
+  if (L.K % decode_unit(L.block) != 0) return false;
+  return M <= kSmallMaxM && plan_decode_small(L, M, compute_units(), sp) && sp->S > 0;
 }
+
+static int prefill_supported(const dvssq_layout &L, int32_t M);
+static int prefill_launch(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M, void *ws,
+                          uint32_t flags, hipStream_t s);
 
 int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M,
                         void *ws, uint32_t flags, void *stream) {
   int rc = check_call(L, blob, x, y, M, ws, DVSSQ_DECODE_MAX_M);
   if (rc != DVSSQ_OK) return rc;
-  if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
-  if (L->K % decode_unit(L->block) != 0) return DVSSQ_EUNSUPPORTED;
-  const int g4 = decode_groups(L->n_int4), g8 = decode_groups(L->n_int8);
-  const int unit = decode_unit(L->block), nsp = nsr_pad_of(L->n_seg, L->r);
+  if (flags & ~(DVSSQ_X_ROTATED | DVSSQ_TEST_NO_PUBLISH)) return DVSSQ_EINVAL;
   SmallPlan sp{};
-  const bool small = M <= kSmallMaxM && plan_decode_small(*L, M, compute_units(), &sp);
-  const int S = small ? sp.S : decode_split(L->K, g4 + g8, M, unit, nsp);
-  if (S == 0) return DVSSQ_EUNSUPPORTED;
+  if (!decode_single_launch(*L, M, &sp)) {
+    if ((rc = prefill_supported(*L, M)) != DVSSQ_OK) return rc;
+    return prefill_launch(L, blob, x, y, M, ws, flags & DVSSQ_X_ROTATED, static_cast<hipStream_t>(stream));
+  }
+  const int g4 = decode_groups(L->n_int4), g8 = decode_groups(L->n_int8);
   const WsLayout W = ws_layout(*L);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   const Blob B{static_cast<const uint8_t *>(blob), L};
@@ -233,17 +214,15 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.V = B.V();
   d.idx = B.idx();
   d.x = static_cast<const uint16_t *>(x);
-  d.xq = reinterpret_cast<uint16_t *>(wsb + W.d_xq);
-  d.sc = reinterpret_cast<float *>(wsb + W.d_sc);
   d.tp = reinterpret_cast<float *>(wsb + W.d_tp);
   d.flag = reinterpret_cast<uint64_t *>(wsb + W.d_flag);
-  d.cnt = reinterpret_cast<int *>(wsb + W.d_cnt);
   d.part = reinterpret_cast<float *>(wsb + W.d_part);
   d.xg1 = reinterpret_cast<int8_t *>(wsb + W.d_xq);
   d.xg2 = d.xg1 + static_cast<int64_t>(kDecodeRows) * L->K;
   d.x8g = reinterpret_cast<int *>(wsb + W.d_x8g);
   d.escg = reinterpret_cast<float *>(wsb + W.d_escg);
   d.cntw = reinterpret_cast<uint64_t *>(wsb + W.d_cntw);
+  d.status = reinterpret_cast<int *>(wsb);
   d.y = static_cast<uint16_t *>(y);
   d.gen = next_generation();
   d.tag = static_cast<uint32_t>(d.gen ^ (d.gen >> 32));
@@ -258,36 +237,34 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.block = L->block;
   d.unit = decode_unit(L->block);
   d.nunit = L->K / d.unit;
-  d.nprod = small ? small_producers(d.nunit, M) : decode_producers(d.nunit, M);
+  d.nprod = small_producers(d.nunit, M);
   d.nsr = L->n_seg * L->r;
   d.nsr_pad = nsr_pad_of(L->n_seg, L->r);
-  d.g4 = small ? (g4 + sp.RT - 1) / sp.RT : g4;
-  d.g8 = small ? (g8 + sp.RT - 1) / sp.RT : g8;
-  d.S = S;
-  d.RT = small ? sp.RT : 0;
-  d.MAXG = small ? sp.MAXG : 0;
-  d.KQ = small ? sp.KQ : 0;
-  d.GPW = small ? sp.GPW : 0;
-  d.planes = small && M >= kPlanesMinM;
+  d.g4 = (g4 + sp.RT - 1) / sp.RT;
+  d.g8 = (g8 + sp.RT - 1) / sp.RT;
+  d.S = sp.S;
+  d.RT = sp.RT;
+  d.MAXG = sp.MAXG;
+  d.KQ = sp.KQ;
+  d.GPW = sp.GPW;
+  d.planes = M >= kPlanesMinM;
   d.KW = L->K / d.S;
-  if (small) {
-    d.ngrp_w = d.KW / kGroup;
-    d.nu_w = d.KW / d.unit;
-    d.magic_s = d.S > 1 ? static_cast<uint32_t>(((uint64_t{1} << 32) + d.S - 1) / d.S) : 0u;
-    d.lut_rt = d.lut_kq = d.lut_m = d.lut_u = 0;
-    for (int w = 0; w < 16; ++w) {
-      const uint64_t rt = static_cast<uint64_t>(std::min(w / sp.KQ, 15)), kq = static_cast<uint64_t>(w % sp.KQ);
-      d.lut_rt |= rt << (4 * w);
-      d.lut_kq |= kq << (4 * w);
-      d.lut_m |= static_cast<uint64_t>(w % M) << (4 * w);
-      d.lut_u |= static_cast<uint64_t>(w / M) << (4 * w);
-    }
+  d.ngrp_w = d.KW / kGroup;
+  d.nu_w = d.KW / d.unit;
+  d.magic_s = d.S > 1 ? static_cast<uint32_t>(((uint64_t{1} << 32) + d.S - 1) / d.S) : 0u;
+  d.lut_rt = d.lut_kq = d.lut_m = d.lut_u = 0;
+  for (int w = 0; w < 16; ++w) {
+    const uint64_t rt = static_cast<uint64_t>(std::min(w / sp.KQ, 15)), kq = static_cast<uint64_t>(w % sp.KQ);
+    d.lut_rt |= rt << (4 * w);
+    d.lut_kq |= kq << (4 * w);
+    d.lut_m |= static_cast<uint64_t>(w % M) << (4 * w);
+    d.lut_u |= static_cast<uint64_t>(w / M) << (4 * w);
   }
   d.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
-  d.fused = M <= kDecodeFusedMaxM ? 1 : 0;
+  d.publish = (flags & DVSSQ_TEST_NO_PUBLISH) ? 0 : 1;
+  d.spin_limit = (flags & DVSSQ_TEST_NO_PUBLISH) ? kTestSpinLimit : kSpinLimit;
   d.hscale = inv_sqrt_block(L->block);
-  const hipError_t e = small ? launch_decode_small(d, static_cast<hipStream_t>(stream))
-                               : launch_decode(d, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_decode_small(d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
@@ -304,11 +281,16 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
   // the GEMM addresses one workgroup's weight rows, t and U with 32-bit byte offsets
   if ((rc = prefill_supported(*L, M)) != DVSSQ_OK) return rc;
+  return prefill_launch(L, blob, x, y, M, ws, flags, static_cast<hipStream_t>(stream));
+}
+
+// The prefill's launches, after every argument check has passed.
+static int prefill_launch(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M, void *ws,
+                          uint32_t flags, hipStream_t s) {
   const WsLayout W = ws_layout(*L);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   const Blob B{static_cast<const uint8_t *>(blob), L};
   const int nsp = nsr_pad_of(L->n_seg, L->r);
-  hipStream_t s = static_cast<hipStream_t>(stream);
 
   PrologueArgs p{};
   p.x = static_cast<const uint16_t *>(x);
@@ -329,6 +311,9 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   p.exp_bias = (p.rotate ? (__builtin_ctz(static_cast<unsigned>(L->block)) + 1) / 2 : 0) + 1 - 15;
   // a single Hadamard block of 256 or more: its rotation kernel sees whole rows
   p.fuse_scale = (L->K == L->block && L->block >= 256) ? 1 : 0;
+  p.s4 = B.s4();
+  p.rsh = reinterpret_cast<float *>(wsb + W.p_rsh);
+  p.n4 = L->n_int4;
   hipError_t e = launch_prologue(p, L->block, L->K / L->block, compute_units(), s);
   if (e != hipSuccess) return DVSSQ_EHIP;
 
@@ -357,6 +342,7 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   f.m_tiles = (M + kPfTileM - 1) / kPfTileM;
   f.ksplit = pf_ksplit(f.m_tiles * (f.n4_tiles + f.n8_tiles), L->K / kGroup, &f.kspw);
   f.part = reinterpret_cast<float *>(wsb + W.p_part);
+  f.rsh = p.rsh;
   e = launch_prefill(f, s);
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
@@ -423,6 +409,16 @@ int dvssq_mlp_ws_bytes(const dvssq_layout *gu, const dvssq_layout *down, int64_t
   return DVSSQ_OK;
 }
 
+int dvssq_mlp_ws_offsets(const dvssq_layout *gu, const dvssq_layout *down, int64_t *off_ygu, int64_t *off_h) {
+  if (off_ygu == nullptr || off_h == nullptr) return DVSSQ_EINVAL;
+  const int rc = check_mlp(gu, down);
+  if (rc != DVSSQ_OK) return rc;
+  const MlpWs w = mlp_ws(*gu, *down);
+  *off_ygu = w.ygu;
+  *off_h = w.h;
+  return DVSSQ_OK;
+}
+
 // argument checks shared by the decode and prefill forms of the block
 static int check_mlp_call(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down,
                           const void *down_blob, const void *x, void *y, int32_t M, void *ws, uint32_t flags) {
@@ -446,7 +442,10 @@ int dvssq_mlp_decode(const dvssq_layout *gu, const void *gu_blob, const dvssq_la
   int rc = check_mlp_call(gu, gu_blob, down, down_blob, x, y, M, ws, flags);
   if (rc != DVSSQ_OK) return rc;
   if (M > DVSSQ_DECODE_MAX_M) return DVSSQ_EUNSUPPORTED;
-  if ((rc = decode_supported(*gu, M)) != DVSSQ_OK || (rc = decode_supported(*down, M)) != DVSSQ_OK) return rc;
+  // a projection that the single-launch kernel cannot take runs the prefill path
+  SmallPlan sp{};
+  if (!decode_single_launch(*gu, M, &sp) && (rc = prefill_supported(*gu, M)) != DVSSQ_OK) return rc;
+  if (!decode_single_launch(*down, M, &sp) && (rc = prefill_supported(*down, M)) != DVSSQ_OK) return rc;
   const MlpWs W = mlp_ws(*gu, *down);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   void *ygu = wsb + W.ygu;
@@ -476,12 +475,19 @@ int dvssq_mlp_prefill(const dvssq_layout *gu, const void *gu_blob, const dvssq_l
   return dvssq_linear_prefill(down, down_blob, h, y, M, ws, 0, stream);
 }
 
+int dvssq_stream_read(const void *buf, int64_t bytes, void *sink, void *stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 != 0 || bytes > (int64_t(1) << 40)) return DVSSQ_EINVAL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return DVSSQ_EINVAL;
+  return launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
+}
+
 const char *dvssq_status_str(int status) {
   switch (status) {
     case DVSSQ_OK: return "ok";
     case DVSSQ_EINVAL: return "invalid argument";
     case DVSSQ_EUNSUPPORTED: return "unsupported configuration";
     case DVSSQ_EHIP: return "HIP launch error";
+    case DVSSQ_STATUS_WAIT_TIMEOUT: return "a bounded wait gave up (outputs poisoned with NaN)";
     default: return "unknown status";
   }
 }

@@ -46,7 +46,6 @@ constexpr int kRed = 8;                 // partial-tile rows per lane in LDS (tw
 constexpr int kMaxRT = 7;               // largest number of 16-row tiles per workgroup
 constexpr int kUVec = kMaxRT * kTile * 64 * 2 / 16 / 64;  // 16-byte U loads per spare lane (r <= 64)
 constexpr int kRowVec = (kMaxRT * kTile + 63) / 64;         // column / INT8-scale loads per spare lane
-constexpr long kSpinLimit = 1L << 22;   // bounded wait for a producer flag
 constexpr int kLoadBatch = 16;          // device-scope loads issued together before their first use
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -263,7 +262,7 @@ __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
   }
   drain_stores();
   __syncthreads();
-  if (tid == 0) st_dev(a.flag + pidx, a.gen);
+  if (tid == 0 && a.publish) st_dev(a.flag + pidx, a.gen);
 }
 
 // --------------------------------------------------------------------------- consumer
@@ -339,7 +338,7 @@ __device__ void copy_planes(const DecodeArgs &a, int t0, int nt, int k0, int KW,
 // the compute wavefronts pass at the same points of their own path.
 template <bool T8>
 __device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows, int u0, int nu, u32x4 *ush,
-                      int *cols, float *s8s, float *ts) {
+                      int *cols, float *s8s, float *ts, int *tout) {
   const int lane = threadIdx.x & 63;
   const int M = a.M, nsp = a.nsr_pad;
   u32x4 uv[kUVec];
@@ -360,16 +359,25 @@ __device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows
     rv[j] = buf_load4(ri, ok ? static_cast<uint32_t>(wbase + e) * 4 : kOutOfRange);
     sv[j] = T8 ? buf_load4(rs8, ok ? static_cast<uint32_t>(wbase + e - a.n4) * 4 : kOutOfRange) : 0u;
   }
-  auto wait_flags = [&]() {   // every spare wavefront waits for every flag it depends on
+  // Every spare wavefront waits for every flag it depends on, each wait
+  // bounded by a.spin_limit polls; the first spare wavefront records in LDS
+  // whether any of its waits gave up (read by all after barrier B).
+  auto wait_flags = [&]() {
     const int nrg = (M + kProdRows - 1) / kProdRows;
+    bool late = false;
     for (int i = lane; i < nu * nrg; i += 64) {
       const int rg = i / nu, uu = i - rg * nu;
-      long spins = 0;
-      while (ld_dev(a.flag + rg * a.nunit + u0 + uu) != a.gen && spins < kSpinLimit) {
+      int spins = 0;
+      while (ld_dev(a.flag + rg * a.nunit + u0 + uu) != a.gen) {
+        if (++spins > a.spin_limit) {
+          late = true;
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
-        ++spins;
       }
     }
+    const bool any_late = __builtin_amdgcn_ballot_w64(late) != 0;
+    if (sw == 0 && lane == 0) *tout = any_late ? 1 : 0;
     __builtin_amdgcn_wave_barrier();
   };
   if (a.planes) {
@@ -435,10 +443,11 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   int *cols = reinterpret_cast<int *>(ush + kUVec * 64);           // [16 RT] output columns
   float *s8s = reinterpret_cast<float *>(cols + kMaxRT * kTile);   // [16 RT] INT8 row scales
   float *ts = s8s + kMaxRT * kTile;                                // [M][nsp]
+  int *tout = reinterpret_cast<int *>(ts + M * nsp);               // 1: a wait for the producers gave up
 
   if (wave >= NCW) {
     const int wrows = min(RT * kTile, (T8 ? a.n4 + a.n8 : a.n4) - wbase);
-    spare<T8>(a, wave - NCW, kWaves - NCW, wbase, wrows, u0, nu, ush, cols, s8s, ts);
+    spare<T8>(a, wave - NCW, kWaves - NCW, wbase, wrows, u0, nu, ush, cols, s8s, ts, tout);
     return;
   }
   const int tile = tile0 + rt;
@@ -681,7 +690,17 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
     }
   }
 
-  // ---- 7. output: direct, or split-K partials summed by the last arriver
+  // ---- 7. output: direct, or split-K partials summed by the last arriver.
+  // If a wait for the producers gave up, t and the planes may be stale: every
+  // output of this workgroup becomes NaN (a split-K sum with a NaN partial is
+  // NaN) and the workspace's status word records the timeout.
+  if (*tout) {
+    if (lane == 0) st_dev(a.status, DVSSQ_STATUS_WAIT_TIMEOUT);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < R; ++r) cacc[t][r] = __builtin_nanf("");
+  }
   const bool out_lane = row_ok && (MT != 1 || q == 0);
   if (a.S == 1) {
     if (!out_lane) return;
@@ -758,7 +777,7 @@ size_t consumer_lds(int M, int unit, int KW, int nsr_pad) {
   const size_t nu = KW / unit, ngrp = KW / kGroup;
   return static_cast<size_t>(2) * M * KW + ngrp * kTab * 4 + nu * kTab * 4 + static_cast<size_t>(kWaves) * kRed * 64 * 4 +
          static_cast<size_t>(kUVec) * 64 * 16 + 2 * kMaxRT * kTile * 4 +
-         static_cast<size_t>(M) * nsr_pad * 4;
+         static_cast<size_t>(M) * nsr_pad * 4 + 16;
 }
 
 size_t small_lds(int M, int unit, int KW, int nsr_pad) {

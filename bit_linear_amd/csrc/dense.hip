@@ -1,8 +1,9 @@
 // Dense materialization of a packed layer: the bf16 weight W = (W_hat + U V_seg) H^T
 // in the original input domain, rows in original output order, so that
-// x W^T is the layer's forward (MiniCPM5-2B-Hadamard-GSQ model card: usage
-// section, materializing the quantized MLP weights as plain BF16; the layer
-// itself: Mathematical Foundations 2, runtime equation).  H is symmetric, so
+// x W^T is the layer's forward (Spark-X2.5-4B-Hadamard-GSQ model card,
+// Quickstart & Inference Guide: materialize_weights() turns the quantized MLP
+// weights into plain BF16; the layer itself: MiniCPM5-2B-Hadamard-GSQ model
+// card, Mathematical Foundations 2, runtime equation).  H is symmetric, so
 // each Hadamard block of a rotated row is transformed by H_b again.
 //
 // One wavefront per (1 to 16 packed rows, Hadamard block): each lane dequantizes VPL

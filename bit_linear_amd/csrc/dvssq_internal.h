@@ -28,6 +28,13 @@ inline hipError_t launch_kernel(const void *fn, dim3 grid, dim3 block, size_t ld
   return hipLaunchKernel(fn, grid, block, args, lds, s);
 }
 
+// Launch of a kernel with plain parameters.
+template <typename... T>
+inline hipError_t launch_kernel_args(const void *fn, dim3 grid, dim3 block, size_t lds, hipStream_t s, T... v) {
+  void *args[] = {static_cast<void *>(&v)...};
+  return hipLaunchKernel(fn, grid, block, args, lds, s);
+}
+
 constexpr int kGroup = 64;      // INT4 group size
 constexpr int kDecodeRows = 32; // M rows held by the decode workspace (MFMA tile height)
 
@@ -102,9 +109,10 @@ __device__ __forceinline__ uint32_t pk_add(uint32_t a, uint32_t b) {
 // One dword of packed INT4 codes (byte j: code k+j low, k+j+4 high) -> 8 exact
 // f16 (n - 8) s in slots k+0,2,4,6,1,3,5,7.  Each nibble pair is moved to bits
 // 6-9 of the two halves; or-ed with 0x4C00
-// that is the f16 value 16 + n.  With s = m 2^E (m < 256), -24 s = -3m 2^(E+3)
-// has at most 10 significant bits and (n - 8) s at most 11, so the fused
-// fma(16 + n, s, -24 s) returns (n - 8) s exactly.
+// that is the f16 value 16 + n.  With s = m 2^E (m < 256, a bf16 value in
+// [2^-17, 2^11)), s, -24 s = -3m 2^(E+3) and (n - 8) s are multiples of 2^-24
+// with at most 10, 10 and 11 significant bits, so s and -24 s are exact f16
+// and the fused fma(16 + n, s, -24 s) returns (n - 8) s exactly.
 __device__ __forceinline__ u32x4 int4_to_f16(uint32_t w, uint32_t s2, uint32_t c24) {
   const uint32_t m = 0x03C003C0u, o = 0x4C004C00u;
   u32x4 r;
@@ -294,21 +302,25 @@ inline int64_t pf_rows(int M) { return (static_cast<int64_t>(M) + kPfTileM - 1) 
 constexpr int kMaxSplit = 16;   // largest decode split-K factor
 constexpr int kTSplitMax = 16;  // largest number of K-ranges of the prefill's t product
 
+// The first kStatusBytes of every workspace are its status area: the int32 at
+// offset 0 is set to DVSSQ_STATUS_WAIT_TIMEOUT by a kernel whose bounded wait
+// gave up (sticky: the library never clears it).
+constexpr int64_t kStatusBytes = 256;
+
 struct WsLayout {
   // decode
-  int64_t d_xq;    // f16 [32][K]: rotated x scaled by 2^-e per (row, unit), runs of 8 in order 0,2,4,6,1,3,5,7
-  int64_t d_sc;    // fp32 [nunit][32]: 2^e of each (unit, row)
+  int64_t d_xq;    // int8 planes [2][32][K]: x_rot quantized to X = 256 x1 + x2 per (row, unit)
   int64_t d_tp;    // fp32 [nunit][32][nsr_pad]: partial t = x_rot V^T of each unit
-  int64_t d_flag;  // u64 [nunit * 4]: generation stamp written by each producer
-  int64_t d_cnt;   // int32 [groups]: split-K arrivals per 16-row group
+  int64_t d_flag;  // u64 [nunit * 2]: generation stamp written by each producer
   int64_t d_part;  // fp32 [kMaxSplit][32][N]: split-K partial outputs
-  int64_t d_x8g;   // int32 [K/64][32]: 8 x (sum of the quantized x of a group) (small-M path)
-  int64_t d_escg;  // fp32 [nunit][32]: 2^e of each (unit, row) (small-M path)
-  int64_t d_cntw;  // u64 [groups]: tagged split-K arrival counters (small-M path)
+  int64_t d_x8g;   // int32 [K/64][32]: 8 x (sum of the quantized x of a group)
+  int64_t d_escg;  // fp32 [nunit][32]: 2^e of each (unit, row)
+  int64_t d_cntw;  // u64 [groups]: tagged split-K arrival counters
   int64_t d_end;
   // prefill
   int64_t p_xr;    // f16 x_rot tiles of [M_max rounded up to 128][K], scaled by 2^-e per row
   int64_t p_sc;    // fp32 [M_max] 2^e per row
+  int64_t p_rsh;   // fp32 [n_int4] 2^c per INT4 row: its group scales are used as s4 2^-c
   int64_t p_t;     // fp32 [M_max][nsr_pad] t = x_rot V^T
   int64_t p_tpart; // fp32 [kTSplitMax][M_max][nsr_pad] partial t of each K-range
   int64_t p_part;  // fp32 [ksplit][M][N] partial sums of a split GEMM (pf_part_bytes)
@@ -320,7 +332,7 @@ inline int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 inline int nsr_pad_of(int n_seg, int r) { return (n_seg * r + 31) / 32 * 32; }
 inline int decode_unit(int block) { return block > 256 ? block : 256; }
 inline int decode_groups(int n) { return (n + 15) / 16; }   // 16 packed rows per consumer group
-inline int decode_producers(int nunit, int M) { return nunit * ((M + 7) / 8); }
+inline int decode_producers(int nunit, int M) { return nunit * ((M + 15) / 16); }
 
 // Prefill K split: a GEMM of fewer tiles than kPfSplitTiles (half the compute
 // units of an MI355X) runs each tile as up to kPfSplitMax workgroups over
@@ -363,20 +375,19 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
   const int64_t K = L.K, N = L.N;
   const int nsp = nsr_pad_of(L.n_seg, L.r);
   const int64_t nunit = K / decode_unit(L.block);
-  int64_t cur = 0;
+  int64_t cur = kStatusBytes;
   w.d_xq = cur;   cur = align256(cur + 2 * kDecodeRows * K);
-  w.d_sc = cur;   cur = align256(cur + 4 * nunit * kDecodeRows);
   w.d_tp = cur;   cur = align256(cur + 4 * nunit * kDecodeRows * nsp);
   w.d_flag = cur; cur = align256(cur + 8 * decode_producers(nunit, kDecodeRows));
-  w.d_cnt = cur;  cur = align256(cur + 4 * (decode_groups(L.n_int4) + decode_groups(L.n_int8)));
   w.d_part = cur; cur = align256(cur + 4 * int64_t(kMaxSplit) * kDecodeRows * N);
   w.d_x8g = cur;  cur = align256(cur + 4 * (K / kGroup) * kDecodeRows);
   w.d_escg = cur; cur = align256(cur + 4 * nunit * kDecodeRows);
   w.d_cntw = cur; cur = align256(cur + 8 * (decode_groups(L.n_int4) + decode_groups(L.n_int8)));
   w.d_end = cur;
-  cur = 0;
+  cur = kStatusBytes;
   w.p_xr = cur;   cur = align256(cur + 2 * pf_rows(L.M_max) * K);
   w.p_sc = cur;   cur = align256(cur + 4 * static_cast<int64_t>(L.M_max));
+  w.p_rsh = cur;  cur = align256(cur + 4 * static_cast<int64_t>(L.n_int4));
   w.p_t = cur;    cur = align256(cur + 4 * static_cast<int64_t>(L.M_max) * nsp);
   w.p_tpart = cur; cur = align256(cur + 4 * kTSplitMax * static_cast<int64_t>(L.M_max) * nsp);
   w.p_part = cur; cur = align256(cur + pf_part_bytes(L));
@@ -399,6 +410,9 @@ struct PrologueArgs {
   float hscale;        // 1/sqrt(block)
   int exp_bias;        // prefill: row exponent = ilogb(max |x|) + exp_bias (log2 sqrt(block) if rotating, + 1 - 15)
   int fuse_scale;      // prefill with K == block >= 256: the rotation kernel finds the row exponents itself
+  const uint16_t *s4;  // prefill: bf16 [n4][K/64] INT4 group scales
+  float *rsh;          // prefill: fp32 [n4] 2^c per INT4 row (from its largest group scale)
+  int n4;              // prefill: INT4 rows
 };
 
 struct DecodeArgs {
@@ -412,21 +426,20 @@ struct DecodeArgs {
   const int32_t *idx;
   const uint16_t *x;   // bf16 [M][K]
   // workspace
-  uint16_t *xq;        // f16 [32][K]
-  float *sc;           // fp32 [nunit][32]
   float *tp;           // fp32 [nunit][32][nsr_pad]
   uint64_t *flag;      // [nprod]
-  int *cnt;            // [g4 + g8]
   float *part;         // fp32 [S][32][N]
-  int8_t *xg1, *xg2;   // small-M path: x_rot quantized to X = 256 x1 + x2, int8 planes [32][K]
-  int *x8g;            // small-M path: [K/64][32] 8 x sum of X over each group
-  float *escg;         // small-M path: [nunit][32] 2^e of each (unit, row)
-  uint64_t *cntw;      // tagged arrival counters [g4 + g8] (small-M path)
+  int8_t *xg1, *xg2;   // x_rot quantized to X = 256 x1 + x2, int8 planes [32][K]
+  int *x8g;            // [K/64][32] 8 x sum of X over each group
+  float *escg;         // [nunit][32] 2^e of each (unit, row)
+  uint64_t *cntw;      // tagged arrival counters [g4 + g8]
+  int *status;         // the workspace's status word
   uint16_t *y;         // bf16 [M][N]
   uint64_t gen;        // generation stamp of this call
-  uint32_t tag;        // 32-bit tag of this call (small-M path), never 0
+  uint32_t tag;        // 32-bit tag of this call, never 0
   int N, K, r, n_seg, n4, n8, M, block, unit, nunit, nprod, nsr, nsr_pad, S, KW, g4, g8, rotate;
-  int fused;           // 1: producers and consumers in one launch; 0: two launches
+  int publish;         // 1: producers publish their flags (0 only under DVSSQ_TEST_NO_PUBLISH)
+  int spin_limit;      // polls of a producer flag before the wait gives up
   int RT, MAXG;        // small-M path: 16-row tiles per workgroup, most groups per wavefront
   int KQ, GPW;         // small-M path: wavefronts per tile, groups per wavefront (even)
   int planes;          // small-M path: producers publish x_rot planes, consumers copy them (else rotate)
@@ -449,6 +462,7 @@ struct PrefillArgs {
   const float *t;      // fp32 [M][nsr_pad]
   uint16_t *y;         // bf16 [M][N]
   float *part;         // K split: fp32 [ksplit][M][N] partial sums per packed row
+  const float *rsh;    // fp32 [n4] 2^c per INT4 row (group scales enter the f16 weights as s4 2^-c)
   int N, K, r, n_seg, n4, n8, M, nsr, nsr_pad;
   int n4_tiles, n8_tiles, m_tiles;
   int ksplit, kspw;    // K-ranges per tile (1: no split) and GEMM steps per range
@@ -478,9 +492,6 @@ hipError_t launch_materialize(const DenseArgs &a, int block, hipStream_t s);
 hipError_t launch_geglu(const GegluArgs &a, hipStream_t s);
 hipError_t launch_fwht(const PrologueArgs &a, int block, hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, int cus, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
-size_t decode_lds_bytes(int M, int unit, int KW, int nsr_pad);
-int decode_max_spans();   // most 128-input spans one decode workgroup takes
 // small-M decode (M <= 4): int8 matrix cores, 16-wavefront workgroups
 struct SmallPlan {
   int RT;    // 16-row tiles per workgroup (1 .. 7)
@@ -494,5 +505,6 @@ bool plan_decode_small(const dvssq_layout &L, int M, int cus, SmallPlan *plan);
 int small_producers(int nunit, int M);   // t producers of the small-M kernel (one per unit and 16 rows)
 hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_stream_read(const void *buf, int64_t bytes, void *sink, hipStream_t s);
 
 }  // namespace dvssq

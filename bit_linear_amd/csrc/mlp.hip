@@ -2,7 +2,7 @@
 // (Spark-X2.5-4B GGUF page, "The model": a GELU feed-forward block; ASHQ1 page,
 // Architecture: ffn_gate, ffn_up and ffn_down).  gate and up are the two
 // segments of the fused layer's bf16 output [M][2I]; GELU is the exact
-// v Phi(v) = v (1 + erf(v / sqrt 2)) / 2; the product is rounded once to bf16,
+// v Phi(v) = v erfc(-v / sqrt 2) / 2; the product is rounded once to bf16,
 // the input of the down projection.
 #include "dvssq_internal.h"
 
@@ -12,7 +12,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float gelu(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+// v Phi(v) with Phi(v) = erfc(-v / sqrt 2) / 2: relatively accurate in the
+// negative tail, where 1 + erf(v / sqrt 2) would cancel
+__device__ __forceinline__ float gelu(float v) { return 0.5f * v * erfcf(v * -0.70710678118654752f); }
 
 // eight consecutive intermediate values per thread (I is a multiple of 64)
 __global__ __launch_bounds__(kThreads) void geglu_kernel(GegluArgs a) {

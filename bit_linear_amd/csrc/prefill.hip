@@ -2,9 +2,10 @@
 // (MiniCPM5-2B-Hadamard-GSQ model card, Mathematical Foundations 2, runtime
 // equation).  A tiled GEMM on the f16 matrix cores: x_rot tiles (f16, scaled
 // by a power of two per row, from the prologue) times weights dequantized in
-// registers as exact f16 values -- INT4 rows as (n - 8) s_g (same card, INT4
-// equation), INT8 rows as the code q, whose fp32 row scale (Spark-X2.5-4B-
-// Hadamard-GSQ model card, Tier A) is applied to the accumulator afterwards.
+// registers as exact f16 values -- INT4 rows as (n - 8) s_g 2^-c (same card,
+// INT4 equation; 2^c one power of two per row from the prologue, applied to
+// the accumulator afterwards), INT8 rows as the code q, whose fp32 row scale
+// (Spark-X2.5-4B-Hadamard-GSQ model card, Tier A) is applied likewise.
 // Both operands hold each run of 8 inputs in the order 0,2,4,6,1,3,5,7, which
 // leaves the K-reduction unchanged.  The epilogue undoes the row scale, then
 // adds the low-rank term as one bf16 MFMA slab of t (bf16) times the U rows.
@@ -87,12 +88,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0,
                             static_cast<uint32_t>(nrow * rb));
   const auto rs = make_rsrc(a.s4 + static_cast<int64_t>(tile0) * KGa, static_cast<uint32_t>(T8 ? 0 : nrow * KGa * 2));
   uint32_t oq[NF], os[NF];
+  // INT4 rows: 2^c of the row (prologue); group scales enter the f16 weights as s4 2^-c
+  float rsh[NF], rinv[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     const int rl = 64 * wave + 32 * j + fr;   // row inside the workgroup's tile
     const bool ok = rl < nrow;
     oq[j] = ok ? static_cast<uint32_t>(rl * rb + (T8 ? 32 : 16) * fh + (T8 ? 64 : 32) * s0) : kOutOfRange;
     os[j] = ok ? static_cast<uint32_t>((rl * KGa + s0) * 2) : kOutOfRange;
+    rsh[j] = T8 || !ok ? 1.0f : a.rsh[tile0 + rl];
+    rinv[j] = __uint_as_float((254u << 23) - __float_as_uint(rsh[j]));   // 2^-c
   }
 
   // x_rot tiles: a direct copy into LDS (each wavefront instruction fills 1 KB
@@ -158,7 +163,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0,
       if constexpr (T8) {
         return int8_to_f16(Q[bu][j][ks >> 1][2 * (ks & 1)], Q[bu][j][ks >> 1][2 * (ks & 1) + 1]);
       } else {
-        const float sc = bf16_to_f32(S[bu][j]);
+        const float sc = bf16_to_f32(S[bu][j]) * rinv[j];
         return int4_to_f16(Q[bu][j][0][ks], pack_f16x2(sc, sc), pack_f16x2(-24.0f * sc, -24.0f * sc));
       }
     };
@@ -242,7 +247,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs &a, uint16_t *A0,
     okj[j] = pl < rows;
     pj[j] = (T8 ? a.n4 : 0) + (okj[j] ? pl : 0);
     col[j] = a.idx[pj[j]];
-    s8[j] = T8 ? a.s8[okj[j] ? pl : 0] : 1.0f;
+    s8[j] = T8 ? a.s8[okj[j] ? pl : 0] : rsh[j];
   }
   const int seg_cols = a.N / a.n_seg;
   if (!lowrank) {

@@ -342,10 +342,39 @@ __global__ __launch_bounds__(kThreads) void treduce_kernel(PrologueArgs a, int n
   reinterpret_cast<f32x4 *>(a.t)[e] = s;
 }
 
+// INT4 row shifts of the prefill GEMM, one wavefront per packed INT4 row: the
+// GEMM enters group g of row p as the exact f16 values (n - 8) s4[p][g] 2^-c
+// and multiplies the row's fp32 result by 2^c.  c puts the row's largest
+// scale in [2^10, 2^11), so that every scale within 2^27 of it is an exact f16
+// of at least 2^-17 (whose multiples by n - 8 and -24 stay exact) and
+// (16 + n) s 2^-c stays below the f16 maximum.  An all-zero row keeps c = 0.
+__device__ void row_shift(const PrologueArgs &a, int p) {
+  const int lane = threadIdx.x & 63;
+  const int KG = a.K / kGroup;
+  const uint16_t *row = a.s4 + static_cast<int64_t>(p) * KG;
+  uint32_t mx = 0;
+  for (int g = lane; g < KG; g += 64) mx = max(mx, static_cast<uint32_t>(row[g]) & 0x7FFFu);
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), sft, 64)));
+  if (lane != 0) return;
+  int c = 0;
+  if (mx != 0) {
+    const int be = static_cast<int>(mx >> 7);          // biased exponent (0: subnormal)
+    c = max(-116, min(117, (be == 0 ? -126 : be - 127) - 10));
+  }
+  a.rsh[p] = __uint_as_float(static_cast<uint32_t>(127 + c) << 23);
+}
+
 // Per-row power-of-two scale 2^e of the f16 x_rot: from the bound
 // max |x H| <= sqrt(block) max |x|, e puts the scaled row below 2^15.  One
 // wavefront per row, its 16-byte chunks read with several loads in flight.
-__global__ __launch_bounds__(kThreads) void rowscale_kernel(PrologueArgs a) {
+// The blocks from row_blocks on compute the INT4 row shifts (row_shift).
+__global__ __launch_bounds__(kThreads) void rowscale_kernel(PrologueArgs a, int row_blocks) {
+  if (static_cast<int>(blockIdx.x) >= row_blocks) {
+    const int p = (blockIdx.x - row_blocks) * (kThreads / 64) + (threadIdx.x >> 6);
+    if (p < a.n4) row_shift(a, p);
+    return;
+  }
   const int lane = threadIdx.x & 63, m = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (m >= a.M) return;
   const u32x4 *row = reinterpret_cast<const u32x4 *>(a.x + static_cast<int64_t>(m) * a.K);
@@ -396,10 +425,16 @@ hipError_t launch_fwht(const PrologueArgs &a, int block, hipStream_t s) {
 hipError_t launch_prologue(const PrologueArgs &a, int block, int n_wg_blocks, int cus, hipStream_t s) {
   if (a.fuse_scale && (a.K != block || block < 256)) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
-  if (!a.fuse_scale) {
-    e = launch_kernel(reinterpret_cast<const void *>(rowscale_kernel),
-                      dim3((a.M + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, s, a);
-    if (e != hipSuccess) return e;
+  {
+    // row scales of x (unless the rotation finds them) and the INT4 row shifts
+    int row_blocks = a.fuse_scale ? 0 : (a.M + kThreads / 64 - 1) / (kThreads / 64);
+    const int shift_blocks = (a.n4 + kThreads / 64 - 1) / (kThreads / 64);
+    void *args[] = {const_cast<PrologueArgs *>(&a), &row_blocks};
+    if (row_blocks + shift_blocks > 0) {
+      e = hipLaunchKernel(reinterpret_cast<const void *>(rowscale_kernel), dim3(row_blocks + shift_blocks),
+                          dim3(kThreads), args, 0, s);
+      if (e != hipSuccess) return e;
+    }
   }
   switch (block) {
     case 64: e = launch_vpl<1, 32>(a, n_wg_blocks, s); break;

@@ -71,6 +71,20 @@ extern "C" {
 
 /* flags */
 #define DVSSQ_X_ROTATED 1u      /* x already holds x.H (bf16): skip the rotation */
+/* Test only, dvssq_linear_decode: the producers of t do not publish that they
+   are done, so every consumer's bounded wait for them gives up after a few
+   polls; the kernel then poisons its outputs and sets the status word (below).
+   Lets a test force the timeout path without making any kernel hang. */
+#define DVSSQ_TEST_NO_PUBLISH 0x80000000u
+
+/* Workspace status word: the int32 at byte offset 0 of every workspace.  A
+   kernel whose bounded wait for another workgroup gave up writes NaN (bf16
+   0x7FC0) into every output element it owns and stores
+   DVSSQ_STATUS_WAIT_TIMEOUT there.  The library never clears it; a caller that
+   wants to read it zeroes it once after allocating the workspace.  Bytes
+   1 .. DVSSQ_WS_STATUS_BYTES-1 are reserved. */
+#define DVSSQ_WS_STATUS_BYTES 256
+#define DVSSQ_STATUS_WAIT_TIMEOUT 1
 
 typedef struct dvssq_layout {
   int32_t N;        /* output features (all segments) */
@@ -110,22 +124,23 @@ int dvssq_pack_info(int32_t N, int32_t K, int32_t r, int32_t block, int32_t n_se
 int dvssq_fwht(const void *x, void *xrot, int32_t M, int32_t K, int32_t block, void *stream);
 
 /*
- * Decode forward (memory-bound GEMV path), 1 <= M <= min(32, L->M_max), one
- * kernel launch.  Needs K to be a multiple of max(block, 256)
- * (DVSSQ_EUNSUPPORTED otherwise).
+ * Decode forward (memory-bound GEMV path), 1 <= M <= min(32, L->M_max)
+ * (DVSSQ_EUNSUPPORTED above 32), normally one kernel launch.
  * L: from dvssq_pack_info.  blob: device, L->blob_bytes, 256-byte aligned.
  * x: device bf16 [M][K] (x.H when flags has DVSSQ_X_ROTATED).  y: device bf16
  * [M][N] in original column order; y must not overlap x, blob or ws.
  * ws: device workspace of L->ws_bytes, 256-byte aligned, contents need no
- * initialization; one ws must not be used by two calls in flight at once.
+ * initialization (see the status word above); one ws must not be used by two
+ * calls in flight at once.
  * Each (row, max(block, 256) inputs) of the rotated activations is held as a
  * 15-bit integer with a power-of-two scale and multiplied exactly against the
- * integer codes (int32 products, fp32 group sums); where that kernel's plan does
- * not fit (per-wavefront load count, LDS, 32-bit offsets) a second kernel holds
- * it in f16 with the same scales against exact f16 weights, which needs the
- * INT4 scales s4 to lie in [2^-14, 63].  No overflow for finite fp32 values.
+ * integer codes (int32 products), each group's scale applied in fp32, for any
+ * finite scales.  Where K is not a multiple of max(block, 256) or no plan of
+ * the single-launch kernel fits (LDS, per-wavefront load count, 32-bit
+ * offsets: large M with blocks of 1024 or 2048), the call runs the prefill
+ * path instead (dvssq_linear_prefill, same arguments).
  * x and y must be 16-byte aligned.  Accumulation is fp32; y is rounded once to
- * bf16 (nearest-even).
+ * bf16 (nearest-even).  flags: DVSSQ_X_ROTATED, DVSSQ_TEST_NO_PUBLISH.
  */
 int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, void *y,
                         int32_t M, void *ws, uint32_t flags, void *stream);
@@ -138,16 +153,21 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
  * their results).  Needs K <= 2^22,
  * M <= 2^22 and N r <= 2^29 (DVSSQ_EUNSUPPORTED otherwise).  Same arguments and ownership rules as
  * dvssq_linear_decode.  The rotated activations are held in f16 with one
- * power-of-two scale per row, the weights as exact f16 values (same s4 range
- * as decode), t = (x H) V^T in bf16 for the low-rank product; accumulation is
- * fp32.
+ * power-of-two scale per row, the weights as exact f16 values: INT8 codes as
+ * they are (the row scale applied in fp32), INT4 codes as (n - 8) s4 2^-c with
+ * one power of two 2^c per row taken from the row's largest group scale and
+ * applied in fp32, which is exact for every group scale within 2^-27 of the
+ * row's largest (a smaller one enters with an error below 2^-35 of the row's
+ * largest weight).  t = (x H) V^T is rounded to bf16 for the low-rank
+ * product; accumulation is fp32.  flags: DVSSQ_X_ROTATED.
  */
 int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x, void *y,
                          int32_t M, void *ws, uint32_t flags, void *stream);
 
 /*
- * Dense materialization of a packed layer (MiniCPM5-2B-Hadamard-GSQ model card,
- * usage section: the quantized MLP weights materialized as plain BF16):
+ * Dense materialization of a packed layer (Spark-X2.5-4B-Hadamard-GSQ model
+ * card, Quickstart & Inference Guide: materialize_weights() turns the quantized
+ * MLP weights into plain BF16):
  *     w[idx[p]][k] = bf16( sum_j (W_hat[p] + U[p] V_seg(p))[j] H[j][k] ),
  * the layer's weight in the original input domain (H symmetric, H^T = H), so
  * that x w^T is the layer's forward up to the bf16 rounding of w.
@@ -164,6 +184,16 @@ int dvssq_materialize(const dvssq_layout *L, const void *blob, void *w, void *st
  * dvssq_mlp_decode) or bytes is null.
  */
 int dvssq_mlp_ws_bytes(const dvssq_layout *gu, const dvssq_layout *down, int64_t *bytes);
+
+/*
+ * Where dvssq_mlp_decode / dvssq_mlp_prefill leave the block's intermediates
+ * in their workspace: after a call on M rows, bytes off_ygu .. hold the fused
+ * layer's output, bf16 [M][gu->N] (gate then up), and bytes off_h .. hold
+ * gelu(gate) * up, bf16 [M][down->K], the down projection's input.  Host-only;
+ * same pairing rules and errors as dvssq_mlp_ws_bytes; off_ygu and off_h must
+ * not be null.
+ */
+int dvssq_mlp_ws_offsets(const dvssq_layout *gu, const dvssq_layout *down, int64_t *off_ygu, int64_t *off_h);
 
 /*
  * Gated MLP block, decode form (Spark-X2.5-4B GGUF page, "The model": a GELU
@@ -202,6 +232,17 @@ int dvssq_mlp_decode(const dvssq_layout *gu, const void *gu_blob, const dvssq_la
 int dvssq_mlp_prefill(const dvssq_layout *gu, const void *gu_blob, const dvssq_layout *down,
                       const void *down_blob, const void *x, void *y, int32_t M, void *ws,
                       uint32_t flags, void *stream);
+
+/*
+ * Measurement aid, not part of the layer: one kernel that reads `bytes` bytes
+ * of the device buffer buf (16-byte aligned, bytes a multiple of 16) with a
+ * plain streaming pattern (contiguous 16 KB per 256-thread workgroup, 16-byte
+ * loads) and computes nothing, the achievable-bandwidth reference for a decode
+ * call that reads a layer of the same size.  sink: device, 4 bytes, written
+ * only for a contrived buffer content (keeps the loads alive).  1 <= bytes <=
+ * 2^40.  One kernel launch on `stream`.
+ */
+int dvssq_stream_read(const void *buf, int64_t bytes, void *sink, void *stream);
 
 /* Static text for a return code. */
 const char *dvssq_status_str(int status);

@@ -10,13 +10,6 @@ import oracle
 import synth
 
 TOL = 5e-3          # max|y_gpu - y_ref| / max|y_ref|
-# The gated MLP block applies two projections in sequence; each is held to TOL
-# of its own output scale.  The gate+up error reaches the down projection
-# through h = bf16(gelu(gate) up): a gate/up element's absolute error is scaled
-# by its partner factor, and a bf16 rounding of g, u or h that lands on the
-# other side of a tie moves that element by one bf16 unit (2^-8 relative).
-# The block is therefore held to twice the layer tolerance.
-TOL_BLOCK = 2 * TOL
 
 
 def all_layers():
@@ -99,3 +92,20 @@ def sample_columns(lay, blob, n_random: int = 96, seed: int = 1) -> np.ndarray:
     cols |= set(idx[L["N4"]:][:: max(1, n8 // 16)].tolist())    # INT8 rows
     cols |= set(idx[:L["N4"]][:: max(1, L["N4"] // 16)].tolist())  # INT4 rows
     return np.array(sorted(c for c in cols if 0 <= c < lay.N), dtype=np.int32)
+
+
+@functools.lru_cache(maxsize=None)
+def planted_blob(name: str, kind: str):
+    """(layer, blob, extra) of a planted variant of an oracle-quantized layer
+    (tests/planted.py): kind is lowrank, edge or scales; extra is the INT4 row
+    class array for scales, else None."""
+    import planted
+    lay, blob = quantized(name)
+    if kind == "lowrank":
+        return lay, planted.lowrank_only(blob, lay), None
+    if kind == "edge":
+        return lay, planted.edge_codes(blob, lay), None
+    if kind == "scales":
+        b, cls, _ = planted.scale_range(blob, lay)
+        return lay, b, cls
+    raise ValueError(kind)

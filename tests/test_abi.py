@@ -141,10 +141,19 @@ def test_decode_rejects_large_m():
     assert call("dvssq_linear_decode", L, M=33) == dv.DVSSQ_EUNSUPPORTED
 
 
-def test_decode_needs_k_multiple_of_unit():
-    # decode works on units of max(block, 256) inputs; prefill has no such limit
-    L = dv.pack_info(136, 192, 3, 64, 1, M_max=64)
-    assert call("dvssq_linear_decode", L, M=1) == dv.DVSSQ_EUNSUPPORTED
+def test_test_only_flag_is_decode_only():
+    # DVSSQ_TEST_NO_PUBLISH is a decode flag; the prefill refuses it before any HIP call
+    L = dv.pack_info(512, 256, 4, 256, 1, M_max=64)
+    assert call("dvssq_linear_prefill", L, M=40, flags=dv.DVSSQ_TEST_NO_PUBLISH) == dv.DVSSQ_EINVAL
+    assert call("dvssq_linear_decode", L, M=1, flags=dv.DVSSQ_TEST_NO_PUBLISH | 4) == dv.DVSSQ_EINVAL
+
+
+def test_workspace_keeps_its_status_area():
+    # the first DVSSQ_WS_STATUS_BYTES of a workspace are the status area, never
+    # part of the decode or prefill regions: ws_bytes covers it as well
+    for args in ((512, 256, 4, 256, 1, 1), (10240, 2560, 16, 256, 1, 32), (6144, 2048, 16, 2048, 1, 4096)):
+        L = dv.pack_info(*args)
+        assert L.ws_bytes > dv.DVSSQ_WS_STATUS_BYTES and L.ws_bytes % 256 == 0
 
 
 def test_fwht_error_paths():
@@ -161,7 +170,7 @@ def test_fwht_error_paths():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, 7):
+    for code in (0, -1, -2, -3, 7, dv.DVSSQ_STATUS_WAIT_TIMEOUT):
         assert isinstance(dv.status_str(code), str) and dv.status_str(code)
     assert dv.status_str(dv.DVSSQ_EINVAL) != dv.status_str(dv.DVSSQ_EHIP)
 
@@ -209,11 +218,7 @@ def test_mlp_decode_error_paths():
     assert c(y=X + 256) == E                                   # y overlaps x
     assert c(y=WS + 1024) == E                                 # y overlaps ws
     assert c(g=dn, d=gu) == E                                  # swapped pair
-    # both projections must be decodable (K a multiple of max(block, 256)):
-    # refused before anything is enqueued
-    g2 = dv.pack_info(384, 192, 4, 64, 2, M_max=64)
-    d2 = dv.pack_info(192, 192, 4, 64, 1, M_max=64)
-    assert c(g=g2, d=d2) == dv.DVSSQ_EUNSUPPORTED
+    assert c(flags=dv.DVSSQ_TEST_NO_PUBLISH) == E              # test flag of the layer call only
 
 
 def test_mlp_prefill_error_paths():
@@ -241,3 +246,12 @@ def test_materialize_error_paths():
     bad = dv.pack_info(512, 256, 4, 256, 1, M_max=8)
     bad.off_U += 256
     assert f(C.byref(bad), BLOB, Y, None) == E
+
+
+def test_stream_read_error_paths():
+    f, E = dv.lib().dvssq_stream_read, dv.DVSSQ_EINVAL
+    assert f(None, 1024, Y, None) == E
+    assert f(X, 1024, None, None) == E
+    assert f(X, 0, Y, None) == E and f(X, 1000, Y, None) == E     # size: positive multiple of 16
+    assert f(X + 8, 1024, Y, None) == E                           # buffer alignment
+    assert f(X, 1 << 41, Y, None) == E

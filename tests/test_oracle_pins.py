@@ -531,3 +531,44 @@ def test_materialize_two_segments():
     x = synth.activations_bf16(4, "seg2m", 3, lay.K)
     y = oracle.forward(blob, lay.N, lay.K, lay.r, lay.block, 2, x)
     assert np.abs(y - synth.bf16_bits_to_f64(x) @ Wm.T).max() <= 1e-12 * np.abs(y).max()
+
+
+# ------------------------------------------------------------------ randomized SVD inside the quantizer
+
+@pytest.mark.parametrize("power_iters", [2, 6])
+def test_quantizer_randomized_svd_two_segments(power_iters):
+    """The quantizer's randomized-SVD branch (the one every full-size layer
+    takes: subspace iteration on a per-segment sketch, then Jacobi) on a
+    two-segment layer of 1024 rows per segment, r = 8.  For each segment s,
+    with R_s = W_rot - W_hat rebuilt here from the weights and the unpacked codes:
+    * the quantizer's ||R_s|| is that residual's norm;
+    * its stored factors are those of svd_lowrank(R_s, sketch of segment s),
+      placed at the segment's packed rows (the wiring of segment, sketch and rows);
+    * the residual shrinks strictly, with fp64 and with the stored bf16 factors;
+    * it is never below the optimum sqrt(sum_{i>r} sigma_i^2) (numpy's SVD), and
+      the energy the factors remove is at least half of the optimum's."""
+    lay = synth.Layer("svd_pin", N=2 * 1024, K=512, block=256, r=8, n_seg=2, n_outlier=5, outlier_tag="svd_pin")
+    W = synth.weights_bf16(0, lay)
+    l = lay.r + 8
+    omega = np.stack([synth.sketch(0, lay, s, l) for s in range(2)])
+    blob, diag = oracle.quantize(W, lay.r, lay.block, 2, omega=omega, power_iters=power_iters, want_diag=True)
+    idx, What, U, V = oracle.unpack(blob, lay.N, lay.K, lay.r, 2)
+    Wrot = oracle.fwht_rows(synth.bf16_bits_to_f64(W), lay.block)
+    Ns = lay.N // 2
+    for s in range(2):
+        rows = np.nonzero(idx // Ns == s)[0]            # packed rows of segment s, in packed order
+        order = np.argsort(idx[rows])                   # -> original row order of the segment
+        prow = rows[order]
+        R = Wrot[idx[prow]] - What[prow]
+        fr = np.linalg.norm(R)
+        assert abs(diag[s, 0] - fr) <= 1e-12 * fr
+        A, B, _ = oracle.svd_lowrank(R, lay.r, omega[s], power_iters)
+        np.testing.assert_array_equal(U[prow], synth.bf16_bits_to_f64(oracle.bf16_round_bits(A)))
+        np.testing.assert_array_equal(V[s * lay.r:(s + 1) * lay.r], synth.bf16_bits_to_f64(oracle.bf16_round_bits(B)))
+        f64, fbf = diag[s, 1], diag[s, 2]
+        assert f64 < fr and fbf < fr
+        assert abs(np.linalg.norm(R - U[prow] @ V[s * lay.r:(s + 1) * lay.r]) - fbf) <= 1e-9 * fr
+        sv = np.linalg.svd(R, compute_uv=False)
+        opt = np.sqrt((sv[lay.r:] ** 2).sum())
+        assert f64 >= opt * (1 - 1e-12)
+        assert fr ** 2 - f64 ** 2 >= 0.5 * (fr ** 2 - opt ** 2)
