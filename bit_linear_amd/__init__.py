@@ -30,7 +30,7 @@ DECODE_MAX_M = 32
 
 EXPORTS = ("dvssq_pack_info", "dvssq_fwht", "dvssq_linear_decode", "dvssq_linear_prefill",
            "dvssq_materialize", "dvssq_mlp_ws_bytes", "dvssq_mlp_ws_offsets", "dvssq_mlp_decode",
-           "dvssq_mlp_prefill", "dvssq_stream_read", "dvssq_status_str")
+           "dvssq_mlp_prefill", "dvssq_stream_read", "dvssq_linear_decode_noalloc", "dvssq_status_str")
 
 
 class Layout(C.Structure):
@@ -71,6 +71,8 @@ _lib.dvssq_fwht.argtypes = [_P, _P, C.c_int32, C.c_int32, C.c_int32, _P]
 for _n in ("dvssq_linear_decode", "dvssq_linear_prefill"):
     getattr(_lib, _n).restype = C.c_int
     getattr(_lib, _n).argtypes = [C.POINTER(Layout), _P, _P, _P, C.c_int32, _P, C.c_uint32, _P]
+_lib.dvssq_linear_decode_noalloc.restype = C.c_int
+_lib.dvssq_linear_decode_noalloc.argtypes = [C.POINTER(Layout), _P, _P, _P, C.c_int32, C.c_uint32, _P]
 _lib.dvssq_materialize.restype = C.c_int
 _lib.dvssq_materialize.argtypes = [C.POINTER(Layout), _P, _P, _P]
 _lib.dvssq_mlp_ws_bytes.restype = C.c_int
@@ -136,6 +138,11 @@ def linear_decode(layout: Layout, blob, x, y, M: int, ws, flags: int = 0, stream
 def linear_prefill(layout: Layout, blob, x, y, M: int, ws, flags: int = 0, stream=None) -> None:
     _check(_lib.dvssq_linear_prefill(C.byref(layout), _ptr(blob), _ptr(x), _ptr(y), M, _ptr(ws),
                                      flags, _stream(stream)), "dvssq_linear_prefill")
+
+
+def linear_decode_noalloc(layout: Layout, blob, x, y, M: int, flags: int = 0, stream=None) -> None:
+    _check(_lib.dvssq_linear_decode_noalloc(C.byref(layout), _ptr(blob), _ptr(x), _ptr(y), M, flags,
+                                            _stream(stream)), "dvssq_linear_decode_noalloc")
 
 
 def materialize(layout: Layout, blob, w, stream=None) -> None:

@@ -188,21 +188,40 @@ static bool decode_single_launch(const dvssq_layout &L, int32_t M, SmallPlan *sp
 }
 
 static int prefill_supported(const dvssq_layout &L, int32_t M);
-static int prefill_launch(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M, void *ws,
-                          uint32_t flags, hipStream_t s);
+static int prefill_launch(const dvssq_layout *L, const WsLayout &W, const void *blob, const void *x, void *y,
+                          int32_t M, void *ws, uint32_t flags, hipStream_t s);
 
-int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M,
-                        void *ws, uint32_t flags, void *stream) {
-  int rc = check_call(L, blob, x, y, M, ws, DVSSQ_DECODE_MAX_M);
+}  // extern "C"
+
+namespace dvssq {
+
+int decode_check_args(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M, uint32_t flags) {
+  int rc = check_layout(L);
   if (rc != DVSSQ_OK) return rc;
+  if (!blob || !x || !y) return DVSSQ_EINVAL;
+  if (M < 1 || M > L->M_max) return DVSSQ_EINVAL;
+  if (M > DVSSQ_DECODE_MAX_M) return DVSSQ_EUNSUPPORTED;
+  if (!aligned(blob, 256) || !aligned(x, 16) || !aligned(y, 16)) return DVSSQ_EINVAL;
+  const size_t xb = static_cast<size_t>(M) * L->K * 2, yb = static_cast<size_t>(M) * L->N * 2;
+  if (overlap(x, xb, y, yb) || overlap(y, yb, blob, L->blob_bytes)) return DVSSQ_EINVAL;
   if (flags & ~(DVSSQ_X_ROTATED | DVSSQ_TEST_NO_PUBLISH)) return DVSSQ_EINVAL;
   SmallPlan sp{};
+  if (!decode_single_launch(*L, M, &sp)) return prefill_supported(*L, M);
+  return DVSSQ_OK;
+}
+
+int decode_dispatch(const dvssq_layout &Lr, const WsLayout &W, const void *blob, const void *x, void *y, int32_t M,
+                    void *ws, uint32_t flags, hipStream_t s, int64_t *ws_need, bool dry_run) {
+  const dvssq_layout *L = &Lr;
+  SmallPlan sp{};
   if (!decode_single_launch(*L, M, &sp)) {
-    if ((rc = prefill_supported(*L, M)) != DVSSQ_OK) return rc;
-    return prefill_launch(L, blob, x, y, M, ws, flags & DVSSQ_X_ROTATED, static_cast<hipStream_t>(stream));
+    if (ws_need) *ws_need = W.p_end;
+    if (dry_run) return DVSSQ_OK;
+    return prefill_launch(L, W, blob, x, y, M, ws, flags & DVSSQ_X_ROTATED, s);
   }
+  if (ws_need) *ws_need = sp.S > 1 ? W.d_part + 4 * int64_t(sp.S) * kDecodeRows * L->N : W.d_part;
+  if (dry_run) return DVSSQ_OK;
   const int g4 = decode_groups(L->n_int4), g8 = decode_groups(L->n_int8);
-  const WsLayout W = ws_layout(*L);
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   const Blob B{static_cast<const uint8_t *>(blob), L};
   DecodeArgs d{};
@@ -264,8 +283,21 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
   d.publish = (flags & DVSSQ_TEST_NO_PUBLISH) ? 0 : 1;
   d.spin_limit = (flags & DVSSQ_TEST_NO_PUBLISH) ? kTestSpinLimit : kSpinLimit;
   d.hscale = inv_sqrt_block(L->block);
-  const hipError_t e = launch_decode_small(d, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_decode_small(d, s);
   return e == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
+}
+
+}  // namespace dvssq
+
+extern "C" {
+
+int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M,
+                        void *ws, uint32_t flags, void *stream) {
+  int rc = check_call(L, blob, x, y, M, ws, DVSSQ_DECODE_MAX_M);
+  if (rc != DVSSQ_OK) return rc;
+  if ((rc = decode_check_args(L, blob, x, y, M, flags)) != DVSSQ_OK) return rc;
+  return decode_dispatch(*L, ws_layout(*L), blob, x, y, M, ws, flags, static_cast<hipStream_t>(stream), nullptr,
+                         false);
 }
 
 // the prefill's own limits (32-bit offsets in the GEMM)
@@ -281,13 +313,13 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
   if (flags & ~DVSSQ_X_ROTATED) return DVSSQ_EINVAL;
   // the GEMM addresses one workgroup's weight rows, t and U with 32-bit byte offsets
   if ((rc = prefill_supported(*L, M)) != DVSSQ_OK) return rc;
-  return prefill_launch(L, blob, x, y, M, ws, flags, static_cast<hipStream_t>(stream));
+  return prefill_launch(L, ws_layout(*L), blob, x, y, M, ws, flags, static_cast<hipStream_t>(stream));
 }
 
-// The prefill's launches, after every argument check has passed.
-static int prefill_launch(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M, void *ws,
-                          uint32_t flags, hipStream_t s) {
-  const WsLayout W = ws_layout(*L);
+// The prefill's launches, after every argument check has passed, with the
+// workspace regions of W.
+static int prefill_launch(const dvssq_layout *L, const WsLayout &W, const void *blob, const void *x, void *y,
+                          int32_t M, void *ws, uint32_t flags, hipStream_t s) {
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   const Blob B{static_cast<const uint8_t *>(blob), L};
   const int nsp = nsr_pad_of(L->n_seg, L->r);

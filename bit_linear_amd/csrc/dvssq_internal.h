@@ -312,10 +312,10 @@ struct WsLayout {
   int64_t d_xq;    // int8 planes [2][32][K]: x_rot quantized to X = 256 x1 + x2 per (row, unit)
   int64_t d_tp;    // fp32 [nunit][32][nsr_pad]: partial t = x_rot V^T of each unit
   int64_t d_flag;  // u64 [nunit * 2]: generation stamp written by each producer
-  int64_t d_part;  // fp32 [kMaxSplit][32][N]: split-K partial outputs
   int64_t d_x8g;   // int32 [K/64][32]: 8 x (sum of the quantized x of a group)
   int64_t d_escg;  // fp32 [nunit][32]: 2^e of each (unit, row)
   int64_t d_cntw;  // u64 [groups]: tagged split-K arrival counters
+  int64_t d_part;  // fp32 [S][32][N]: split-K partial outputs (last: a call uses S <= kMaxSplit planes)
   int64_t d_end;
   // prefill
   int64_t p_xr;    // f16 x_rot tiles of [M_max rounded up to 128][K], scaled by 2^-e per row
@@ -379,10 +379,10 @@ inline WsLayout ws_layout(const dvssq_layout &L) {
   w.d_xq = cur;   cur = align256(cur + 2 * kDecodeRows * K);
   w.d_tp = cur;   cur = align256(cur + 4 * nunit * kDecodeRows * nsp);
   w.d_flag = cur; cur = align256(cur + 8 * decode_producers(nunit, kDecodeRows));
-  w.d_part = cur; cur = align256(cur + 4 * int64_t(kMaxSplit) * kDecodeRows * N);
   w.d_x8g = cur;  cur = align256(cur + 4 * (K / kGroup) * kDecodeRows);
   w.d_escg = cur; cur = align256(cur + 4 * nunit * kDecodeRows);
   w.d_cntw = cur; cur = align256(cur + 8 * (decode_groups(L.n_int4) + decode_groups(L.n_int8)));
+  w.d_part = cur; cur = align256(cur + 4 * int64_t(kMaxSplit) * kDecodeRows * N);
   w.d_end = cur;
   cur = kStatusBytes;
   w.p_xr = cur;   cur = align256(cur + 2 * pf_rows(L.M_max) * K);
@@ -506,5 +506,14 @@ int small_producers(int nunit, int M);   // t producers of the small-M kernel (o
 hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_stream_read(const void *buf, int64_t bytes, void *sink, hipStream_t s);
+
+// Decode call after its argument checks (check_call): the single-launch kernel
+// or the prefill route, with the workspace regions of W.  *ws_need (if not
+// null) receives the bytes of ws the call touches; with dry_run nothing is
+// launched.
+int decode_dispatch(const dvssq_layout &L, const WsLayout &W, const void *blob, const void *x, void *y, int32_t M,
+                    void *ws, uint32_t flags, hipStream_t s, int64_t *ws_need, bool dry_run);
+// argument checks of dvssq_linear_decode except the workspace pointer
+int decode_check_args(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M, uint32_t flags);
 
 }  // namespace dvssq

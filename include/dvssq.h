@@ -146,6 +146,26 @@ int dvssq_linear_decode(const dvssq_layout *L, const void *blob, const void *x, 
                         int32_t M, void *ws, uint32_t flags, void *stream);
 
 /*
+ * Decode forward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The same computation, kernels and arguments as
+ * dvssq_linear_decode, except that the workspace is a scratch array of
+ * DVSSQ_NOALLOC_SCRATCH_BYTES that the library holds in device memory on each
+ * GPU it runs on, from the first call on that GPU until the process ends; the
+ * call itself allocates nothing.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (different streams, or other
+ * threads) race and must not be made.  Nothing in the array needs to start at
+ * zero.  DVSSQ_EUNSUPPORTED when the call needs more scratch than the array
+ * holds (large N with a split-K plan at large M; decode shapes that take the
+ * prefill route with very large K); DVSSQ_EHIP when the array's device address
+ * cannot be obtained.  A wait that gives up poisons the outputs with NaN as in
+ * dvssq_linear_decode (the status word is not visible to the caller here).
+ */
+#define DVSSQ_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int dvssq_linear_decode_noalloc(const dvssq_layout *L, const void *blob, const void *x, void *y,
+                                int32_t M, uint32_t flags, void *stream);
+
+/*
  * Prefill forward (MFMA GEMM path), 1 <= M <= L->M_max: three to six kernel
  * launches (per-row scales, unless K == block >= 256, where the rotation finds
  * them; rotation; t and, when t is split over K-ranges, their ordered sum; the

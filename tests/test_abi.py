@@ -255,3 +255,24 @@ def test_stream_read_error_paths():
     assert f(X, 0, Y, None) == E and f(X, 1000, Y, None) == E     # size: positive multiple of 16
     assert f(X + 8, 1024, Y, None) == E                           # buffer alignment
     assert f(X, 1 << 41, Y, None) == E
+
+
+def test_decode_noalloc_error_paths():
+    """The no-allocation decode checks its arguments like dvssq_linear_decode
+    (there is no workspace argument), all before any HIP launch."""
+    f = dv.lib().dvssq_linear_decode_noalloc
+    L = dv.pack_info(512, 256, 4, 256, 1, M_max=64)
+    E = dv.DVSSQ_EINVAL
+
+    def c(L=L, blob=BLOB, x=X, y=Y, M=1, flags=0):
+        return f(C.byref(L) if L is not None else None, blob, x, y, M, flags, None)
+
+    assert c(L=None) == E and c(blob=None) == E and c(x=None) == E and c(y=None) == E
+    assert c(M=0) == E and c(M=65) == E
+    assert c(M=33) == dv.DVSSQ_EUNSUPPORTED
+    assert c(flags=2) == E
+    assert c(blob=BLOB + 16) == E and c(x=X + 2) == E and c(y=Y + 8) == E
+    assert c(y=X + 256) == E                                   # y overlaps x
+    bad = dv.pack_info(512, 256, 4, 256, 1, M_max=64)
+    bad.off_U += 256
+    assert c(L=bad) == E
