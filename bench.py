@@ -38,7 +38,7 @@ METRIC = "effective weight GB/s (M=1 decode) and TFLOP/s (M=2048 prefill), % of 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_spark_up_m1_traffic.json")
-KERNEL_SOURCES = ("decode_small.hip", "dvssq_internal.h", "api.hip")
+KERNEL_SOURCES = ("decode_gemv.hip", "decode_small.hip", "dvssq_internal.h", "api.hip")
 
 
 def parse():
@@ -324,7 +324,7 @@ def main():
                    "packed_bytes": head.L.algo_bytes, "blob_copies": head.C, "wall_s": round(wall, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(),
-                     "kernel": "decode_small_kernel", "algo_bytes_per_launch": head.algo_bytes(),
+                     "kernel": "gemv_kernel", "algo_bytes_per_launch": head.algo_bytes(),
                      "us_per_launch": round(ms * 1e3, 3)},
     }
     head_blob, head_x = head.blob, head.x_bits

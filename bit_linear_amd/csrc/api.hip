@@ -210,9 +210,65 @@ int decode_check_args(const dvssq_layout *L, const void *blob, const void *x, vo
   return DVSSQ_OK;
 }
 
+// the few-token kernel (gemv_kernel), after the checks: one launch
+static int gemv_launch(const dvssq_layout &L, const WsLayout &W, const GemvPlan &gp, const void *blob, const void *x,
+                       void *y, int32_t M, void *ws, uint32_t flags, hipStream_t s) {
+  uint8_t *wsb = static_cast<uint8_t *>(ws);
+  const Blob B{static_cast<const uint8_t *>(blob), &L};
+  GemvArgs g{};
+  g.q4 = B.q4();
+  g.s4 = B.s4();
+  g.q8 = B.q8();
+  g.s8 = B.s8();
+  g.U = B.U();
+  g.V = B.V();
+  g.idx = B.idx();
+  g.x = static_cast<const uint16_t *>(x);
+  g.y = static_cast<uint16_t *>(y);
+  g.tp = reinterpret_cast<uint64_t *>(wsb + W.d_tp);
+  g.part = reinterpret_cast<float *>(wsb + W.d_part);
+  g.cnt = reinterpret_cast<uint64_t *>(wsb + W.d_cntw);
+  g.status = reinterpret_cast<int *>(wsb);
+  const uint64_t gen = next_generation();
+  g.stamp = static_cast<uint32_t>(gen ^ (gen >> 32));
+  if (g.stamp == 0) g.stamp = 1;
+  g.N = L.N;
+  g.K = L.K;
+  g.r = L.r;
+  g.n_seg = L.n_seg;
+  g.n4 = L.n_int4;
+  g.n8 = L.n_int8;
+  g.M = M;
+  g.block = L.block;
+  g.unit = decode_unit(L.block);
+  g.nunit = L.K / g.unit;
+  g.nsr = L.n_seg * L.r;
+  g.nsr_pad = nsr_pad_of(L.n_seg, L.r);
+  g.S = gp.S;
+  g.KW = L.K / gp.S;
+  g.nu_w = g.nunit / gp.S;
+  g.W = gp.W;
+  g.GPW = gp.GPW;
+  g.t4 = (L.n_int4 + 31) / 32;
+  g.t8 = (L.n_int8 + 31) / 32;
+  g.nprod = g.nunit;
+  g.local_rot = gp.local_rot;
+  g.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
+  g.publish = (flags & DVSSQ_TEST_NO_PUBLISH) ? 0 : 1;
+  g.spin_limit = (flags & DVSSQ_TEST_NO_PUBLISH) ? kTestSpinLimit : kSpinLimit;
+  g.hscale = inv_sqrt_block(L.block);
+  return launch_gemv(g, s) == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
+}
+
 int decode_dispatch(const dvssq_layout &Lr, const WsLayout &W, const void *blob, const void *x, void *y, int32_t M,
                     void *ws, uint32_t flags, hipStream_t s, int64_t *ws_need, bool dry_run) {
   const dvssq_layout *L = &Lr;
+  GemvPlan gp{};
+  if (M <= kGemvMaxM && L->K % decode_unit(L->block) == 0 && plan_gemv(*L, M, compute_units(), &gp)) {
+    if (ws_need) *ws_need = gp.S > 1 ? W.d_part + 4 * int64_t(gp.S) * M * L->N : W.d_part;
+    if (dry_run) return DVSSQ_OK;
+    return gemv_launch(*L, W, gp, blob, x, y, M, ws, flags, s);
+  }
   SmallPlan sp{};
   if (!decode_single_launch(*L, M, &sp)) {
     if (ws_need) *ws_need = W.p_end;

@@ -48,35 +48,6 @@ constexpr int kUVec = kMaxRT * kTile * 64 * 2 / 16 / 64;  // 16-byte U loads per
 constexpr int kRowVec = (kMaxRT * kTile + 63) / 64;         // column / INT8-scale loads per spare lane
 constexpr int kLoadBatch = 16;          // device-scope loads issued together before their first use
 
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void st_dev(uint64_t *p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ void st_dev(T *p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_dev(const T *p) {
-  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ u32x4 ld_dev16(const void *p) {
-  const uint64_t *q = static_cast<const uint64_t *>(p);
-  const uint64_t lo = ld_dev(q), hi = ld_dev(q + 1);
-  u32x4 r;
-  r[0] = static_cast<uint32_t>(lo);
-  r[1] = static_cast<uint32_t>(lo >> 32);
-  r[2] = static_cast<uint32_t>(hi);
-  r[3] = static_cast<uint32_t>(hi >> 32);
-  return r;
-}
-// wait until every store this thread issued has completed
-__device__ __forceinline__ void drain_stores() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // Groups of 64 inputs per wavefront when KQ wavefronts split ngrp groups: an
 // even number, so that every wavefront's first group is even and its group
@@ -87,33 +58,6 @@ __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0,
                                                0);
 }
-// cross-lane steps on the DPP network (rows of 16 lanes): xor 1, xor 2 inside
-// a quad, mirror inside 8 and inside 16 lanes
-#define DVSSQ_DPP(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), (ctrl), 0xF, 0xF, false)
-__device__ __forceinline__ float wave_max(float v) {
-  int b = __float_as_int(v);
-  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0xB1))));
-  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0x4E))));
-  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0x141))));
-  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0x140))));
-  const float m0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
-  const float m1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
-  const float m2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
-  const float m3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
-  return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
-}
-__device__ __forceinline__ int quad_sum(int v) {
-  v += DVSSQ_DPP(v, 0xB1);
-  v += DVSSQ_DPP(v, 0x4E);
-  return v;
-}
-// four bytes (the low byte of each value) in one dword, v0 lowest
-__device__ __forceinline__ uint32_t pack_bytes(int v0, int v1, int v2, int v3) {
-  const uint32_t lo = __builtin_amdgcn_perm(static_cast<uint32_t>(v1), static_cast<uint32_t>(v0), 0x0C0C0400u);
-  const uint32_t hi = __builtin_amdgcn_perm(static_cast<uint32_t>(v3), static_cast<uint32_t>(v2), 0x0C0C0400u);
-  return lo | (hi << 16);
-}
-
 // Rotation of one (row, unit) item by one wavefront (rotate_blocks), or the
 // plain bf16 values when x already holds x H.
 template <int C>
@@ -129,37 +73,6 @@ __device__ __forceinline__ void rotate_item(const DecodeArgs &a, const u32x2 (&x
     return;
   }
   rotate_blocks<C>(xw, y, a.block, a.hscale);
-}
-
-// 15-bit quantization of one rotated (row, unit) item held by a wavefront:
-// max |X| in [2^13, 2^14] with X = rint(x_rot 2^-e); X = 256 x1 + x2 with x2
-// the signed low byte.  Returns e; p1 / p2 get the lane's four x1 / x2 bytes of
-// each 256-block and gsum 8 x the sum of X over the lane's group of 64 inputs
-// (the same in the 16 lanes of that group).
-template <int C>
-__device__ __forceinline__ int quantize_item(const float (&y)[C][4], uint32_t (&p1)[C], uint32_t (&p2)[C],
-                                             int (&gsum)[C]) {
-  float mx = 0.0f;
-#pragma unroll
-  for (int c = 0; c < C; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(y[c][j]));
-  mx = wave_max(mx);
-  const int e = (mx > 0.0f && mx <= 3.0e38f) ? max(-100, min(114, ilogbf(mx) - 13)) : 0;
-  const float down = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    int X[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) X[j] = __float2int_rn(y[c][j] * down);
-    p1[c] = pack_bytes((X[0] + 128) >> 8, (X[1] + 128) >> 8, (X[2] + 128) >> 8, (X[3] + 128) >> 8);
-    p2[c] = pack_bytes(X[0], X[1], X[2], X[3]);
-    int g = quad_sum(X[0] + X[1] + X[2] + X[3]);
-    g += __shfl_xor(g, 16, 64);
-    g += __shfl_xor(g, 32, 64);
-    gsum[c] = 8 * g;
-  }
-  return e;
 }
 
 // --------------------------------------------------------------------------- producer

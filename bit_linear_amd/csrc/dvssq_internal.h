@@ -225,6 +225,113 @@ __device__ __forceinline__ void rotate_blocks(const u32x2 (&xw)[C], float (&y)[C
     for (int j = 0; j < 4; ++j) y[c][j] *= hscale;
 }
 
+// ------------------------------------------------------------------ decode helpers
+// device-scope (agent) relaxed stores and loads: visible to every workgroup
+__device__ __forceinline__ void st_dev(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 ld_dev16(const void *p) {
+  const uint64_t *q = static_cast<const uint64_t *>(p);
+  const uint64_t lo = ld_dev(q), hi = ld_dev(q + 1);
+  u32x4 r;
+  r[0] = static_cast<uint32_t>(lo);
+  r[1] = static_cast<uint32_t>(lo >> 32);
+  r[2] = static_cast<uint32_t>(hi);
+  r[3] = static_cast<uint32_t>(hi >> 32);
+  return r;
+}
+// wait until every store this thread issued has completed
+__device__ __forceinline__ void drain_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// cross-lane steps on the DPP network (rows of 16 lanes): xor 1, xor 2 inside
+// a quad, mirror inside 8 and inside 16 lanes
+#define DVSSQ_DPP(v, ctrl) __builtin_amdgcn_update_dpp(0, (v), (ctrl), 0xF, 0xF, false)
+__device__ __forceinline__ float wave_max(float v) {
+  int b = __float_as_int(v);
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0xB1))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0x4E))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0x141))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(DVSSQ_DPP(b, 0x140))));
+  const float m0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float m1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float m2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float m3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+}
+__device__ __forceinline__ int quad_sum(int v) {
+  v += DVSSQ_DPP(v, 0xB1);
+  v += DVSSQ_DPP(v, 0x4E);
+  return v;
+}
+// four bytes (the low byte of each value) in one dword, v0 lowest
+__device__ __forceinline__ uint32_t pack_bytes(int v0, int v1, int v2, int v3) {
+  const uint32_t lo = __builtin_amdgcn_perm(static_cast<uint32_t>(v1), static_cast<uint32_t>(v0), 0x0C0C0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(static_cast<uint32_t>(v3), static_cast<uint32_t>(v2), 0x0C0C0400u);
+  return lo | (hi << 16);
+}
+
+// 15-bit quantization of one rotated (row, unit) item held by a wavefront:
+// max |X| in [2^13, 2^14] with X = rint(x_rot 2^-e); X = 256 x1 + x2 with x2
+// the signed low byte.  Returns e; p1 / p2 get the lane's four x1 / x2 bytes of
+// each 256-block and gsum 8 x the sum of X over the lane's group of 64 inputs
+// (the same in the 16 lanes of that group).
+template <int C>
+__device__ __forceinline__ int quantize_item(const float (&y)[C][4], uint32_t (&p1)[C], uint32_t (&p2)[C],
+                                             int (&gsum)[C]) {
+  float mx = 0.0f;
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(y[c][j]));
+  mx = wave_max(mx);
+  const int e = (mx > 0.0f && mx <= 3.0e38f) ? max(-100, min(114, ilogbf(mx) - 13)) : 0;
+  const float down = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    int X[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) X[j] = __float2int_rn(y[c][j] * down);
+    p1[c] = pack_bytes((X[0] + 128) >> 8, (X[1] + 128) >> 8, (X[2] + 128) >> 8, (X[3] + 128) >> 8);
+    p2[c] = pack_bytes(X[0], X[1], X[2], X[3]);
+    int g = quad_sum(X[0] + X[1] + X[2] + X[3]);
+    g += __shfl_xor(g, 16, 64);
+    g += __shfl_xor(g, 32, 64);
+    gsum[c] = 8 * g;
+  }
+  return e;
+}
+
+// Rotation of one (row, unit) item by one wavefront (rotate_blocks), or the
+// plain bf16 values when x already holds x H.
+template <int C>
+__device__ __forceinline__ void rotate_x_item(int rotate, int block, float hscale, const u32x2 (&xw)[C],
+                                              float (&y)[C][4]) {
+  if (!rotate) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      y[c][0] = __uint_as_float(xw[c][0] << 16);
+      y[c][1] = __uint_as_float(xw[c][0] & 0xFFFF0000u);
+      y[c][2] = __uint_as_float(xw[c][1] << 16);
+      y[c][3] = __uint_as_float(xw[c][1] & 0xFFFF0000u);
+    }
+    return;
+  }
+  rotate_blocks<C>(xw, y, block, hscale);
+}
+
 // ------------------------------------------------------------------ register FWHT
 // Fast Walsh-Hadamard transform of one block of 64 VPL values held by a
 // wavefront, VPL consecutive values per lane (Sylvester order, unnormalized):
@@ -506,6 +613,38 @@ int small_producers(int nunit, int M);   // t producers of the small-M kernel (o
 hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_stream_read(const void *buf, int64_t bytes, void *sink, hipStream_t s);
+
+// few-token decode (1 <= M <= kGemvMaxM): 32-row tiles on the int8 32x32x32 matrix cores
+constexpr int kGemvMaxM = 4;
+struct GemvArgs {
+  const uint8_t *q4;
+  const uint16_t *s4;
+  const int8_t *q8;
+  const float *s8;
+  const uint16_t *U;
+  const uint16_t *V;
+  const int32_t *idx;
+  const uint16_t *x;   // bf16 [M][K]
+  uint16_t *y;         // bf16 [M][N]
+  uint64_t *tp;        // stamped partial t {fp32 bits, stamp << 32} [nunit][8][nsr_pad]
+  float *part;         // split-K: fp32 [S][M][N] results per packed row
+  uint64_t *cnt;       // tagged arrival counters [32-row tiles]
+  int *status;         // the workspace's status word
+  uint32_t stamp;      // nonzero 32-bit stamp of this call
+  int N, K, r, n_seg, n4, n8, M, block, unit, nunit, nsr, nsr_pad;
+  int S, KW, nu_w;     // K-ranges, inputs and rotation units per range
+  int W, GPW;          // wavefronts per workgroup, groups of 64 per wavefront (even)
+  int t4, t8;          // 32-row tiles of each tier
+  int nprod;           // producer workgroups (one per rotation unit)
+  int local_rot;       // 1: each compute wavefront rotates the units of its own groups
+  int rotate, publish, spin_limit;
+  float hscale;        // 1/sqrt(block)
+};
+struct GemvPlan {
+  int S, W, GPW, local_rot;
+};
+bool plan_gemv(const dvssq_layout &L, int M, int cus, GemvPlan *plan);
+hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);
 
 // Decode call after its argument checks (check_call): the single-launch kernel
 // or the prefill route, with the workspace regions of W.  *ws_need (if not
