@@ -294,9 +294,19 @@ __device__ __forceinline__ void gemv_spare(const GemvArgs &a, int cidx, uint8_t 
     bare_barrier();   // (1) x in LDS
     bare_barrier();   // (2) planes in LDS
   }
-  // t[m][i] = sum over the range's units of their partial t, in unit order
+  // t[m][i] = sum over the range's units of their partial t, in unit order.
+  // First every unit's word (token 0, i = 0) is polled, one unit per lane, so
+  // that one round trip serves all units (the words of a unit are stored
+  // together); the per-word waits below then rarely spin.
   bool late = false;
   const int64_t ustr = static_cast<int64_t>(kTokPad) * nsp;
+  for (int spins = 0;; ++spins) {
+    bool mine = true;
+    for (int j = lane; j < nu; j += 64)
+      mine = mine && static_cast<uint32_t>(ld_dev(a.tp + static_cast<int64_t>(u0 + j) * ustr) >> 32) == a.stamp;
+    if (__builtin_amdgcn_ballot_w64(!mine) == 0 || spins >= a.spin_limit) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
   for (int e = lane; e < M * nsp; e += 64) {
     const int m = e / nsp, i = e - m * nsp;
     float s = 0.0f;
