@@ -290,6 +290,27 @@ def prefill_table(dv, torch, layers, steps):
     return table
 
 
+def quantize_table(dv, torch, layers, steps=3):
+    """dvssq_quantize (weights to packed layer, on the GPU) on the spark MLP
+    shapes, sketch width l = r + 8 and two power iterations."""
+    import synth
+    out = []
+    for name in ("spark_gateup", "spark_down"):
+        lay = layers[name]
+        l = lay.r + 8
+        L = dv.pack_info(lay.N, lay.K, lay.r, lay.block, lay.n_seg)
+        W = torch.from_numpy(synth.weights_bf16(0, lay).view(np.int16)).cuda()
+        om = torch.from_numpy(np.stack([synth.sketch(0, lay, s, l) for s in range(lay.n_seg)])).cuda()
+        blob = dv.device_buffer(L.blob_bytes)
+        ws = dv.device_buffer(dv.quantize_ws_bytes(L, l))
+        st = torch.cuda.current_stream().cuda_stream
+        t, _ = time_calls(torch, lambda i: dv.quantize(L, W, om, l, 2, blob, ws, st), steps, 1)
+        out.append({"workload": f"{name} quantize on the GPU (N={lay.N}, K={lay.K}, r={lay.r}, l={l}, 2 power "
+                                f"iterations)", "ms_per_call": round(t, 2)})
+        del W, om, blob, ws
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -356,6 +377,7 @@ def main():
                           "us_per_call": round(t * 1e3, 3), "gbs": round(g, 1), "frac_hbm": round(g / HBM_PEAK_GBS, 4)})
             r.free()
         table += prefill_table(dv, torch, layers, args.prefill_steps)
+        table += quantize_table(dv, torch, layers)
         out["table"] = table
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(up, head_blob, head_x, args.cpu_seconds)

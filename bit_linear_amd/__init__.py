@@ -30,7 +30,8 @@ DECODE_MAX_M = 32
 
 EXPORTS = ("dvssq_pack_info", "dvssq_fwht", "dvssq_linear_decode", "dvssq_linear_prefill",
            "dvssq_materialize", "dvssq_mlp_ws_bytes", "dvssq_mlp_ws_offsets", "dvssq_mlp_decode",
-           "dvssq_mlp_prefill", "dvssq_stream_read", "dvssq_linear_decode_noalloc", "dvssq_status_str")
+           "dvssq_mlp_prefill", "dvssq_stream_read", "dvssq_linear_decode_noalloc", "dvssq_quantize_ws_bytes",
+           "dvssq_quantize", "dvssq_status_str")
 
 
 class Layout(C.Structure):
@@ -83,6 +84,10 @@ _lib.dvssq_mlp_ws_offsets.argtypes = [C.POINTER(Layout), C.POINTER(Layout), C.PO
 for _n in ("dvssq_mlp_decode", "dvssq_mlp_prefill"):
     getattr(_lib, _n).restype = C.c_int
     getattr(_lib, _n).argtypes = [C.POINTER(Layout), _P, C.POINTER(Layout), _P, _P, _P, C.c_int32, _P, C.c_uint32, _P]
+_lib.dvssq_quantize_ws_bytes.restype = C.c_int64
+_lib.dvssq_quantize_ws_bytes.argtypes = [C.POINTER(Layout), C.c_int32]
+_lib.dvssq_quantize.restype = C.c_int
+_lib.dvssq_quantize.argtypes = [C.POINTER(Layout), _P, _P, C.c_int32, C.c_int32, _P, _P, _P]
 _lib.dvssq_stream_read.restype = C.c_int
 _lib.dvssq_stream_read.argtypes = [_P, C.c_int64, _P, _P]
 _lib.dvssq_status_str.restype = C.c_char_p
@@ -147,6 +152,18 @@ def linear_decode_noalloc(layout: Layout, blob, x, y, M: int, flags: int = 0, st
 
 def materialize(layout: Layout, blob, w, stream=None) -> None:
     _check(_lib.dvssq_materialize(C.byref(layout), _ptr(blob), _ptr(w), _stream(stream)), "dvssq_materialize")
+
+
+def quantize_ws_bytes(layout: Layout, l: int) -> int:
+    n = int(_lib.dvssq_quantize_ws_bytes(C.byref(layout), l))
+    if n < 0:
+        raise DvssqError(DVSSQ_EINVAL, "dvssq_quantize_ws_bytes")
+    return n
+
+
+def quantize(layout: Layout, W, omega, l: int, power_iters: int, blob, ws, stream=None) -> None:
+    _check(_lib.dvssq_quantize(C.byref(layout), _ptr(W), _ptr(omega), l, power_iters, _ptr(blob), _ptr(ws),
+                               _stream(stream)), "dvssq_quantize")
 
 
 def mlp_ws_bytes(gu: Layout, down: Layout) -> int:

@@ -461,6 +461,44 @@ int dvssq_materialize(const dvssq_layout *L, const void *blob, void *w, void *st
   return launch_materialize(a, L->block, static_cast<hipStream_t>(stream)) == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
+// ------------------------------------------------------------------ GPU quantizer
+namespace {
+constexpr int kQzMaxPowerIters = 16;
+// rotation row of the quantizer in LDS: K fp64 + K int32 codes + a reduction
+size_t quantize_row_lds(int K) { return static_cast<size_t>(K) * 12 + 256 * 8; }
+int check_quantize(const dvssq_layout *L, int32_t l) {
+  const int rc = check_layout(L);
+  if (rc != DVSSQ_OK) return rc;
+  const int64_t Ns = L->N / L->n_seg;
+  if (l < L->r || l > std::min<int64_t>(Ns, L->K)) return DVSSQ_EINVAL;
+  if (quantize_row_lds(L->K) > 160 * 1024) return DVSSQ_EUNSUPPORTED;
+  return DVSSQ_OK;
+}
+}  // namespace
+
+int64_t dvssq_quantize_ws_bytes(const dvssq_layout *L, int32_t l) {
+  if (check_quantize(L, l) != DVSSQ_OK) return -1;
+  return quantize_ws_layout(*L, l).bytes;
+}
+
+int dvssq_quantize(const dvssq_layout *L, const void *W, const double *omega, int32_t l, int32_t power_iters,
+                   void *blob, void *ws, void *stream) {
+  const int rc = check_quantize(L, l);
+  if (rc != DVSSQ_OK) return rc;
+  if (!W || !omega || !blob || !ws) return DVSSQ_EINVAL;
+  if (power_iters < 0 || power_iters > kQzMaxPowerIters) return DVSSQ_EINVAL;
+  if (!aligned(W, 16) || !aligned(omega, 8) || !aligned(blob, 256) || !aligned(ws, 256)) return DVSSQ_EINVAL;
+  const size_t wb = static_cast<size_t>(L->N) * L->K * 2, ob = static_cast<size_t>(L->n_seg) * L->K * l * 8;
+  const size_t sb = static_cast<size_t>(quantize_ws_layout(*L, l).bytes);
+  if (overlap(W, wb, blob, L->blob_bytes) || overlap(W, wb, ws, sb) || overlap(omega, ob, blob, L->blob_bytes) ||
+      overlap(omega, ob, ws, sb) || overlap(blob, L->blob_bytes, ws, sb))
+    return DVSSQ_EINVAL;
+  return launch_quantize(*L, static_cast<const uint16_t *>(W), omega, l, power_iters, static_cast<uint8_t *>(blob),
+                         static_cast<uint8_t *>(ws), static_cast<hipStream_t>(stream)) == hipSuccess
+             ? DVSSQ_OK
+             : DVSSQ_EHIP;
+}
+
 // ------------------------------------------------------------------ gated MLP block
 // workspace: [0, base) shared by the two projections (one after the other on
 // the stream), then the fused gate+up output and the intermediate h, for up

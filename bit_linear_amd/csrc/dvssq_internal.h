@@ -614,6 +614,14 @@ hipError_t launch_decode_small(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_stream_read(const void *buf, int64_t bytes, void *sink, hipStream_t s);
 
+// GPU quantizer: workspace byte offsets (per segment, reused) and the launch
+struct QuantizeWs {
+  int64_t R, Q, Z, Bt, G, J, sig, norm0, sgn, ord, S, salient, pos, bytes;
+};
+QuantizeWs quantize_ws_layout(const dvssq_layout &L, int l);
+hipError_t launch_quantize(const dvssq_layout &L, const uint16_t *W, const double *omega, int l, int power_iters,
+                           uint8_t *blob, uint8_t *ws, hipStream_t s);
+
 // few-token decode (1 <= M <= kGemvMaxM): 32-row tiles on the int8 32x32x32 matrix cores
 constexpr int kGemvMaxM = 4;
 struct GemvArgs {

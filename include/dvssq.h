@@ -198,6 +198,36 @@ int dvssq_linear_prefill(const dvssq_layout *L, const void *blob, const void *x,
 int dvssq_materialize(const dvssq_layout *L, const void *blob, void *w, void *stream);
 
 /*
+ * GPU quantizer: the packed layer of a bf16 weight W, per segment of N/n_seg
+ * rows (Spark-X2.5-4B-Hadamard-GSQ model card, Architectural Pillars 1: Tier A
+ * salience and INT8 rows, Tier B rotation and INT4 groups, Tier C low-rank
+ * residual; MiniCPM5-2B-Hadamard-GSQ model card, Mathematical Foundations 1
+ * and 2):
+ *   salience = sum of squares of a row (fp64, ascending k), the top 1/8 of
+ *   the segment's rows (stable descending order) form the INT8 tier; rotation
+ *   W H per row (fp64 butterflies, then 1/sqrt(block)); INT8 rows
+ *   s = fp32(max|w|/127), q = clip(rint(w/s), -128, 127); INT4 groups of 64
+ *   s = bf16(max|w|/7), q = clip(rint(w/s), -8, 7) against the stored scale;
+ *   residual R = W H - W_hat; rank-r factors by randomized subspace iteration
+ *   from the sketch (power_iters rounds), a one-sided Jacobi SVD of the
+ *   projection, U = A = U_r sqrt(S_r), V rows = sqrt(S_r) V_r^T, bf16.
+ * L: from dvssq_pack_info (N, K, r, block, n_seg).  W: device bf16 [N][K],
+ * 16-byte aligned.  omega: device fp64 [n_seg][K][l], the Gaussian sketch of
+ * each segment, r <= l <= min(N/n_seg, K).  power_iters: 0 .. 16.
+ * blob: device, L->blob_bytes, 256-byte aligned; every byte is written (the
+ * padding between sub-buffers zero).  ws: device workspace of
+ * dvssq_quantize_ws_bytes(L, l) bytes, 256-byte aligned, no initialization.
+ * W, omega, blob and ws must not overlap.  Codes, scales, idx and the tier
+ * split are those of the same fp64 steps done in this order on a CPU, bit for
+ * bit; U and V agree with them up to the order of fp64 sums (within a bf16
+ * unit almost everywhere).  DVSSQ_EUNSUPPORTED for K > 13482 (one row in
+ * LDS).  Kernels are launched on `stream`; the call does not synchronize.
+ */
+int64_t dvssq_quantize_ws_bytes(const dvssq_layout *L, int32_t l);
+int dvssq_quantize(const dvssq_layout *L, const void *W, const double *omega, int32_t l, int32_t power_iters,
+                   void *blob, void *ws, void *stream);
+
+/*
  * Workspace size of dvssq_mlp_decode / dvssq_mlp_prefill for the pair (gu,
  * down) and up to min(gu->M_max, down->M_max) rows, into *bytes.  Host-only.
  * DVSSQ_EINVAL if the pair does not form a gated MLP block (see

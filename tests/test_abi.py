@@ -276,3 +276,42 @@ def test_decode_noalloc_error_paths():
     bad = dv.pack_info(512, 256, 4, 256, 1, M_max=64)
     bad.off_U += 256
     assert c(L=bad) == E
+
+
+def test_quantize_ws_bytes():
+    L = dv.pack_info(512, 256, 4, 256, 1)
+    f = dv.lib().dvssq_quantize_ws_bytes
+    n = f(C.byref(L), 12)
+    # R [N][K], Q [N][l], three [K][l] and the small arrays, each 256-aligned
+    assert n >= 8 * (512 * 256 + 512 * 12 + 3 * 256 * 12) and n % 256 == 0
+    assert f(C.byref(L), 3) == -1                 # l < r
+    assert f(C.byref(L), 257) == -1               # l > min(N / n_seg, K)
+    assert f(None, 12) == -1
+    seg = dv.pack_info(2 * 256, 256, 4, 256, 2)
+    assert f(C.byref(seg), 256) > 0 and f(C.byref(seg), 257) == -1
+    with pytest.raises(dv.DvssqError):
+        dv.quantize_ws_bytes(L, 2)
+
+
+def test_quantize_error_paths():
+    """Every argument check of the GPU quantizer runs before its first launch."""
+    f, E = dv.lib().dvssq_quantize, dv.DVSSQ_EINVAL
+    L = dv.pack_info(512, 256, 4, 256, 1)
+    OM = 0x50000000
+
+    def c(L=L, W=X, om=OM, l=12, p=2, blob=BLOB, ws=WS):
+        return f(C.byref(L) if L is not None else None, W, om, l, p, blob, ws, None)
+
+    assert c(L=None) == E and c(W=None) == E and c(om=None) == E and c(blob=None) == E and c(ws=None) == E
+    assert c(l=3) == E and c(l=257) == E
+    assert c(p=-1) == E and c(p=17) == E
+    assert c(W=X + 8) == E and c(om=OM + 4) == E and c(blob=BLOB + 16) == E and c(ws=WS + 128) == E
+    assert c(blob=X + 1024) == E                        # blob inside W
+    assert c(ws=BLOB + 256) == E                        # ws inside the blob
+    assert c(om=WS + 256) == E                          # sketch inside ws
+    bad = dv.pack_info(512, 256, 4, 256, 1)
+    bad.off_U += 256
+    assert c(L=bad) == E
+    # one rotation row (fp64 + codes) must fit the 160 KB of LDS
+    big = dv.pack_info(512, 16384, 4, 256, 1)
+    assert c(L=big) == dv.DVSSQ_EUNSUPPORTED
