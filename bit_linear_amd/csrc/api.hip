@@ -187,6 +187,13 @@ static bool decode_single_launch(const dvssq_layout &L, int32_t M, SmallPlan *sp
   return M <= kSmallMaxM && plan_decode_small(L, M, compute_units(), sp) && sp->S > 0;
 }
 
+// the decode kernels take a gated input (the block's h formed in their loads):
+// the single-launch kernels, with the gate+up rows addressable in 32 bits
+static bool decode_takes_gated(const dvssq_layout &L, int32_t M) {
+  SmallPlan sp{};
+  return static_cast<int64_t>(M) * L.K * 4 < (int64_t{1} << 31) && decode_single_launch(L, M, &sp);
+}
+
 static int prefill_supported(const dvssq_layout &L, int32_t M);
 static int prefill_launch(const dvssq_layout *L, const WsLayout &W, const void *blob, const void *x, void *y,
                           int32_t M, void *ws, uint32_t flags, hipStream_t s);
@@ -212,7 +219,7 @@ int decode_check_args(const dvssq_layout *L, const void *blob, const void *x, vo
 
 // the few-token kernel (gemv_kernel), after the checks: one launch
 static int gemv_launch(const dvssq_layout &L, const WsLayout &W, const GemvPlan &gp, const void *blob, const void *x,
-                       void *y, int32_t M, void *ws, uint32_t flags, hipStream_t s) {
+                       void *y, int32_t M, void *ws, uint32_t flags, hipStream_t s, bool gated, uint16_t *hout) {
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   const Blob B{static_cast<const uint8_t *>(blob), &L};
   GemvArgs g{};
@@ -224,6 +231,8 @@ static int gemv_launch(const dvssq_layout &L, const WsLayout &W, const GemvPlan 
   g.V = B.V();
   g.idx = B.idx();
   g.x = static_cast<const uint16_t *>(x);
+  g.gated = gated ? 1 : 0;
+  g.hout = hout;
   g.y = static_cast<uint16_t *>(y);
   g.tp = reinterpret_cast<uint64_t *>(wsb + W.d_tp);
   g.part = reinterpret_cast<float *>(wsb + W.d_part);
@@ -261,16 +270,18 @@ static int gemv_launch(const dvssq_layout &L, const WsLayout &W, const GemvPlan 
 }
 
 int decode_dispatch(const dvssq_layout &Lr, const WsLayout &W, const void *blob, const void *x, void *y, int32_t M,
-                    void *ws, uint32_t flags, hipStream_t s, int64_t *ws_need, bool dry_run) {
+                    void *ws, uint32_t flags, hipStream_t s, int64_t *ws_need, bool dry_run, bool gated,
+                    uint16_t *hout) {
   const dvssq_layout *L = &Lr;
   GemvPlan gp{};
-  if (M <= kGemvMaxM && L->K % decode_unit(L->block) == 0 && plan_gemv(*L, M, compute_units(), &gp)) {
+  if (M <= kGemvMaxM && L->K % decode_unit(L->block) == 0 && plan_gemv(*L, M, compute_units(), gated, &gp)) {
     if (ws_need) *ws_need = gp.S > 1 ? W.d_part + 4 * int64_t(gp.S) * M * L->N : W.d_part;
     if (dry_run) return DVSSQ_OK;
-    return gemv_launch(*L, W, gp, blob, x, y, M, ws, flags, s);
+    return gemv_launch(*L, W, gp, blob, x, y, M, ws, flags, s, gated, hout);
   }
   SmallPlan sp{};
   if (!decode_single_launch(*L, M, &sp)) {
+    if (gated) return DVSSQ_EUNSUPPORTED;   // the callers form h first (decode_takes_gated)
     if (ws_need) *ws_need = W.p_end;
     if (dry_run) return DVSSQ_OK;
     return prefill_launch(L, W, blob, x, y, M, ws, flags & DVSSQ_X_ROTATED, s);
@@ -289,6 +300,8 @@ int decode_dispatch(const dvssq_layout &Lr, const WsLayout &W, const void *blob,
   d.V = B.V();
   d.idx = B.idx();
   d.x = static_cast<const uint16_t *>(x);
+  d.gated = gated ? 1 : 0;
+  d.hout = hout;
   d.tp = reinterpret_cast<float *>(wsb + W.d_tp);
   d.flag = reinterpret_cast<uint64_t *>(wsb + W.d_flag);
   d.part = reinterpret_cast<float *>(wsb + W.d_part);
@@ -580,6 +593,12 @@ int dvssq_mlp_decode(const dvssq_layout *gu, const void *gu_blob, const dvssq_la
   // disjoint by construction): after the first launch only a launch error can occur
   rc = dvssq_linear_decode(gu, gu_blob, x, ygu, M, ws, flags, stream);
   if (rc != DVSSQ_OK) return rc;
+  // the down projection's single-launch kernels form h = gelu(gate) * up as
+  // they load their input (h also lands in the workspace); the prefill
+  // fallback takes h from the separate kernel
+  if (decode_takes_gated(*down, M))
+    return decode_dispatch(*down, ws_layout(*down), down_blob, ygu, y, M, ws, 0, static_cast<hipStream_t>(stream),
+                           nullptr, false, true, static_cast<uint16_t *>(h));
   GegluArgs g{static_cast<const uint16_t *>(ygu), static_cast<uint16_t *>(h), M, down->K};
   if (launch_geglu(g, static_cast<hipStream_t>(stream)) != hipSuccess) return DVSSQ_EHIP;
   return dvssq_linear_decode(down, down_blob, h, y, M, ws, 0, stream);

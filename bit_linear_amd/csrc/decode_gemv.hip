@@ -87,17 +87,30 @@ __device__ __forceinline__ void gemv_produce(const GemvArgs &a, int u, uint8_t *
   float *tred = reinterpret_cast<float *>(smem + 16 * LDB * 2);       // [W][NI][4][64]
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   const auto rv = make_rsrc(a.V, static_cast<uint32_t>(a.nsr) * a.K * 2);
-  const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * a.K * 2);
+  const int xrow = a.gated ? 2 * a.K : a.K;            // inputs per row of x
+  const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * xrow * 2);
 
-  // x rows wave, wave + W (M <= 4 <= 2 W), then the first batch of V
-  u32x2 xw[2][C];
+  // x rows wave, wave + W (M <= 4 <= 2 W) (gated: the gate and the up
+  // values), then the first batch of V
+  u32x2 xw[2][C], xu[2][C];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int m = wave + j * W;
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-      xw[j][c] = buf_load8(rx, m < M ? static_cast<uint32_t>(m * a.K + k0 + 256 * c + 16 * n + 4 * q) * 2 : kOutOfRange);
+    for (int c = 0; c < C; ++c) {
+      xw[j][c] = buf_load8(rx, m < M ? static_cast<uint32_t>(m * xrow + k0 + 256 * c + 16 * n + 4 * q) * 2 : kOutOfRange);
+      xu[j][c] = u32x2{0u, 0u};
+    }
   }
+  if (a.gated)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = wave + j * W;
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        xu[j][c] = buf_load8(rx, m < M ? static_cast<uint32_t>(m * xrow + a.K + k0 + 256 * c + 16 * n + 4 * q) * 2
+                                       : kOutOfRange);
+    }
   u32x4 vb[VJ][4];
   auto load_v = [&](int ks0) {
 #pragma unroll
@@ -121,6 +134,14 @@ __device__ __forceinline__ void gemv_produce(const GemvArgs &a, int u, uint8_t *
   for (int j = 0; j < 2; ++j) {
     const int m = wave + j * W;
     if (m < M) {
+      if (a.gated) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          xw[j][c][0] = geglu_bf16x2(xw[j][c][0], xu[j][c][0]);
+          xw[j][c][1] = geglu_bf16x2(xw[j][c][1], xu[j][c][1]);
+          if (a.hout) *reinterpret_cast<u32x2 *>(a.hout + static_cast<int64_t>(m) * a.K + k0 + 256 * c + 16 * n + 4 * q) = xw[j][c];
+        }
+      }
       float y[C][4];
       rotate_x_item<C>(a.rotate, a.block, a.hscale, xw[j], y);
 #pragma unroll
@@ -227,7 +248,8 @@ __device__ __forceinline__ uint32_t quantize_fast(const float (&y)[C][4], uint32
   return static_cast<uint32_t>(eb - 13) << 23;
 }
 
-// LDS of a consumer workgroup: x of the range (bf16 [M][KW], in 1 KB chunks),
+// LDS of a consumer workgroup: x of the range (bf16 [M][KW], in 1 KB chunks;
+// gated: the gate values, then the up values, each rounded up to 1 KB),
 // the planes [2][MT][XP], 8 x group sums [KGw][8], unit scales [nu][8],
 // partial results [W][NV][64], low-rank terms [NV][64], t [MT][nsp], output
 // columns [32], INT8 scales [32], timeout word
@@ -245,8 +267,9 @@ struct GemvLds {
   __device__ __forceinline__ GemvLds(const GemvArgs &a, uint8_t *smem) {
     const int KW = a.KW, KGw = KW >> 6;
     XP = KW + 16;
-    xslab = (a.M * a.GPW * kGroup * 2 + 1023) & ~1023;
-    xbytes = max((a.M * KW * 2 + 1023) & ~1023, a.W * xslab);
+    const int gx = a.gated ? 2 : 1;    // gated: the gate values, then the up values
+    xslab = gx * ((a.M * a.GPW * kGroup * 2 + 1023) & ~1023);
+    xbytes = max(gx * ((a.M * KW * 2 + 1023) & ~1023), a.W * xslab);
     xs = reinterpret_cast<uint16_t *>(smem);
     pl1 = reinterpret_cast<int8_t *>(smem + xbytes);
     pl2 = pl1 + MT * XP;
@@ -438,19 +461,22 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   const int n = lane & 15, q = lane >> 4;
   const int LW = lnu * P;                               // local path: inputs of the slab's rows
   uint16_t *slab = xs + wave * (sm.xslab >> 1);         // local path: this wavefront's slab
+  const int span = a.local_rot ? 2 * LW : 2 * KW;        // bytes of one row of the copy
+  const int nch = (M * span + 1023) >> 10;               // 1 KB chunks of the copy
+  const int uofs = a.gated ? nch * 512 : 0;              // gated: the up values, inputs after the gate values
   {
-    const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * K * 2);
-    const int span = a.local_rot ? 2 * LW : 2 * KW;      // bytes of one row of the copy
-    const int kbase = a.local_rot ? k0 + lu0 * P : k0;    // its first input
+    const int xrow = a.gated ? 2 * K : K;                // inputs per row of x
+    const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * xrow * 2);
+    const int kbase = a.local_rot ? k0 + lu0 * P : k0;    // first input of the copy
     uint8_t *dst = reinterpret_cast<uint8_t *>(a.local_rot ? slab : xs);
-    const int nch = (M * span + 1023) >> 10;
-    for (int c = a.local_rot ? 0 : wave; c < nch; c += a.local_rot ? 1 : W) {
-      const int f = c * 1024 + lane * 16;               // flattened byte
-      const int m = f / span, kb = f - m * span;
-      const uint32_t off = m < M ? static_cast<uint32_t>(m * 2 * K + 2 * kbase + kb) : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)(dst + c * 1024), 16, off,
-                                               0, 0, 0);
-    }
+    for (int h2 = 0; h2 < (a.gated ? 2 : 1); ++h2)
+      for (int c = a.local_rot ? 0 : wave; c < nch; c += a.local_rot ? 1 : W) {
+        const int f = c * 1024 + lane * 16;             // flattened byte
+        const int m = f / span, kb = f - m * span;
+        const uint32_t off = m < M ? static_cast<uint32_t>(m * 2 * xrow + 2 * (h2 * K + kbase) + kb) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (__attribute__((address_space(3))) void *)(dst + (h2 * nch + c) * 1024), 16, off, 0, 0, 0);
+      }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -489,8 +515,15 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
       const int m = it % M, ul = it / M;
       u32x2 xw[C];
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-        xw[c] = *reinterpret_cast<const u32x2 *>(slab + m * LW + ul * P + 256 * c + 16 * n + 4 * q);
+      for (int c = 0; c < C; ++c) {
+        const int e = m * LW + ul * P + 256 * c + 16 * n + 4 * q;
+        xw[c] = *reinterpret_cast<const u32x2 *>(slab + e);
+        if (a.gated) {
+          const u32x2 uv = *reinterpret_cast<const u32x2 *>(slab + uofs + e);
+          xw[c][0] = geglu_bf16x2(xw[c][0], uv[0]);
+          xw[c][1] = geglu_bf16x2(xw[c][1], uv[1]);
+        }
+      }
       put_item(m, lu0 + ul, xw);
     }
     __builtin_amdgcn_s_waitcnt(kLgkm0);
@@ -501,8 +534,15 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
       const int m = it % M, u = it / M;
       u32x2 xw[C];
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-        xw[c] = *reinterpret_cast<const u32x2 *>(xs + m * KW + u * P + 256 * c + 16 * n + 4 * q);
+      for (int c = 0; c < C; ++c) {
+        const int e = m * KW + u * P + 256 * c + 16 * n + 4 * q;
+        xw[c] = *reinterpret_cast<const u32x2 *>(xs + e);
+        if (a.gated) {
+          const u32x2 uv = *reinterpret_cast<const u32x2 *>(xs + uofs + e);
+          xw[c][0] = geglu_bf16x2(xw[c][0], uv[0]);
+          xw[c][1] = geglu_bf16x2(xw[c][1], uv[1]);
+        }
+      }
       put_item(m, u, xw);
     }
     __builtin_amdgcn_s_waitcnt(kLgkm0);
@@ -649,10 +689,10 @@ size_t producer_lds(int unit, int W, int nsp) {
   return static_cast<size_t>(16) * (unit + 8) * 2 + static_cast<size_t>(W) * (nsp / 16) * 4 * 64 * 4;
 }
 
-size_t consumer_lds(int MT, int M, int KW, int nu, int W, int GPW, int nsp) {
-  const size_t NV = MT == 1 ? 1 : 4;
-  const size_t xslab = (static_cast<size_t>(M) * GPW * kGroup * 2 + 1023) & ~size_t(1023);
-  const size_t xbytes = std::max((static_cast<size_t>(M) * KW * 2 + 1023) & ~size_t(1023), W * xslab);
+size_t consumer_lds(int MT, int M, int KW, int nu, int W, int GPW, int nsp, bool gated) {
+  const size_t NV = MT == 1 ? 1 : 4, gx = gated ? 2 : 1;
+  const size_t xslab = gx * ((static_cast<size_t>(M) * GPW * kGroup * 2 + 1023) & ~size_t(1023));
+  const size_t xbytes = std::max(gx * ((static_cast<size_t>(M) * KW * 2 + 1023) & ~size_t(1023)), W * xslab);
   return xbytes + 2 * static_cast<size_t>(MT) * (KW + 16) + static_cast<size_t>(KW / kGroup + nu) * kTokPad * 4 +
          (static_cast<size_t>(W) + 1) * NV * 64 * 4 + static_cast<size_t>(MT) * nsp * 4 + 2 * kRows * 4 + 16;
 }
@@ -693,14 +733,14 @@ hipError_t launch_m(const GemvArgs &a, size_t lds, hipStream_t s) {
 // (or the largest feasible), and W compute wavefronts per workgroup (plus the
 // spare one), each taking GPW (even, at most 12) of the range's groups, about
 // 8 where W <= 7 allows.
-bool plan_gemv(const dvssq_layout &L, int M, int cus, GemvPlan *p) {
+bool plan_gemv(const dvssq_layout &L, int M, int cus, bool gated, GemvPlan *p) {
   if (M < 1 || M > kGemvMaxM) return false;
   const int unit = L.block > 256 ? L.block : 256;
   if (L.K % unit) return false;
   const int64_t big = std::max<int64_t>(static_cast<int64_t>(L.n_int4) * L.K / 2,
                                         std::max<int64_t>(static_cast<int64_t>(L.n_int8) * L.K,
                                                           static_cast<int64_t>(L.N) * L.r * 2));
-  if (big >= (int64_t{1} << 31) || static_cast<int64_t>(M) * L.K * 2 >= (int64_t{1} << 31)) return false;
+  if (big >= (int64_t{1} << 31) || static_cast<int64_t>(M) * L.K * 4 >= (int64_t{1} << 31)) return false;
   const int nunit = L.K / unit, KG = L.K / kGroup;
   const int tiles = (L.n_int4 + kRows - 1) / kRows + (L.n_int8 + kRows - 1) / kRows;
   const int nsp = (L.n_seg * L.r + 31) / 32 * 32;
@@ -723,7 +763,8 @@ bool plan_gemv(const dvssq_layout &L, int M, int cus, GemvPlan *p) {
         W = (KGr + gpw - 1) / gpw;
       }
     }
-    const size_t lds = std::max(consumer_lds(MT, M, L.K / S, nu, W, gpw, nsp), producer_lds(unit, W + 1, nsp));
+    const size_t lds =
+        std::max(consumer_lds(MT, M, L.K / S, nu, W, gpw, nsp, gated), producer_lds(unit, W + 1, nsp));
     if (lds > 160 * 1024) continue;
     p->S = S;
     p->W = W;
@@ -745,7 +786,7 @@ bool plan_gemv(const dvssq_layout &L, int M, int cus, GemvPlan *p) {
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s) {
   if (a.unit != 256 && a.unit != 512 && a.unit != 1024 && a.unit != 2048) return hipErrorInvalidValue;
   const int MT = a.M <= 1 ? 1 : 4;
-  const size_t lds = std::max(consumer_lds(MT, a.M, a.KW, a.nu_w, a.W, a.GPW, a.nsr_pad),
+  const size_t lds = std::max(consumer_lds(MT, a.M, a.KW, a.nu_w, a.W, a.GPW, a.nsr_pad, a.gated != 0),
                               producer_lds(a.unit, a.W + 1, a.nsr_pad));
   return a.M <= 1 ? launch_m<1>(a, lds, s) : launch_m<4>(a, lds, s);
 }

@@ -78,7 +78,8 @@ __device__ __forceinline__ void rotate_item(const DecodeArgs &a, const u32x2 (&x
 // --------------------------------------------------------------------------- producer
 
 // Partial t of one rotation unit (C blocks of 256) for up to 8 activation rows.
-template <int C>
+// GT: gated input (h = geglu(gate, up) formed from the block's gate+up output).
+template <int C, bool GT>
 __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
   constexpr int P = 256 * C;
   constexpr int LDB = P + 8;             // bf16 x_rot row in LDS
@@ -106,10 +107,15 @@ __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
   };
   const bool r_wave = wave < mrows;
   const int m = m0 + min(wave, mrows - 1);
-  u32x2 xw[C];
+  const int64_t xrow = GT ? 2 * static_cast<int64_t>(a.K) : a.K;   // inputs per row of x
+  u32x2 xw[C], xu[C];
 #pragma unroll
   for (int c = 0; c < C; ++c)
-    xw[c] = *reinterpret_cast<const u32x2 *>(a.x + static_cast<int64_t>(m) * a.K + k0 + 256 * c + 16 * n + 4 * q);
+    xw[c] = *reinterpret_cast<const u32x2 *>(a.x + m * xrow + k0 + 256 * c + 16 * n + 4 * q);
+  if constexpr (GT)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      xu[c] = *reinterpret_cast<const u32x2 *>(a.x + m * xrow + a.K + k0 + 256 * c + 16 * n + 4 * q);
   if (t_wave)
 #pragma unroll
     for (int j = 0; j < 8; ++j) vload(j, j);
@@ -118,6 +124,13 @@ __device__ void produce(const DecodeArgs &a, int pidx, uint8_t *smem) {
   // a.planes, also the row's 15-bit planes, group sums and unit scale for the
   // consumers (device-scope stores, drained before the flag)
   if (r_wave) {
+    if constexpr (GT)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        xw[c][0] = geglu_bf16x2(xw[c][0], xu[c][0]);
+        xw[c][1] = geglu_bf16x2(xw[c][1], xu[c][1]);
+        if (a.hout) *reinterpret_cast<u32x2 *>(a.hout + static_cast<int64_t>(m) * a.K + k0 + 256 * c + 16 * n + 4 * q) = xw[c];
+      }
     float y[C][4];
     rotate_item<C>(a, xw, y);
 #pragma unroll
@@ -320,7 +333,7 @@ __device__ void spare(const DecodeArgs &a, int sw, int nsw, int wbase, int wrows
 // groups (an even number); the wavefronts from RT * KQ on are spare.  Values
 // that are the same across a wavefront are kept in scalar registers: the
 // vector ALU, shared by the four wavefronts of each SIMD, is the scarce unit.
-template <int MT, int C, int MAXG, bool T8>
+template <int MT, int C, int MAXG, bool T8, bool GT>
 __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   constexpr int R = MT == 1 ? 1 : 4;    // accumulator rows per lane and token tile
   constexpr int NT = MT > 16 ? 2 : 1;   // token tiles of 16
@@ -381,14 +394,20 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   // Loads go through buffer resources: a lane with nothing to load gets an
   // offset past the end, which reads zeros without touching memory, so the
   // loads are issued unconditionally and each wait covers only what it needs.
-  const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * a.K * 2);
-  u32x2 xw[C];
+  const uint32_t xrow = GT ? 2u * a.K : static_cast<uint32_t>(a.K);   // inputs per row of x
+  const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * xrow * 2);
+  // gated: the gate values at x[m][k], the up values at x[m][K + k]
+  const uint32_t uoff = static_cast<uint32_t>(a.K) * 2;
+  u32x2 xw[C], xu[C];
   {
     const int m = static_cast<int>((a.lut_m >> (4 * wave)) & 15u), u = static_cast<int>((a.lut_u >> (4 * wave)) & 15u);
-    const uint32_t off = !a.planes && wave < nitem ? (static_cast<uint32_t>(m) * a.K + k0 + u * P + 16 * n + 4 * q) * 2
+    const uint32_t off = !a.planes && wave < nitem ? (static_cast<uint32_t>(m) * xrow + k0 + u * P + 16 * n + 4 * q) * 2
                                       : kOutOfRange;
 #pragma unroll
     for (int c = 0; c < C; ++c) xw[c] = buf_load8(rx, off + 512 * c);
+    if constexpr (GT)
+#pragma unroll
+      for (int c = 0; c < C; ++c) xu[c] = buf_load8(rx, off == kOutOfRange ? kOutOfRange : off + uoff + 512 * c);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -420,7 +439,13 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   // ---- 3. items -> quantized int8 planes in LDS.  The first item is handled
   // outside any loop, so its wait covers only the activation loads issued
   // before the weights; later items (M > 1) are loaded here.
-  auto quantize = [&](int m, int u, const u32x2(&xv)[C]) {
+  auto quantize = [&](int m, int u, u32x2(&xv)[C], const u32x2(&uv)[C]) {
+    if constexpr (GT)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        xv[c][0] = geglu_bf16x2(xv[c][0], uv[c][0]);
+        xv[c][1] = geglu_bf16x2(xv[c][1], uv[c][1]);
+      }
     float y[C][4];
     rotate_item<C>(a, xv, y);
     uint32_t p1[C], p2[C];
@@ -444,15 +469,19 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
     sum_t(a, wave * 64 + lane, NCW * 64, u0, nu, ts);
   } else {
     if (wave < nitem)
-      quantize(static_cast<int>((a.lut_m >> (4 * wave)) & 15u), static_cast<int>((a.lut_u >> (4 * wave)) & 15u), xw);
+      quantize(static_cast<int>((a.lut_m >> (4 * wave)) & 15u), static_cast<int>((a.lut_u >> (4 * wave)) & 15u), xw,
+               xu);
     __builtin_amdgcn_sched_barrier(0);
     for (int it = wave + NCW; it < nitem; it += NCW) {
       const int m = it % M, u = it / M;
-      u32x2 xv[C];
+      u32x2 xv[C], uv[C];
+      const uint32_t off = (static_cast<uint32_t>(m) * xrow + k0 + u * P + 16 * n + 4 * q) * 2;
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-        xv[c] = buf_load8(rx, (static_cast<uint32_t>(m) * a.K + k0 + u * P + 256 * c + 16 * n + 4 * q) * 2);
-      quantize(m, u, xv);
+      for (int c = 0; c < C; ++c) xv[c] = buf_load8(rx, off + 512 * c);
+      if constexpr (GT)
+#pragma unroll
+        for (int c = 0; c < C; ++c) uv[c] = buf_load8(rx, off + uoff + 512 * c);
+      quantize(m, u, xv, uv);
     }
   }
   __syncthreads();   // (A) planes, group sums and unit scales are in LDS
@@ -669,17 +698,17 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   }
 }
 
-template <int MT, int C, int MAXG>
+template <int MT, int C, int MAXG, bool GT>
 __global__ __launch_bounds__(kThreads) void decode_small_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int b = blockIdx.x;
   if (b < a.nprod) {
-    produce<C>(a, b, smem);
+    produce<C, GT>(a, b, smem);
     return;
   }
   const int c = b - a.nprod;   // consumer index = group * S + split
-  if (c < a.g4 * a.S) consume<MT, C, MAXG, false>(a, c, smem);
-  else consume<MT, C, MAXG, true>(a, c, smem);
+  if (c < a.g4 * a.S) consume<MT, C, MAXG, false, GT>(a, c, smem);
+  else consume<MT, C, MAXG, true, GT>(a, c, smem);
 }
 
 size_t producer_lds(int unit) {
@@ -697,18 +726,23 @@ size_t small_lds(int M, int unit, int KW, int nsr_pad) {
   return std::max(producer_lds(unit), consumer_lds(M, unit, KW, nsr_pad));
 }
 
-template <int MT, int C, int MAXG>
-hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
+template <int MT, int C, int MAXG, bool GT>
+hipError_t launch_gt(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = small_lds(a.M, a.unit, a.KW, a.nsr_pad);
   if (lds > 65536) {
     static std::atomic<uint64_t> done{0};
     const hipError_t e =
-        ensure_lds_limit(reinterpret_cast<const void *>(decode_small_kernel<MT, C, MAXG>), 160 * 1024, done);
+        ensure_lds_limit(reinterpret_cast<const void *>(decode_small_kernel<MT, C, MAXG, GT>), 160 * 1024, done);
     if (e != hipSuccess) return e;
   }
   const int grid = a.nprod + (a.g4 + a.g8) * a.S;
-  return launch_kernel(reinterpret_cast<const void *>(decode_small_kernel<MT, C, MAXG>), dim3(grid), dim3(kThreads), lds,
-                       s, a);
+  return launch_kernel(reinterpret_cast<const void *>(decode_small_kernel<MT, C, MAXG, GT>), dim3(grid), dim3(kThreads),
+                       lds, s, a);
+}
+
+template <int MT, int C, int MAXG>
+hipError_t launch_t(const DecodeArgs &a, hipStream_t s) {
+  return a.gated ? launch_gt<MT, C, MAXG, true>(a, s) : launch_gt<MT, C, MAXG, false>(a, s);
 }
 
 template <int MT, int C>

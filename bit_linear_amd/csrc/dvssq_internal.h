@@ -52,6 +52,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu);
 }
 
+// The gated MLP block's intermediate h = gelu(gate) * up (Spark-X2.5-4B GGUF
+// page, "The model": a GELU feed-forward block; ASHQ1 page, Architecture:
+// ffn_gate, ffn_up, ffn_down): GELU is the exact v Phi(v) with
+// Phi(v) = erfc(-v / sqrt 2) / 2 (relatively accurate in the negative tail,
+// where 1 + erf(v / sqrt 2) would cancel), the product rounded once to bf16.
+// Every kernel that forms h uses these two functions, so h has the same bits
+// wherever it is formed.
+__device__ __forceinline__ float gelu_exact(float v) { return 0.5f * v * erfcf(v * -0.70710678118654752f); }
+// two bf16 gate values and the matching up values -> two bf16 h values
+__device__ __forceinline__ uint32_t geglu_bf16x2(uint32_t g, uint32_t u) {
+  const float lo = gelu_exact(__uint_as_float(g << 16)) * __uint_as_float(u << 16);
+  const float hi = gelu_exact(__uint_as_float(g & 0xFFFF0000u)) * __uint_as_float(u & 0xFFFF0000u);
+  return pack_bf16x2(lo, hi);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -531,7 +546,8 @@ struct DecodeArgs {
   const uint16_t *U;
   const uint16_t *V;
   const int32_t *idx;
-  const uint16_t *x;   // bf16 [M][K]
+  const uint16_t *x;   // bf16 [M][K], or with gated the fused gate+up output [M][2K]
+  uint16_t *hout;      // gated: bf16 [M][K], the intermediate h as the producers formed it (may be null)
   // workspace
   float *tp;           // fp32 [nunit][32][nsr_pad]
   uint64_t *flag;      // [nprod]
@@ -550,6 +566,7 @@ struct DecodeArgs {
   int RT, MAXG;        // small-M path: 16-row tiles per workgroup, most groups per wavefront
   int KQ, GPW;         // small-M path: wavefronts per tile, groups per wavefront (even)
   int planes;          // small-M path: producers publish x_rot planes, consumers copy them (else rotate)
+  int gated;           // 1: the input row m is h = geglu(x[m][0 .. K), x[m][K .. 2K)), formed as it loads
   int ngrp_w, nu_w;    // small-M path: groups of 64 and rotation units in one K-range (K / S)
   uint32_t magic_s;    // small-M path: ceil(2^32 / S), S > 1: x / S = umulhi(x, magic_s) for x < 2^16
   uint64_t lut_rt, lut_kq;  // small-M path: tile and K-slice of wavefront w in bits 4w .. 4w + 3
@@ -632,8 +649,9 @@ struct GemvArgs {
   const uint16_t *U;
   const uint16_t *V;
   const int32_t *idx;
-  const uint16_t *x;   // bf16 [M][K]
+  const uint16_t *x;   // bf16 [M][K], or with gated the fused gate+up output [M][2K]
   uint16_t *y;         // bf16 [M][N]
+  uint16_t *hout;      // gated: bf16 [M][K], the intermediate h as the producers formed it (may be null)
   uint64_t *tp;        // stamped partial t {fp32 bits, stamp << 32} [nunit][8][nsr_pad]
   float *part;         // split-K: fp32 [S][M][N] results per packed row
   uint64_t *cnt;       // tagged arrival counters [32-row tiles]
@@ -646,20 +664,26 @@ struct GemvArgs {
   int nprod;           // producer workgroups (one per rotation unit)
   int local_rot;       // 1: each compute wavefront rotates the units of its own groups
   int rotate, publish, spin_limit;
+  int gated;           // 1: the input row m is h = geglu(x[m][0 .. K), x[m][K .. 2K)), formed as it loads
   float hscale;        // 1/sqrt(block)
 };
 struct GemvPlan {
   int S, W, GPW, local_rot;
 };
-bool plan_gemv(const dvssq_layout &L, int M, int cus, GemvPlan *plan);
+bool plan_gemv(const dvssq_layout &L, int M, int cus, bool gated, GemvPlan *plan);
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);
 
 // Decode call after its argument checks (check_call): the single-launch kernel
 // or the prefill route, with the workspace regions of W.  *ws_need (if not
 // null) receives the bytes of ws the call touches; with dry_run nothing is
 // launched.
+// gated: x is the fused gate+up output [M][2K] of the block's first layer and
+// the input row m is h = geglu(x[m][0 .. K), x[m][K .. 2K)), formed by the
+// kernels as they load it (h also written to hout when not null); only the
+// single-launch kernels take it (decode_takes_gated)
 int decode_dispatch(const dvssq_layout &L, const WsLayout &W, const void *blob, const void *x, void *y, int32_t M,
-                    void *ws, uint32_t flags, hipStream_t s, int64_t *ws_need, bool dry_run);
+                    void *ws, uint32_t flags, hipStream_t s, int64_t *ws_need, bool dry_run, bool gated = false,
+                    uint16_t *hout = nullptr);
 // argument checks of dvssq_linear_decode except the workspace pointer
 int decode_check_args(const dvssq_layout *L, const void *blob, const void *x, void *y, int32_t M, uint32_t flags);
 

@@ -1,9 +1,9 @@
-// Intermediate of the gated MLP block around the layer: h = gelu(gate) * up
-// (Spark-X2.5-4B GGUF page, "The model": a GELU feed-forward block; ASHQ1 page,
-// Architecture: ffn_gate, ffn_up and ffn_down).  gate and up are the two
-// segments of the fused layer's bf16 output [M][2I]; GELU is the exact
-// v Phi(v) = v erfc(-v / sqrt 2) / 2; the product is rounded once to bf16,
-// the input of the down projection.
+// Intermediate of the gated MLP block around the layer, h = gelu(gate) * up,
+// as a kernel of its own (the prefill form of the block, and decode shapes
+// whose down projection runs the prefill path): gate and up are the two
+// segments of the fused layer's bf16 output [M][2I]; geglu_bf16x2 gives the
+// GELU and the single bf16 rounding that the decode kernels use when they
+// form h in their input loads.
 #include "dvssq_internal.h"
 
 namespace dvssq {
@@ -11,10 +11,6 @@ namespace dvssq {
 namespace {
 
 constexpr int kThreads = 256;
-
-// v Phi(v) with Phi(v) = erfc(-v / sqrt 2) / 2: relatively accurate in the
-// negative tail, where 1 + erf(v / sqrt 2) would cancel
-__device__ __forceinline__ float gelu(float v) { return 0.5f * v * erfcf(v * -0.70710678118654752f); }
 
 // eight consecutive intermediate values per thread (I is a multiple of 64)
 __global__ __launch_bounds__(kThreads) void geglu_kernel(GegluArgs a) {
@@ -27,11 +23,7 @@ __global__ __launch_bounds__(kThreads) void geglu_kernel(GegluArgs a) {
   const u32x4 u = *reinterpret_cast<const u32x4 *>(row + a.I + j);
   u32x4 o;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float lo = gelu(bf16_to_f32(g[q] & 0xFFFFu)) * bf16_to_f32(u[q] & 0xFFFFu);
-    const float hi = gelu(bf16_to_f32(g[q] >> 16)) * bf16_to_f32(u[q] >> 16);
-    o[q] = pack_bf16x2(lo, hi);
-  }
+  for (int q = 0; q < 4; ++q) o[q] = geglu_bf16x2(g[q], u[q]);
   *reinterpret_cast<u32x4 *>(a.h + m * a.I + j) = o;
 }
 
