@@ -52,6 +52,7 @@ def lib():
             "orc_forward": (i32, [P, i32, i32, i32, i32, i32, P, i32, P, i32]),
             "orc_forward_cols": (i32, [P, i32, i32, i32, i32, i32, P, i32, P, i32, P, i32]),
             "orc_rotate_x": (i32, [P, i32, i32, i32, P]),
+            "orc_kvbss_attention": (i32, [P, P, P, i32, i32, i32, i32, i32, i32, i32, f64, f64, P, i64, P, i32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -293,3 +294,31 @@ def materialize(blob: np.ndarray, N, K, r, block, n_seg=1) -> np.ndarray:
     W = np.empty_like(Wr)
     W[idx] = fwht_rows(Wr, block)
     return W
+
+
+# ------------------------------------------------------------------ KV-BSS attention (test infrastructure)
+# Spark-X2.5-4B-Hadamard-GSQ card, section 2 (KV-BSS); Spark-X2.5-4B discussion
+# 14, Mathematical Formulation and the eager attention change.
+
+KVBSS_TAU = 1.10      # focus factor
+KVBSS_HAZE = 12.0     # nats below the row maximum at which logits are dropped
+
+
+def kvbss_attention(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, scale: float, haze: float,
+                    window: int = 0, rows=None, nthreads: int = 0) -> np.ndarray:
+    """Causal grouped-query attention with the KV-BSS logit scale and haze mask, fp64.
+
+    q [B][Mq][Hq][D], k and v [B][Nk][Hkv][D] (uint16 bf16 bits).  Returns
+    o [B][Mq][Hq][D], or [len(rows)][D] for the flattened query rows
+    (b * Mq + i) * Hq + h listed in rows.  haze = inf turns the mask off."""
+    q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k = np.ascontiguousarray(k_bits, dtype=np.uint16)
+    v = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    B, Mq, Hq, D = q.shape
+    _, Nk, Hkv, _ = k.shape
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = B * Mq * Hq if r is None else r.size
+    o = np.zeros((n, D))
+    _chk(lib().orc_kvbss_attention(_p(q), _p(k), _p(v), B, Mq, Nk, Hq, Hkv, D, window, float(scale), float(haze),
+                                   _p(r) if r is not None else None, n, _p(o), nthreads), "kvbss_attention")
+    return o.reshape(B, Mq, Hq, D) if r is None else o

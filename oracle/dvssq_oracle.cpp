@@ -51,6 +51,7 @@
 #include <algorithm>
 #include <cfenv>
 #include <cmath>
+#include <limits>
 #include <cstdint>
 #include <cstring>
 #include <numeric>
@@ -671,6 +672,66 @@ int orc_rotate_x(const uint16_t *x, int M, int K, int b, double *xr) {
   if (!x || !xr || !pow2(b) || K % b != 0) return -1;
   for (int64_t i = 0; i < static_cast<int64_t>(M) * K; ++i) xr[i] = double_from_bf16(x[i]);
   fwht_rows(xr, M, K, b);
+  return 0;
+}
+
+// KV-BSS attention (Spark-X2.5-4B-Hadamard-GSQ model card, section 2, KV-BSS:
+// focus factor scaling and attention haze truncation; Spark-X2.5-4B discussion
+// 14, Mathematical Formulation 1-2 and the eager attention change), for
+// grouped-query causal attention (Spark-X2.5-4B GGUF page, "The model": 16
+// query heads, 4 KV heads, head_dim 256, sliding window 512 on the sliding
+// layers).  Per query row (sequence b, query i, head h):
+//   position p = Nk - Mq + i (the queries are the last Mq of the Nk tokens),
+//   visible keys j <= p, and j > p - window when window > 0;
+//   KV head h / (Hq / Hkv);
+//   s_j = scale * (q . k_j)          (scale = tau_focus / sqrt(head_dim))
+//   m = max_j s_j over the visible keys;
+//   key j is dropped when s_j < m - haze (haze = 12 nats on the pages);
+//   o = sum_j exp(s_j - m) v_j / sum_j exp(s_j - m) over the kept keys.
+// Layouts (bf16 bits): q and o [B][Mq][Hq][D], k and v [B][Nk][Hkv][D].
+// rows: flattened query rows ((b * Mq + i) * Hq + h) to evaluate, o [nrows][D];
+// all rows in order when rows == nullptr (o [B][Mq][Hq][D]).  fp64 throughout.
+int orc_kvbss_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int Mq, int Nk, int Hq,
+                        int Hkv, int D, int window, double scale, double haze, const int64_t *rows, int64_t nrows,
+                        double *o, int nthreads) {
+  if (!q || !k || !v || !o || B < 1 || Mq < 1 || Nk < Mq || Hkv < 1 || Hq % Hkv != 0 || D < 1 || window < 0)
+    return -1;
+  const int64_t total = static_cast<int64_t>(B) * Mq * Hq;
+  if (!rows) nrows = total;
+  for (int64_t e = 0; rows && e < nrows; ++e)
+    if (rows[e] < 0 || rows[e] >= total) return -1;
+  const int rep = Hq / Hkv;
+  parallel_parts(nrows, nthreads > 0 ? nthreads : default_threads(), [&](int, int64_t lo, int64_t hi) {
+    std::vector<double> sj(Nk), acc(D);
+    for (int64_t e = lo; e < hi; ++e) {
+      const int64_t row = rows ? rows[e] : e;
+      const int h = static_cast<int>(row % Hq);
+      const int64_t bi = row / Hq;
+      const int i = static_cast<int>(bi % Mq), b = static_cast<int>(bi / Mq);
+      const int g = h / rep;
+      const int p = Nk - Mq + i;
+      const int j0 = window > 0 ? std::max(0, p - window + 1) : 0;
+      const uint16_t *qr = q + row * D;
+      double m = -std::numeric_limits<double>::infinity();
+      for (int j = j0; j <= p; ++j) {
+        const uint16_t *kr = k + ((static_cast<int64_t>(b) * Nk + j) * Hkv + g) * D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += double_from_bf16(qr[d]) * double_from_bf16(kr[d]);
+        sj[j] = scale * dot;
+        m = std::max(m, sj[j]);
+      }
+      double den = 0.0;
+      std::fill(acc.begin(), acc.end(), 0.0);
+      for (int j = j0; j <= p; ++j) {
+        if (sj[j] < m - haze) continue;
+        const double w = std::exp(sj[j] - m);
+        den += w;
+        const uint16_t *vr = v + ((static_cast<int64_t>(b) * Nk + j) * Hkv + g) * D;
+        for (int d = 0; d < D; ++d) acc[d] += w * double_from_bf16(vr[d]);
+      }
+      for (int d = 0; d < D; ++d) o[e * D + d] = acc[d] / den;
+    }
+  });
   return 0;
 }
 

@@ -251,3 +251,21 @@ def random_packed_parts(seed: int, N: int, K: int, r: int, n_seg: int = 1) -> di
     U = to_bf16_bits(0.01 * normal(seed, "U", N * r)).reshape(N, r)
     V = to_bf16_bits(0.01 * normal(seed, "V", n_seg * r * K)).reshape(n_seg * r, K)
     return dict(idx=idx, q4=q4, s4=s4, q8=q8, s8=s8, U=U, V=V)
+
+
+# Query gains per attention head (cycled over the heads).  With unit-variance
+# q and k and the logit scale 1.1 / sqrt(head_dim), the logits of a head have
+# a spread of about 1.1 x gain: from heads where no key falls 12 nats below
+# the row maximum to heads where most keys do.
+ATTN_Q_GAINS = (0.5, 1.0, 3.0, 6.0)
+
+
+def attention_qkv(seed: int, tag: str, B: int, Mq: int, Nk: int, Hq: int, Hkv: int, D: int,
+                  gains=ATTN_Q_GAINS):
+    """uint16 bf16 bits: q [B][Mq][Hq][D], k and v [B][Nk][Hkv][D]; N(0, 1)
+    draws, q scaled per head by gains[h % len(gains)]."""
+    g = np.array([gains[h % len(gains)] for h in range(Hq)], dtype=np.float64)
+    q = normal(seed, f"attn/{tag}/q", B * Mq * Hq * D).reshape(B, Mq, Hq, D) * g[None, None, :, None]
+    k = normal(seed, f"attn/{tag}/k", B * Nk * Hkv * D).reshape(B, Nk, Hkv, D)
+    v = normal(seed, f"attn/{tag}/v", B * Nk * Hkv * D).reshape(B, Nk, Hkv, D)
+    return to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v)
