@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <cmath>
 
 #include "dvssq_internal.h"
 
@@ -624,6 +625,40 @@ int dvssq_stream_read(const void *buf, int64_t bytes, void *sink, void *stream) 
   if (!buf || !sink || bytes < 16 || bytes % 16 != 0 || bytes > (int64_t(1) << 40)) return DVSSQ_EINVAL;
   if (!aligned(buf, 16) || !aligned(sink, 4)) return DVSSQ_EINVAL;
   return launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
+}
+
+int dvssq_kvbss_attention(const dvssq_attn_shape *sh, const void *q, const void *k, const void *v, void *o,
+                          void *stream) {
+  if (!sh || !q || !k || !v || !o) return DVSSQ_EINVAL;
+  const dvssq_attn_shape S = *sh;
+  if (S.B < 1 || S.Mq < 1 || S.Nk < S.Mq || S.Hq < 1 || S.Hkv < 1 || S.Hq % S.Hkv != 0 || S.window < 0)
+    return DVSSQ_EINVAL;
+  if (!std::isfinite(S.scale) || std::isnan(S.haze) || S.haze < 0.0f) return DVSSQ_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DVSSQ_EINVAL;
+  if (S.D != 64 && S.D != 128 && S.D != 256) return DVSSQ_EUNSUPPORTED;
+  const int64_t kvn = static_cast<int64_t>(S.B) * S.Nk * S.Hkv * S.D, qn = static_cast<int64_t>(S.B) * S.Mq * S.Hq * S.D;
+  if (kvn >= (int64_t{1} << 30) || qn >= (int64_t{1} << 30)) return DVSSQ_EUNSUPPORTED;
+  if (overlap(o, 2 * qn, q, 2 * qn) || overlap(o, 2 * qn, k, 2 * kvn) || overlap(o, 2 * qn, v, 2 * kvn))
+    return DVSSQ_EINVAL;
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.o = static_cast<uint16_t *>(o);
+  a.B = S.B;
+  a.Mq = S.Mq;
+  a.Nk = S.Nk;
+  a.Hq = S.Hq;
+  a.Hkv = S.Hkv;
+  a.D = S.D;
+  a.window = S.window;
+  a.rep = S.Hq / S.Hkv;
+  a.rows = S.Mq * a.rep;
+  a.tiles = (a.rows + 63) / 64;
+  a.scale = S.scale;
+  a.haze = S.haze;
+  if (static_cast<int64_t>(a.B) * a.Hkv * a.tiles >= (int64_t{1} << 31)) return DVSSQ_EUNSUPPORTED;
+  return launch_kvbss_attention(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
 const char *dvssq_status_str(int status) {

@@ -639,6 +639,18 @@ QuantizeWs quantize_ws_layout(const dvssq_layout &L, int l);
 hipError_t launch_quantize(const dvssq_layout &L, const uint16_t *W, const double *omega, int l, int power_iters,
                            uint8_t *blob, uint8_t *ws, hipStream_t s);
 
+// KV-BSS attention (attention.hip)
+struct AttnArgs {
+  const uint16_t *q, *k, *v;   // bf16 q [B][Mq][Hq][D], k and v [B][Nk][Hkv][D]
+  uint16_t *o;                 // bf16 [B][Mq][Hq][D]
+  int B, Mq, Nk, Hq, Hkv, D, window;
+  int rep;                     // Hq / Hkv
+  int rows;                    // Mq rep: (query, head) rows of one (sequence, KV head)
+  int tiles;                   // workgroups per (sequence, KV head): ceil(rows / 64)
+  float scale, haze;
+};
+hipError_t launch_kvbss_attention(const AttnArgs &a, hipStream_t s);
+
 // few-token decode (1 <= M <= kGemvMaxM): 32-row tiles on the int8 32x32x32 matrix cores
 constexpr int kGemvMaxM = 4;
 struct GemvArgs {

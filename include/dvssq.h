@@ -17,7 +17,9 @@
  * U, V bf16 rank-r factors of the quantization residual, U = A = U_r sqrt(S_r),
  *      V = B = sqrt(S_r) V_r^T (MiniCPM card, Mathematical Foundations 2).
  *
- * The library only consumes packed layers; it never quantizes.  All device
+ * Beside the layer's forward, the library quantizes a bf16 weight into a
+ * packed layer on the GPU (dvssq_quantize) and runs the cards' KV-BSS
+ * attention (dvssq_kvbss_attention).  All device
  * memory (blob, x, y, workspace) belongs to the caller.  The library never
  * allocates, frees or synchronizes: every call validates its arguments on the
  * host, then enqueues kernels on the caller's HIP stream and returns.  It keeps
@@ -260,8 +262,11 @@ int dvssq_mlp_ws_offsets(const dvssq_layout *gu, const dvssq_layout *down, int64
  * GELU is the exact v Phi(v) = v (1 + erf(v / sqrt 2)) / 2 in fp32; the tensors
  * between the projections are bf16 as in a BF16 model: the fused layer's output
  * is bf16 (as from dvssq_linear_decode), gelu(gate) * up is rounded once to bf16
- * and is the down projection's input.  Three kernel launches on `stream`: the
- * fused decode, the GELU product, the down decode.
+ * and is the down projection's input.  Two kernel launches on `stream` when
+ * the down projection takes the single-launch decode kernels: the fused
+ * decode, then the down decode, which forms gelu(gate) * up where it loads
+ * its input (and also writes it to the workspace); otherwise three: the fused
+ * decode, the GELU product, the down projection.
  * x: device bf16 [M][gu->K] (x.H when flags has DVSSQ_X_ROTATED; the flag
  * concerns x only).  y: device bf16 [M][down->N]; x and y 16-byte aligned and
  * disjoint from each other, from the blobs and from ws.  ws: device,
@@ -293,6 +298,38 @@ int dvssq_mlp_prefill(const dvssq_layout *gu, const void *gu_blob, const dvssq_l
  * 2^40.  One kernel launch on `stream`.
  */
 int dvssq_stream_read(const void *buf, int64_t bytes, void *sink, void *stream);
+
+/*
+ * KV-BSS attention (Spark-X2.5-4B-Hadamard-GSQ model card, section 2, KV-BSS:
+ * focus factor scaling and attention haze truncation; Spark-X2.5-4B discussion
+ * 14, Mathematical Formulation 1-2 and its eager attention change), causal
+ * grouped-query attention as in the Spark model (Spark-X2.5-4B GGUF page, "The
+ * model": 16 query heads, 4 KV heads, head_dim 256, sliding window 512 on the
+ * sliding layers).  For query i of sequence b and query head h:
+ *     position p = Nk - Mq + i (the queries are the last Mq of the Nk tokens),
+ *     visible keys j <= p (and j > p - window when window > 0),
+ *     KV head h / (Hq / Hkv),
+ *     s_j = scale * (q . k_j)          (scale = tau_focus / sqrt(D), tau_focus = 1.10),
+ *     m = max of s_j over the visible keys,
+ *     o = sum exp(s_j - m) v_j / sum exp(s_j - m) over the visible keys with
+ *         s_j >= m - haze (haze = 12.0 on the pages; INFINITY keeps every key).
+ * q and o: device bf16 [B][Mq][Hq][D]; k and v: device bf16 [B][Nk][Hkv][D];
+ * all 16-byte aligned; o disjoint from q, k and v.  D is 64, 128 or 256
+ * (DVSSQ_EUNSUPPORTED otherwise); 1 <= Mq <= Nk; Hq a multiple of Hkv; window
+ * >= 0; scale finite; haze >= 0 (not NaN); B Nk Hkv D and B Mq Hq D below 2^30
+ * (DVSSQ_EUNSUPPORTED above).  Logits and sums in fp32 (the logits from bf16
+ * products on the matrix cores), exp(s - m) rounded to bf16 for the product
+ * with v, output rounded to bf16.  One kernel launch on `stream`; no workspace.
+ */
+typedef struct dvssq_attn_shape {
+  int32_t B, Mq, Nk, Hq, Hkv, D;
+  int32_t window;       /* 0: full causal attention */
+  float scale;          /* logit multiplier */
+  float haze;           /* keys below the row maximum minus haze are dropped */
+} dvssq_attn_shape;
+
+int dvssq_kvbss_attention(const dvssq_attn_shape *shape, const void *q, const void *k, const void *v, void *o,
+                          void *stream);
 
 /* Static text for a return code. */
 const char *dvssq_status_str(int status);

@@ -315,3 +315,29 @@ def test_quantize_error_paths():
     # one rotation row (fp64 + codes) must fit the 160 KB of LDS
     big = dv.pack_info(512, 16384, 4, 256, 1)
     assert c(L=big) == dv.DVSSQ_EUNSUPPORTED
+
+
+def test_kvbss_attention_error_paths():
+    """Every argument check of the attention call runs before its launch."""
+    f, E = dv.lib().dvssq_kvbss_attention, dv.DVSSQ_EINVAL
+    O = 0x60000000
+
+    def shape(**kw):
+        d = dict(B=1, Mq=4, Nk=64, Hq=16, Hkv=4, D=256, window=0, scale=0.06875, haze=12.0)
+        d.update(kw)
+        return dv.AttnShape(**d)
+
+    def c(sh=None, q=X, k=BLOB, v=WS, o=O):
+        return f(C.byref(sh if sh is not None else shape()), q, k, v, o, None)
+
+    assert f(None, X, BLOB, WS, O, None) == E
+    assert c(q=None) == E and c(k=None) == E and c(v=None) == E and c(o=None) == E
+    assert c(shape(Mq=65)) == E                    # more queries than keys
+    assert c(shape(Mq=0)) == E and c(shape(B=0)) == E
+    assert c(shape(Hq=6)) == E                     # not a multiple of Hkv
+    assert c(shape(window=-1)) == E
+    assert c(shape(scale=float("inf"))) == E and c(shape(haze=float("nan"))) == E and c(shape(haze=-1.0)) == E
+    assert c(q=X + 8) == E and c(o=O + 2) == E
+    assert c(o=X + 64) == E                        # output overlaps q
+    assert c(shape(D=96)) == dv.DVSSQ_EUNSUPPORTED
+    assert c(shape(B=1, Nk=1 << 20, Hkv=4, D=256)) == dv.DVSSQ_EUNSUPPORTED
