@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only-prefill", action="store_true",
                     help="time only the prefill shapes (for kernel traces of the prefill path)")
+    ap.add_argument("--only-attention", action="store_true",
+                    help="time only the attention shapes (for kernel traces of the attention kernel)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 256 MiB device copy (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -290,6 +292,38 @@ def prefill_table(dv, torch, layers, steps):
     return table
 
 
+def attention_pairs(Mq, Nk, window):
+    """(query, visible key) pairs of one head: causal, optional sliding window."""
+    p = np.arange(Nk - Mq, Nk, dtype=np.int64)
+    lo = np.maximum(0, p - window + 1) if window > 0 else np.zeros_like(p)
+    return int((p - lo + 1).sum())
+
+
+def attention_table(dv, torch, steps=20):
+    """dvssq_kvbss_attention on the Spark attention heads (16 query heads, 4 KV
+    heads, head_dim 256): a 2048-token prefill of a full layer and of a sliding
+    (window 512) layer.  Algorithmic FLOPs: 4 D per (query, visible key) pair
+    and head (Q K^T and P V), against the dense bf16 matrix-core peak."""
+    import synth
+    out = []
+    B, Mq, Nk, Hq, Hkv, D = 1, 2048, 2048, 16, 4, 256
+    q, k, v = synth.attention_qkv(0, "spark_prefill", B, Mq, Nk, Hq, Hkv, D)
+    qd, kd, vd = (torch.from_numpy(a.view(np.int16)).cuda() for a in (q, k, v))
+    o = torch.empty_like(qd)
+    st = torch.cuda.current_stream().cuda_stream
+    for window in (0, 512):
+        sh = dv.AttnShape(B=B, Mq=Mq, Nk=Nk, Hq=Hq, Hkv=Hkv, D=D, window=window,
+                          scale=float(np.float32(1.10 / math.sqrt(D))), haze=12.0)
+        t, _ = time_calls(torch, lambda i: dv.kvbss_attention(sh, qd, kd, vd, o, st), steps, 3)
+        fl = 4.0 * D * Hq * B * attention_pairs(Mq, Nk, window)
+        tf = fl / (t * 1e-3) / 1e12
+        out.append({"workload": f"KV-BSS attention prefill, Spark heads (Hq=16, Hkv=4, D=256), {Mq} tokens, "
+                                f"window {window or 'none'}", "us_per_call": round(t * 1e3, 2),
+                    "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
+    del qd, kd, vd, o
+    return out
+
+
 def quantize_table(dv, torch, layers, steps=3):
     """dvssq_quantize (weights to packed layer, on the GPU) on the spark MLP
     shapes, sketch width l = r + 8 and two power iterations."""
@@ -326,6 +360,9 @@ def main():
     layers = {l.name: l for w in synth.WORKLOADS.values() for l in w.layers}
     if args.only_prefill:
         print(json.dumps({"prefill_table": prefill_table(dv, torch, layers, args.prefill_steps)}), flush=True)
+        return
+    if args.only_attention:
+        print(json.dumps({"attention_table": attention_table(dv, torch)}), flush=True)
         return
     up = layers["spark_up"]
     M = args.decode_m
@@ -377,6 +414,7 @@ def main():
                           "us_per_call": round(t * 1e3, 3), "gbs": round(g, 1), "frac_hbm": round(g / HBM_PEAK_GBS, 4)})
             r.free()
         table += prefill_table(dv, torch, layers, args.prefill_steps)
+        table += attention_table(dv, torch)
         table += quantize_table(dv, torch, layers)
         out["table"] = table
     if not args.no_cpu:

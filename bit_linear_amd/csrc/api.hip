@@ -654,7 +654,7 @@ int dvssq_kvbss_attention(const dvssq_attn_shape *sh, const void *q, const void 
   a.window = S.window;
   a.rep = S.Hq / S.Hkv;
   a.rows = S.Mq * a.rep;
-  a.tiles = (a.rows + 63) / 64;
+  a.tiles = (a.rows + 16 * attn_waves(a.D) - 1) / (16 * attn_waves(a.D));
   a.scale = S.scale;
   a.haze = S.haze;
   if (static_cast<int64_t>(a.B) * a.Hkv * a.tiles >= (int64_t{1} << 31)) return DVSSQ_EUNSUPPORTED;

@@ -14,232 +14,280 @@
 // which needs no rescaling of the running sums.  The cost is one more
 // Q K^T product per key block.
 //
-// Workgroup: 4 wavefronts, 64 rows of one (sequence, KV head): the rows are
-// the (query, head) pairs of the KV head's query group, query-major, so every
-// row of the tile reads the same K and V.  Wavefront w owns rows 16 w .. 16 w
-// + 15: their q in registers (the A operand of v_mfma_f32_16x16x32_bf16: lane
-// l holds row l % 16, dims 8 (l / 16) .. + 7 of each 32-dim step), the output
-// accumulators D / 16 tiles of 16 x 16 in registers.  Per block of 64 keys:
-// K [64][D] is staged in LDS row-major (the B operand reads 16 bytes of a key
-// row), V transposed [D][64] (the B operand of P V reads 8 keys of one dim),
-// and each wavefront's P [16][64] (bf16) goes through LDS to become the A
-// operand of P V.  fp32 logits and sums; P rounded to bf16 for the matrix
-// cores; output bf16.
+// Workgroup: W = 4 wavefronts, 64 rows of one (sequence, KV head): the rows
+// are the (query, head) pairs of the KV head's query group, query-major, so
+// every row of the tile reads the same K and V.  Wavefront w owns rows 16 w
+// .. 16 w + 15.  Keys go in blocks of 32, K and V each staged row-major in LDS
+// by buffer-to-LDS loads (no registers), double-buffered in four LDS arrays of
+// their own (so the compiler can tell the block being read from the one being
+// filled) so that the next block's loads run under the current block's
+// matrix-core work.  Per block and wavefront (v_mfma_f32_16x16x32_bf16, lane
+// l = (i = l % 16, g = l / 16)):
+//   S^T = K Q^T: A = 16 keys x 32 dims of K (lane: key i, dims 8 g .. + 7),
+//       B = the wavefront's q (lane: row i, dims 8 g .. + 7, in registers);
+//       lane l gets S[row i][keys 4 g .. 4 g + 3] of the 16-key tile;
+//   O += P V: A = P, built in registers from the two tiles' S^T values (slots
+//       0-3: keys 4 g + e, slots 4-7: keys 16 + 4 g + e); B = V, whose
+//       matching keys (4 consecutive per 64-bit read) come from LDS by the
+//       transposing read ds_read_b64_tr_b16: within 16 lanes, lane 4 j + c
+//       points at key row j, dims 4 c .. 4 c + 3, and lane i receives dim i
+//       of the four rows.
+// Every operand read of a block is issued before its first matrix-core
+// instruction.  LDS rows are 2 D bytes; the 16-byte chunks of key row k sit
+// XOR-swizzled by sw(k) (two bits of k per position), so that both the K
+// reads (16 keys, one chunk) and the transposing V reads (4 keys, two
+// chunks) hit distinct banks.  fp32 logits and sums; P rounded to bf16 for
+// the matrix cores; output bf16.
 #include "dvssq_internal.h"
 
 namespace dvssq {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerWg = 64;
-constexpr int kKeys = 64;            // keys per block
+constexpr int kKeys = 32;            // keys per block
 constexpr float kLog2e = 1.4426950408889634f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct AttnLds {
-  static constexpr int KS = D + 8;          // K row stride (bf16)
-  static constexpr int VS = kKeys + 8;      // transposed V row stride (bf16)
-  static constexpr int PS = kKeys + 8;      // P row stride (bf16)
-  static constexpr int bytes = (kKeys * KS + D * VS + 4 * 16 * PS) * 2;
+  static constexpr int kBlock = kKeys * D * 2;    // bytes of one K or V block
 };
 
-// Stage K block [kb, kb + 64) of KV head g into LDS (zeros past the end of
-// the sequence; those keys are never visible)
+// chunk swizzle of key row k: D / 8 chunks of 16 bytes per row
 template <int D>
-__device__ __forceinline__ void stage_k(const AttnArgs &a, __amdgpu_buffer_rsrc_t rk, int b, int g, int kb,
-                                        uint16_t *ks) {
-  constexpr int CH = D / 8;                 // 16-byte chunks of a key row
-  for (int c = threadIdx.x; c < kKeys * CH; c += kThreads) {
-    const int row = c / CH, col = c - row * CH;
+__device__ __forceinline__ int swz(int k) {
+  if constexpr (D >= 128) return (2 * (k & 7)) ^ ((k >> 3) & 1);
+  else return (2 * (k & 3)) ^ ((k >> 2) & 1);
+}
+
+// Buffer-to-LDS loads of key block [kb, kb + 32) of KV head g (K or V) into
+// dst; keys past the end of the sequence read zeros.  Each of the W
+// wavefronts issues D / (16 W) loads of 1 KB (lane l's 16 bytes land at byte
+// 16 l).
+template <int D, int W>
+__device__ __forceinline__ void stage(const AttnArgs &a, __amdgpu_buffer_rsrc_t rs, int b, int g, int kb, uint8_t *dst,
+                                      int wave, int lane) {
+  constexpr int PER = D / (16 * W);
+  static_assert(PER >= 1, "one 1 KB load per wavefront at least");
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int o = 1024 * (wave * PER + t) + 16 * lane;     // LDS byte of this lane
+    const int row = o / (2 * D), c = (o % (2 * D)) / 16;
     const int j = kb + row;
     const uint32_t off =
-        j < a.Nk ? static_cast<uint32_t>(((static_cast<int64_t>(b) * a.Nk + j) * a.Hkv + g) * D + 8 * col) * 2
+        j < a.Nk ? static_cast<uint32_t>((((static_cast<int64_t>(b) * a.Nk + j) * a.Hkv + g) * D + 8 * (c ^ swz<D>(row))) * 2)
                  : kOutOfRange;
-    *reinterpret_cast<u32x4 *>(ks + row * AttnLds<D>::KS + 8 * col) = buf_load16(rk, off);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(dst + 1024 * (wave * PER + t)),
+                                             16, off, 0, 0, 0);
   }
 }
 
-// Stage V block transposed: vt[d][key]; each thread takes a pair of keys and
-// 8 dims and writes the 8 (key, key + 1) pairs as 32-bit words
+// S^T tiles of the wavefront's 16 rows against the 32 keys of a K block:
+// s[nt][v] = S[row l % 16][key 16 nt + 4 (l / 16) + v], unscaled.  Every
+// operand read of the block is issued before the first matrix-core
+// instruction, so the LDS latency is waited for once per block.
 template <int D>
-__device__ __forceinline__ void stage_vt(const AttnArgs &a, __amdgpu_buffer_rsrc_t rv, int b, int g, int kb,
-                                         uint16_t *vt) {
-  constexpr int CH = D / 8;
-  for (int c = threadIdx.x; c < (kKeys / 2) * CH; c += kThreads) {
-    const int jp = c % (kKeys / 2), col = c / (kKeys / 2);
-    const int j = kb + 2 * jp;
-    const int64_t base = ((static_cast<int64_t>(b) * a.Nk + j) * a.Hkv + g) * D + 8 * col;
-    const u32x4 v0 = buf_load16(rv, j < a.Nk ? static_cast<uint32_t>(base * 2) : kOutOfRange);
-    const u32x4 v1 = buf_load16(rv, j + 1 < a.Nk ? static_cast<uint32_t>((base + static_cast<int64_t>(a.Hkv) * D) * 2)
-                                                 : kOutOfRange);
+__device__ __forceinline__ void logits_t(const u32x4 (&qa)[D / 32], const uint8_t *kblk, int lane, f32x4 (&s)[2]) {
+  const int i = lane & 15, gq = lane >> 4;
+  u32x4 ka[2][D / 32];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // dims 8 col + 2 e (low halves) and 8 col + 2 e + 1 (high halves)
-      const uint32_t lo = (v0[e] & 0xFFFFu) | (v1[e] << 16);
-      const uint32_t hi = (v0[e] >> 16) | (v1[e] & 0xFFFF0000u);
-      *reinterpret_cast<uint32_t *>(vt + (8 * col + 2 * e) * AttnLds<D>::VS + 2 * jp) = lo;
-      *reinterpret_cast<uint32_t *>(vt + (8 * col + 2 * e + 1) * AttnLds<D>::VS + 2 * jp) = hi;
-    }
+  for (int nt = 0; nt < 2; ++nt) {
+    const int key = 16 * nt + i;
+    const uint8_t *kr = kblk + key * 2 * D;
+    const int w = gq ^ swz<D>(key);            // chunk 4 st + g sits at slot (4 st + g) ^ sw = w ^ 4 st
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) ka[nt][st] = *reinterpret_cast<const u32x4 *>(kr + 16 * (w ^ (4 * st)));
   }
-}
-
-// logits of the wavefront's 16 rows against the 64 keys in LDS: s[nt] is the
-// 16 x 16 tile of keys 16 nt .. 16 nt + 15 (lane l: rows 4 (l / 16) + v, key
-// 16 nt + l % 16), unscaled
-template <int D>
-__device__ __forceinline__ void logits(const u32x4 (&qa)[D / 32], const uint16_t *ks, int lane, f32x4 (&s)[4]) {
-  const int n = lane & 15, qd = lane >> 4;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < 2; ++nt) {
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint16_t *kr = ks + (16 * nt + n) * AttnLds<D>::KS + 8 * qd;
 #pragma unroll
-    for (int st = 0; st < D / 32; ++st) acc = mfma_bf16(qa[st], *reinterpret_cast<const u32x4 *>(kr + 32 * st), acc);
+    for (int st = 0; st < D / 32; ++st) acc = mfma_bf16(ka[nt][st], qa[st], acc);
     s[nt] = acc;
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void kvbss_attention_kernel(AttnArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  using LD = AttnLds<D>;
-  uint16_t *ks = reinterpret_cast<uint16_t *>(smem);
-  uint16_t *vt = ks + kKeys * LD::KS;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, qd = lane >> 4;
-  uint16_t *ps = vt + D * LD::VS + wave * 16 * LD::PS;
+constexpr int kVm0 = 0x0F70;    // s_waitcnt vmcnt(0), the other counters free
 
-  // heaviest tiles (latest queries, most keys) first
-  const int per_seq = a.Hkv * a.tiles;
-  const int b = blockIdx.x / per_seq;
-  const int rem = blockIdx.x - b * per_seq;
-  const int g = rem / a.tiles;
-  const int tile = a.tiles - 1 - (rem - g * a.tiles);
+// Per-row state of a wavefront lane (row 16 w + l % 16 of the tile).
+struct RowState {
+  int pos, jlo;        // position, first visible key
+  bool rok;            // the row exists
+};
+
+// Pass 1 on block t (keys kb .. kb + 31) held in kcur; the next block is
+// staged into knxt meanwhile.  kcur and knxt are distinct LDS arrays, so the
+// compiler sees that the reads of kcur do not wait for the copy into knxt.
+template <int D, int W>
+__device__ __forceinline__ void max_block(const AttnArgs &a, __amdgpu_buffer_rsrc_t rk, int b, int g, int kb,
+                                          bool more, const uint8_t *kcur, uint8_t *knxt, const u32x4 (&qa)[D / 32],
+                                          const RowState &rs, int wave, int lane, float &mx) {
+  const int gq = lane >> 4;
+  __builtin_amdgcn_s_waitcnt(kVm0);
+  __syncthreads();                           // block t in LDS; block t - 1 no longer read
+  if (more) stage<D, W>(a, rk, b, g, kb + kKeys, knxt, wave, lane);
+  f32x4 s[2];
+  logits_t<D>(qa, kcur, lane, s);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = kb + 16 * nt + 4 * gq + v;
+      if (j <= rs.pos && j >= rs.jlo) mx = fmaxf(mx, s[nt][v] * a.scale);
+    }
+}
+
+// Pass 2 on block t: O += P V and l += sum P over the kept keys, with the
+// next block's K and V staged into knxt / vnxt meanwhile.
+template <int D, int W>
+__device__ __forceinline__ void sum_block(const AttnArgs &a, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          int b, int g, int kb, bool more, const uint8_t *kcur, const uint8_t *vcur,
+                                          uint8_t *knxt, uint8_t *vnxt, const u32x4 (&qa)[D / 32], const RowState &rs,
+                                          float thr, float mb, int wave, int lane, f32x4 (&oacc)[D / 16], float &lsum) {
+  const int i = lane & 15, gq = lane >> 4;
+  const int vj = i >> 2, vc = i & 3;         // transposing reads: lane 4 j + c points at key row j, dims 4 c ..
+  __builtin_amdgcn_s_waitcnt(kVm0);
+  __syncthreads();
+  if (more) {
+    stage<D, W>(a, rk, b, g, kb + kKeys, knxt, wave, lane);
+    stage<D, W>(a, rv, b, g, kb + kKeys, vnxt, wave, lane);
+  }
+  f32x4 s[2];
+  logits_t<D>(qa, kcur, lane, s);
+  // key rows of the two reads (keys 4 g + j and 16 + 4 g + j), this lane's
+  // half chunk; chunk 2 dt + (c >> 1) of a row sits at slot (2 dt + (c >> 1)) ^ sw
+  const int k0 = 4 * gq + vj, k1 = 16 + 4 * gq + vj;
+  const uint8_t *v0 = vcur + k0 * 2 * D + 8 * (vc & 1), *v1 = vcur + k1 * 2 * D + 8 * (vc & 1);
+  const int u0 = (vc >> 1) ^ swz<D>(k0), u1 = (vc >> 1) ^ swz<D>(k1);
+  u32x4 vop[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(v0 + 16 * (u0 ^ (2 * dt))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(v1 + 16 * (u1 ^ (2 * dt))));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    vop[dt] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+  float p[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = kb + 16 * nt + 4 * gq + v;
+      const float sv = s[nt][v] * a.scale;
+      const bool keep = rs.rok && j <= rs.pos && j >= rs.jlo && !(sv < thr);
+      p[nt][v] = keep ? __builtin_amdgcn_exp2f(sv * kLog2e - mb) : 0.0f;   // argument in [-17.4, 0]
+      lsum += p[nt][v];
+    }
+  u32x4 pa;
+  pa[0] = pack_bf16x2(p[0][0], p[0][1]);
+  pa[1] = pack_bf16x2(p[0][2], p[0][3]);
+  pa[2] = pack_bf16x2(p[1][0], p[1][1]);
+  pa[3] = pack_bf16x2(p[1][2], p[1][3]);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = mfma_bf16(pa, vop[dt], oacc[dt]);
+}
+
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void kvbss_attention_kernel(AttnArgs a) {
+  constexpr int kRowsPerWg = 16 * W;
+  // K and V blocks, two buffers each, as four arrays of their own
+  __shared__ __align__(16) uint8_t k0buf[AttnLds<D>::kBlock], k1buf[AttnLds<D>::kBlock];
+  __shared__ __align__(16) uint8_t v0buf[AttnLds<D>::kBlock], v1buf[AttnLds<D>::kBlock];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, gq = lane >> 4;
+
+  // Work rank: tiles of later queries see more keys.  The first half of the
+  // grid takes the ranks heaviest first, the second half lightest first, so
+  // that the two workgroups a compute unit receives (the dispatcher places
+  // the first half, then the second) carry about the same work together.
+  const int nseq = a.B * a.Hkv, total = nseq * a.tiles, half = (total + 1) / 2;
+  const int k = static_cast<int>(blockIdx.x);
+  const int rank = k < half ? k : total - 1 - (k - half);
+  const int tile = a.tiles - 1 - rank / nseq;
+  const int bg = rank - (rank / nseq) * nseq;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int r0 = tile * kRowsPerWg;
   const int r1 = min(a.rows, r0 + kRowsPerWg) - 1;       // last row of the tile
   const int p0 = a.Nk - a.Mq;                             // position of query 0
   const int pmin = p0 + r0 / a.rep, pmax = p0 + r1 / a.rep;
   const int klo = a.window > 0 ? max(0, pmin - a.window + 1) : 0;
   const int kb0 = klo & ~(kKeys - 1);
+  const int nblk = (pmax - kb0) / kKeys + 1;
 
-  const auto rk = make_rsrc(a.k, static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.Nk * a.Hkv * D * 2));
-  const auto rv = make_rsrc(a.v, static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.Nk * a.Hkv * D * 2));
+  const uint32_t kvbytes = static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.Nk * a.Hkv * D * 2);
+  const auto rk = make_rsrc(a.k, kvbytes);
+  const auto rv = make_rsrc(a.v, kvbytes);
   const auto rq = make_rsrc(a.q, static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.Mq * a.Hq * D * 2));
 
-  // q of row 16 wave + n (A operand); rows past the end read zeros
+  // this lane's row 16 wave + i: q (B operand of S^T), position, first visible key
+  const int r = r0 + 16 * wave + i;
+  const int ri = r / a.rep;
+  RowState rs;
+  rs.rok = r < a.rows;
+  rs.pos = rs.rok ? p0 + ri : -1;
+  rs.jlo = a.window > 0 ? rs.pos - a.window + 1 : 0;
   u32x4 qa[D / 32];
   {
-    const int r = r0 + 16 * wave + n;
-    const int i = r / a.rep, h = g * a.rep + (r - i * a.rep);
-    const bool ok = r < a.rows;
-    const uint32_t base = ok ? static_cast<uint32_t>((((static_cast<int64_t>(b) * a.Mq + i) * a.Hq + h) * D + 8 * qd) * 2)
-                             : kOutOfRange;
+    const int h = g * a.rep + (r - ri * a.rep);
+    const uint32_t base = static_cast<uint32_t>((((static_cast<int64_t>(b) * a.Mq + ri) * a.Hq + h) * D + 8 * gq) * 2);
 #pragma unroll
-    for (int st = 0; st < D / 32; ++st) qa[st] = buf_load16(rq, ok ? base + 64 * st : kOutOfRange);
-  }
-  // this lane's accumulator rows 16 wave + 4 qd + v: position and first visible key
-  int pos[4], jlo[4];
-  bool rok[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int r = r0 + 16 * wave + 4 * qd + v;
-    rok[v] = r < a.rows;
-    pos[v] = rok[v] ? p0 + r / a.rep : -1;
-    jlo[v] = a.window > 0 ? pos[v] - a.window + 1 : 0;
+    for (int st = 0; st < D / 32; ++st) qa[st] = buf_load16(rq, rs.rok ? base + 64 * st : kOutOfRange);
   }
 
-  // ---- pass 1: row maxima of the scaled logits over the visible keys
-  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  for (int kb = kb0; kb <= pmax; kb += kKeys) {
-    __syncthreads();
-    stage_k<D>(a, rk, b, g, kb, ks);
-    __syncthreads();
-    f32x4 s[4];
-    logits<D>(qa, ks, lane, s);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int j = kb + 16 * nt + n;
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (j <= pos[v] && j >= jlo[v]) mx[v] = fmaxf(mx[v], s[nt][v] * a.scale);
-    }
+  // ---- pass 1: the row maximum of the scaled logits over the visible keys
+  float mx = -INFINITY;
+  stage<D, W>(a, rk, b, g, kb0, k0buf, wave, lane);
+  for (int t = 0; t < nblk; t += 2) {
+    max_block<D, W>(a, rk, b, g, kb0 + t * kKeys, t + 1 < nblk, k0buf, k1buf, qa, rs, wave, lane, mx);
+    if (t + 1 < nblk)
+      max_block<D, W>(a, rk, b, g, kb0 + (t + 1) * kKeys, t + 2 < nblk, k1buf, k0buf, qa, rs, wave, lane, mx);
   }
-#pragma unroll
-  for (int v = 0; v < 4; ++v)
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) mx[v] = fmaxf(mx[v], __shfl_xor(mx[v], o, 64));
-  float thr[4], mb[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    thr[v] = mx[v] - a.haze;            // keys below are dropped
-    mb[v] = rok[v] ? mx[v] * kLog2e : 0.0f;
-  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float thr = mx - a.haze;             // keys below are dropped
+  const float mb = rs.rok ? mx * kLog2e : 0.0f;
 
-  // ---- pass 2: o = sum exp(s - m) v over the kept keys, l = sum exp(s - m)
+  // ---- pass 2: O = sum exp(s - m) v over the kept keys, l = sum exp(s - m)
   f32x4 oacc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int kb = kb0; kb <= pmax; kb += kKeys) {
-    __syncthreads();
-    stage_k<D>(a, rk, b, g, kb, ks);
-    stage_vt<D>(a, rv, b, g, kb, vt);
-    __syncthreads();
-    f32x4 s[4];
-    logits<D>(qa, ks, lane, s);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int j = kb + 16 * nt + n;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float sv = s[nt][v] * a.scale;
-        const bool keep = rok[v] && j <= pos[v] && j >= jlo[v] && !(sv < thr[v]);
-        const float p = keep ? exp2f(sv * kLog2e - mb[v]) : 0.0f;
-        lsum[v] += p;
-        ps[(4 * qd + v) * LD::PS + 16 * nt + n] = f32_to_bf16(p);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's P is in LDS
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int st = 0; st < kKeys / 32; ++st) {
-      const u32x4 pa = *reinterpret_cast<const u32x4 *>(ps + n * LD::PS + 32 * st + 8 * qd);
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const u32x4 vb = *reinterpret_cast<const u32x4 *>(vt + (16 * dt + n) * LD::VS + 32 * st + 8 * qd);
-        oacc[dt] = mfma_bf16(pa, vb, oacc[dt]);
-      }
-    }
+  float lsum = 0.0f;
+  __syncthreads();                           // pass 1's last block no longer read
+  stage<D, W>(a, rk, b, g, kb0, k0buf, wave, lane);
+  stage<D, W>(a, rv, b, g, kb0, v0buf, wave, lane);
+  for (int t = 0; t < nblk; t += 2) {
+    sum_block<D, W>(a, rk, rv, b, g, kb0 + t * kKeys, t + 1 < nblk, k0buf, v0buf, k1buf, v1buf, qa, rs, thr, mb, wave,
+                 lane, oacc, lsum);
+    if (t + 1 < nblk)
+      sum_block<D, W>(a, rk, rv, b, g, kb0 + (t + 1) * kKeys, t + 2 < nblk, k1buf, v1buf, k0buf, v0buf, qa, rs, thr, mb,
+                   wave, lane, oacc, lsum);
   }
-#pragma unroll
-  for (int v = 0; v < 4; ++v)
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) lsum[v] += __shfl_xor(lsum[v], o, 64);
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
 
-  // ---- output rows 16 wave + 4 qd + v, dims 16 dt + n
+  // ---- output: lane (n = l % 16, g) holds rows 16 wave + 4 g + v, dims 16 dt + n
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    if (!rok[v]) continue;
-    const int r = r0 + 16 * wave + 4 * qd + v;
-    const int i = r / a.rep, h = g * a.rep + (r - i * a.rep);
-    uint16_t *orow = a.o + ((static_cast<int64_t>(b) * a.Mq + i) * a.Hq + h) * D;
-    const float inv = 1.0f / lsum[v];
+    const int rr = r0 + 16 * wave + 4 * gq + v;
+    const float l = __shfl(lsum, 4 * gq + v, 64);       // lanes 0 .. 15 hold rows 0 .. 15
+    if (rr >= a.rows) continue;
+    const int ii = rr / a.rep, h = g * a.rep + (rr - ii * a.rep);
+    uint16_t *orow = a.o + ((static_cast<int64_t>(b) * a.Mq + ii) * a.Hq + h) * D;
+    const float inv = 1.0f / l;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) orow[16 * dt + n] = f32_to_bf16(oacc[dt][v] * inv);
+    for (int dt = 0; dt < D / 16; ++dt) orow[16 * dt + i] = f32_to_bf16(oacc[dt][v] * inv);
   }
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs &a, hipStream_t s) {
-  const size_t lds = AttnLds<D>::bytes;
-  if (lds > 65536) {
-    static std::atomic<uint64_t> done{0};
-    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kvbss_attention_kernel<D>), 160 * 1024, done);
-    if (e != hipSuccess) return e;
-  }
+  // static LDS only (the four block buffers); tiles of 16 W rows
+  constexpr int W = attn_waves(D);
   const int grid = a.B * a.Hkv * a.tiles;
-  return launch_kernel(reinterpret_cast<const void *>(kvbss_attention_kernel<D>), dim3(grid), dim3(kThreads), lds, s,
+  return launch_kernel(reinterpret_cast<const void *>(kvbss_attention_kernel<D, W>), dim3(grid), dim3(64 * W), 0, s,
                        a);
 }
 

@@ -646,10 +646,12 @@ struct AttnArgs {
   int B, Mq, Nk, Hq, Hkv, D, window;
   int rep;                     // Hq / Hkv
   int rows;                    // Mq rep: (query, head) rows of one (sequence, KV head)
-  int tiles;                   // workgroups per (sequence, KV head): ceil(rows / 64)
+  int tiles;                   // workgroups per (sequence, KV head): ceil(rows / (16 attn_waves(D)))
   float scale, haze;
 };
 hipError_t launch_kvbss_attention(const AttnArgs &a, hipStream_t s);
+// wavefronts per attention workgroup (each takes 16 rows of the tile)
+constexpr int attn_waves(int) { return 4; }
 
 // few-token decode (1 <= M <= kGemvMaxM): 32-row tiles on the int8 32x32x32 matrix cores
 constexpr int kGemvMaxM = 4;
