@@ -302,25 +302,43 @@ def attention_pairs(Mq, Nk, window):
 def attention_table(dv, torch, steps=20):
     """dvssq_kvbss_attention on the Spark attention heads (16 query heads, 4 KV
     heads, head_dim 256): a 2048-token prefill of a full layer and of a sliding
-    (window 512) layer.  Algorithmic FLOPs: 4 D per (query, visible key) pair
-    and head (Q K^T and P V), against the dense bf16 matrix-core peak."""
+    (window 512) layer, against the dense bf16 matrix-core peak (algorithmic
+    FLOPs: 4 D per (query, visible key) pair and head, Q K^T and P V); and one
+    decode step over a 32768-token context (1 and 8 sequences), against the HBM
+    peak (algorithmic bytes: the visible keys' K and V, q and o)."""
     import synth
     out = []
-    B, Mq, Nk, Hq, Hkv, D = 1, 2048, 2048, 16, 4, 256
+    D = 256
+    scale = float(np.float32(1.10 / math.sqrt(D)))
+    st = torch.cuda.current_stream().cuda_stream
+    B, Mq, Nk, Hq, Hkv = 1, 2048, 2048, 16, 4
     q, k, v = synth.attention_qkv(0, "spark_prefill", B, Mq, Nk, Hq, Hkv, D)
     qd, kd, vd = (torch.from_numpy(a.view(np.int16)).cuda() for a in (q, k, v))
     o = torch.empty_like(qd)
-    st = torch.cuda.current_stream().cuda_stream
     for window in (0, 512):
-        sh = dv.AttnShape(B=B, Mq=Mq, Nk=Nk, Hq=Hq, Hkv=Hkv, D=D, window=window,
-                          scale=float(np.float32(1.10 / math.sqrt(D))), haze=12.0)
-        t, _ = time_calls(torch, lambda i: dv.kvbss_attention(sh, qd, kd, vd, o, st), steps, 3)
+        sh = dv.AttnShape(B=B, Mq=Mq, Nk=Nk, Hq=Hq, Hkv=Hkv, D=D, window=window, scale=scale, haze=12.0)
+        t, _ = time_calls(torch, lambda i: dv.kvbss_attention(sh, qd, kd, vd, o, None, st), steps, 3)
         fl = 4.0 * D * Hq * B * attention_pairs(Mq, Nk, window)
         tf = fl / (t * 1e-3) / 1e12
         out.append({"workload": f"KV-BSS attention prefill, Spark heads (Hq=16, Hkv=4, D=256), {Mq} tokens, "
                                 f"window {window or 'none'}", "us_per_call": round(t * 1e3, 2),
                     "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4)})
     del qd, kd, vd, o
+    Nk = 32768
+    q, k, v = synth.attention_qkv(0, "spark_decode", 1, 1, Nk, Hq, Hkv, D)
+    for B in (1, 8):
+        # B sequences: the one generated sequence's q, k and v repeated (same timing, distinct memory)
+        qd, kd, vd = (torch.from_numpy(np.ascontiguousarray(np.repeat(a, B, axis=0)).view(np.int16)).cuda()
+                      for a in (q, k, v))
+        o = torch.empty_like(qd)
+        sh = dv.AttnShape(B=B, Mq=1, Nk=Nk, Hq=Hq, Hkv=Hkv, D=D, window=0, scale=scale, haze=12.0)
+        ws = dv.device_buffer(max(dv.kvbss_attention_ws_bytes(sh), 1))
+        t, _ = time_calls(torch, lambda i: dv.kvbss_attention(sh, qd, kd, vd, o, ws, st), steps, 3)
+        nbytes = B * (2 * Nk * Hkv * D * 2 + 2 * 2 * Hq * D)
+        g = nbytes / (t * 1e-3) / 1e9
+        out.append({"workload": f"KV-BSS attention decode step, Spark heads, {Nk}-token context, {B} sequence(s)",
+                    "us_per_call": round(t * 1e3, 2), "gbs": round(g, 1), "frac_hbm": round(g / HBM_PEAK_GBS, 4)})
+        del qd, kd, vd, o, ws
     return out
 
 

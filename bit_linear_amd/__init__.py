@@ -31,7 +31,7 @@ DECODE_MAX_M = 32
 EXPORTS = ("dvssq_pack_info", "dvssq_fwht", "dvssq_linear_decode", "dvssq_linear_prefill",
            "dvssq_materialize", "dvssq_mlp_ws_bytes", "dvssq_mlp_ws_offsets", "dvssq_mlp_decode",
            "dvssq_mlp_prefill", "dvssq_stream_read", "dvssq_linear_decode_noalloc", "dvssq_quantize_ws_bytes",
-           "dvssq_quantize", "dvssq_kvbss_attention", "dvssq_status_str")
+           "dvssq_quantize", "dvssq_kvbss_attention_ws_bytes", "dvssq_kvbss_attention", "dvssq_status_str")
 
 
 class Layout(C.Structure):
@@ -95,7 +95,9 @@ _lib.dvssq_quantize_ws_bytes.argtypes = [C.POINTER(Layout), C.c_int32]
 _lib.dvssq_quantize.restype = C.c_int
 _lib.dvssq_quantize.argtypes = [C.POINTER(Layout), _P, _P, C.c_int32, C.c_int32, _P, _P, _P]
 _lib.dvssq_kvbss_attention.restype = C.c_int
-_lib.dvssq_kvbss_attention.argtypes = [C.POINTER(AttnShape), _P, _P, _P, _P, _P]
+_lib.dvssq_kvbss_attention.argtypes = [C.POINTER(AttnShape), _P, _P, _P, _P, _P, _P]
+_lib.dvssq_kvbss_attention_ws_bytes.restype = C.c_int
+_lib.dvssq_kvbss_attention_ws_bytes.argtypes = [C.POINTER(AttnShape), C.POINTER(C.c_int64)]
 _lib.dvssq_stream_read.restype = C.c_int
 _lib.dvssq_stream_read.argtypes = [_P, C.c_int64, _P, _P]
 _lib.dvssq_status_str.restype = C.c_char_p
@@ -174,8 +176,14 @@ def quantize(layout: Layout, W, omega, l: int, power_iters: int, blob, ws, strea
                                _stream(stream)), "dvssq_quantize")
 
 
-def kvbss_attention(shape: AttnShape, q, k, v, o, stream=None) -> None:
-    _check(_lib.dvssq_kvbss_attention(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _stream(stream)),
+def kvbss_attention_ws_bytes(shape: AttnShape) -> int:
+    n = C.c_int64(0)
+    _check(_lib.dvssq_kvbss_attention_ws_bytes(C.byref(shape), C.byref(n)), "dvssq_kvbss_attention_ws_bytes")
+    return int(n.value)
+
+
+def kvbss_attention(shape: AttnShape, q, k, v, o, ws=None, stream=None) -> None:
+    _check(_lib.dvssq_kvbss_attention(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(ws), _stream(stream)),
            "dvssq_kvbss_attention")
 
 

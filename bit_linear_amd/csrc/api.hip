@@ -627,19 +627,52 @@ int dvssq_stream_read(const void *buf, int64_t bytes, void *sink, void *stream) 
   return launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 
-int dvssq_kvbss_attention(const dvssq_attn_shape *sh, const void *q, const void *k, const void *v, void *o,
-                          void *stream) {
-  if (!sh || !q || !k || !v || !o) return DVSSQ_EINVAL;
+// the attention call's shape checks (shared with its workspace query)
+static int check_attn_shape(const dvssq_attn_shape *sh) {
+  if (!sh) return DVSSQ_EINVAL;
   const dvssq_attn_shape S = *sh;
   if (S.B < 1 || S.Mq < 1 || S.Nk < S.Mq || S.Hq < 1 || S.Hkv < 1 || S.Hq % S.Hkv != 0 || S.window < 0)
     return DVSSQ_EINVAL;
   if (!std::isfinite(S.scale) || std::isnan(S.haze) || S.haze < 0.0f) return DVSSQ_EINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DVSSQ_EINVAL;
   if (S.D != 64 && S.D != 128 && S.D != 256) return DVSSQ_EUNSUPPORTED;
   const int64_t kvn = static_cast<int64_t>(S.B) * S.Nk * S.Hkv * S.D, qn = static_cast<int64_t>(S.B) * S.Mq * S.Hq * S.D;
   if (kvn >= (int64_t{1} << 30) || qn >= (int64_t{1} << 30)) return DVSSQ_EUNSUPPORTED;
+  const int64_t rows = static_cast<int64_t>(S.Mq) * (S.Hq / S.Hkv);
+  const int64_t tiles = (rows + 16 * attn_waves(S.D) - 1) / (16 * attn_waves(S.D));
+  if (static_cast<int64_t>(S.B) * S.Hkv * tiles >= (int64_t{1} << 31)) return DVSSQ_EUNSUPPORTED;
+  return DVSSQ_OK;
+}
+
+static int64_t attn_ws_need(const dvssq_attn_shape &S) {
+  const int rows = S.Mq * (S.Hq / S.Hkv);
+  return attn_split(rows, S.Nk) ? attn_ws_layout(S.B, S.Hkv, S.Nk, S.D).bytes : 0;
+}
+
+int dvssq_kvbss_attention_ws_bytes(const dvssq_attn_shape *sh, int64_t *bytes) {
+  if (!bytes) return DVSSQ_EINVAL;
+  const int rc = check_attn_shape(sh);
+  if (rc != DVSSQ_OK) return rc;
+  *bytes = attn_ws_need(*sh);
+  return DVSSQ_OK;
+}
+
+int dvssq_kvbss_attention(const dvssq_attn_shape *sh, const void *q, const void *k, const void *v, void *o, void *ws,
+                          void *stream) {
+  int rc = check_attn_shape(sh);
+  if (rc != DVSSQ_OK) return rc;
+  if (!q || !k || !v || !o) return DVSSQ_EINVAL;
+  const dvssq_attn_shape S = *sh;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DVSSQ_EINVAL;
+  const int64_t kvn = static_cast<int64_t>(S.B) * S.Nk * S.Hkv * S.D, qn = static_cast<int64_t>(S.B) * S.Mq * S.Hq * S.D;
   if (overlap(o, 2 * qn, q, 2 * qn) || overlap(o, 2 * qn, k, 2 * kvn) || overlap(o, 2 * qn, v, 2 * kvn))
     return DVSSQ_EINVAL;
+  const int64_t need = attn_ws_need(S);
+  if (need > 0) {
+    if (!ws || !aligned(ws, 256)) return DVSSQ_EINVAL;
+    if (overlap(ws, need, q, 2 * qn) || overlap(ws, need, k, 2 * kvn) || overlap(ws, need, v, 2 * kvn) ||
+        overlap(ws, need, o, 2 * qn))
+      return DVSSQ_EINVAL;
+  }
   AttnArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.k = static_cast<const uint16_t *>(k);
@@ -657,7 +690,16 @@ int dvssq_kvbss_attention(const dvssq_attn_shape *sh, const void *q, const void 
   a.tiles = (a.rows + 16 * attn_waves(a.D) - 1) / (16 * attn_waves(a.D));
   a.scale = S.scale;
   a.haze = S.haze;
-  if (static_cast<int64_t>(a.B) * a.Hkv * a.tiles >= (int64_t{1} << 31)) return DVSSQ_EUNSUPPORTED;
+  if (need > 0) {
+    const AttnWs w = attn_ws_layout(S.B, S.Hkv, S.Nk, S.D);
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    a.nchunk = (S.Nk + kAttnChunk - 1) / kAttnChunk;
+    a.logits = reinterpret_cast<float *>(wsb + w.logits);
+    a.cmax = reinterpret_cast<float *>(wsb + w.cmax);
+    a.part = reinterpret_cast<float *>(wsb + w.part);
+    a.partl = reinterpret_cast<float *>(wsb + w.partl);
+    a.cnt = reinterpret_cast<uint64_t *>(wsb + w.cnt);
+  }
   return launch_kvbss_attention(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DVSSQ_OK : DVSSQ_EHIP;
 }
 

@@ -109,6 +109,8 @@ __device__ __forceinline__ void logits_t(const u32x4 (&qa)[D / 32], const uint8_
 }
 
 constexpr int kVm0 = 0x0F70;    // s_waitcnt vmcnt(0), the other counters free
+// s_waitcnt with vmcnt <= n (n < 64) and the other counters free
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Per-row state of a wavefront lane (row 16 w + l % 16 of the tile).
 struct RowState {
@@ -291,13 +293,291 @@ hipError_t launch_d(const AttnArgs &a, hipStream_t s) {
                        a);
 }
 
+// --------------------------------------------------------------------------
+// Split-key form for a few rows (Mq (Hq / Hkv) <= 16, a decode step over a
+// long context): the one-launch kernel would give each (sequence, KV head)
+// one workgroup.  Here each (sequence, KV head, range of kAttnChunk keys) is a
+// workgroup, in two launches, because the haze threshold of a row needs the
+// maximum over all ranges before any range can sum:
+//   1. kvbss_logits_kernel: the scaled logits of the range (-inf where not
+//      visible) into the workspace, and the range's row maxima;
+//   2. kvbss_vsum_kernel: the row maxima over all ranges, then the range's
+//      sum of exp(s - m) v and of exp(s - m) over the kept keys, and the last
+//      workgroup of the (sequence, KV head) to arrive (an arrival counter that
+//      launch 1 zeroes) sums the ranges in range order and writes o.
+// Rows: lane l's row is l % 16 = (query, head) pair r of the KV head's group.
+// Each wavefront takes the 32-key blocks w, w + 4, ... of the range: K comes
+// straight from global memory as the A operand of S^T = K Q^T; V goes to the
+// wavefront's own LDS region by buffer-to-LDS loads and is read back by the
+// transposing read, as in the one-launch kernel.
+
+template <int D>
+__global__ __launch_bounds__(256) void kvbss_logits_kernel(AttnArgs a) {
+  __shared__ float red[4][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, gq = lane >> 4;
+  const int bg = static_cast<int>(blockIdx.x) / a.nchunk, c = static_cast<int>(blockIdx.x) - bg * a.nchunk;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const bool rok = i < a.rows;
+  const int ri = i / a.rep;
+  const int pos = rok ? a.Nk - a.Mq + ri : -1;
+  const int jlo = a.window > 0 ? pos - a.window + 1 : 0;
+  const uint32_t kvbytes = static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.Nk * a.Hkv * D * 2);
+  const auto rk = make_rsrc(a.k, kvbytes);
+  const auto rq = make_rsrc(a.q, static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.Mq * a.Hq * D * 2));
+  u32x4 qa[D / 32];
+  {
+    const int h = g * a.rep + (i - ri * a.rep);
+    const uint32_t base = static_cast<uint32_t>((((static_cast<int64_t>(b) * a.Mq + ri) * a.Hq + h) * D + 8 * gq) * 2);
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) qa[st] = buf_load16(rq, rok ? base + 64 * st : kOutOfRange);
+  }
+  float *lg = a.logits + (static_cast<int64_t>(bg) * 16 + i) * a.Nk;
+  float mx = -INFINITY;
+  for (int t = 0; t < kAttnChunk / 128; ++t) {
+    const int kb = c * kAttnChunk + 32 * (wave + 4 * t);
+    if (kb >= a.Nk) break;
+    u32x4 ka[2][D / 32];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int key = kb + 16 * nt + i;
+      const uint32_t base =
+          static_cast<uint32_t>((((static_cast<int64_t>(b) * a.Nk + key) * a.Hkv + g) * D + 8 * gq) * 2);
+#pragma unroll
+      for (int st = 0; st < D / 32; ++st) ka[nt][st] = buf_load16(rk, key < a.Nk ? base + 64 * st : kOutOfRange);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int st = 0; st < D / 32; ++st) acc = mfma_bf16(ka[nt][st], qa[st], acc);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = kb + 16 * nt + 4 * gq + v;
+        const float sv = (rok && j <= pos && j >= jlo) ? acc[v] * a.scale : -INFINITY;
+        mx = fmaxf(mx, sv);
+        if (j < a.Nk) lg[j] = sv;
+      }
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (gq == 0) red[wave][i] = mx;
+  __syncthreads();
+  if (threadIdx.x < 16)
+    a.cmax[(static_cast<int64_t>(bg) * a.nchunk + c) * 16 + i] =
+        fmaxf(fmaxf(red[0][i], red[1][i]), fmaxf(red[2][i], red[3][i]));
+  // the arrival counter of the second launch starts at zero (this launch
+  // completes before that one starts on the stream)
+  if (c == 0 && threadIdx.x == 0) a.cnt[bg] = 0;
+}
+
+// One block of pass 2 of the split form for a wavefront: P from the row's
+// logits sl (keys 16 nt + 4 g + v of block kb), V from the wavefront's LDS
+// region vcur by transposing reads.
+template <int D>
+__device__ __forceinline__ void vsum_block(const AttnArgs &a, const float (&sl)[2][4], int kb, bool rok, float thr,
+                                           float mb, const uint8_t *vcur, int lane, f32x4 (&oacc)[D / 16],
+                                           float &lsum) {
+  const int i = lane & 15, gq = lane >> 4;
+  const int vj = i >> 2, vc = i & 3;
+  float p[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = kb + 16 * nt + 4 * gq + v;
+      const float sv = j < a.Nk ? sl[nt][v] : -INFINITY;
+      p[nt][v] = (rok && !(sv < thr) && sv > -INFINITY) ? __builtin_amdgcn_exp2f(sv * kLog2e - mb) : 0.0f;
+      lsum += p[nt][v];
+    }
+  u32x4 pa;
+  pa[0] = pack_bf16x2(p[0][0], p[0][1]);
+  pa[1] = pack_bf16x2(p[0][2], p[0][3]);
+  pa[2] = pack_bf16x2(p[1][0], p[1][1]);
+  pa[3] = pack_bf16x2(p[1][2], p[1][3]);
+  const int k0 = 4 * gq + vj, k1 = 16 + 4 * gq + vj;
+  const uint8_t *v0 = vcur + k0 * 2 * D + 8 * (vc & 1), *v1 = vcur + k1 * 2 * D + 8 * (vc & 1);
+  const int u0 = (vc >> 1) ^ swz<D>(k0), u1 = (vc >> 1) ^ swz<D>(k1);
+  u32x4 vop[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(v0 + 16 * (u0 ^ (2 * dt))));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(v1 + 16 * (u1 ^ (2 * dt))));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    vop[dt] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = mfma_bf16(pa, vop[dt], oacc[dt]);
+  __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): the reads are done before the region is refilled
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void kvbss_vsum_kernel(AttnArgs a) {
+  constexpr int VB = kKeys * D * 2;           // bytes of one V block
+  constexpr int NB = kAttnChunk / 128;        // blocks per wavefront
+  constexpr int NL = D / 16;                  // 16-byte loads per lane for one block
+  // one V block per wavefront; later the wavefronts' sums
+  __shared__ __align__(16) uint8_t va[4 * VB];
+  __shared__ float lred[4][16];
+  __shared__ int last_sh;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, gq = lane >> 4;
+  const int bg = static_cast<int>(blockIdx.x) / a.nchunk, c = static_cast<int>(blockIdx.x) - bg * a.nchunk;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const bool rok = i < a.rows;
+  const uint32_t kvbytes = static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.Nk * a.Hkv * D * 2);
+  const auto rv = make_rsrc(a.v, kvbytes);
+
+  // this wavefront's blocks w, w + 4, ... of the range and the row's logits of
+  // each (keys 16 nt + 4 g + v; index clamped, past the end masked at use)
+  const int kbw = c * kAttnChunk + 32 * wave;
+  const int nb = min(NB, max(0, (a.Nk - kbw + 127) / 128));
+  const float *lg = a.logits + (static_cast<int64_t>(bg) * 16 + i) * a.Nk;
+  float sl[NB][2][4];
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sl[t][nt][v] = lg[min(kbw + 128 * t + 16 * nt + 4 * gq + v, a.Nk - 1)];
+
+  // V block t, load u of this lane: key row (64 u + lane) / (D / 8), 16-byte
+  // chunk (64 u + lane) % (D / 8); stored at the row's swizzled slot
+  auto load_v = [&](int t, u32x4 (&r)[NL]) {
+    const int kb = kbw + 128 * t;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int f = 64 * u + lane, row = f / (D / 8), cch = f % (D / 8);
+      const int j = kb + row;
+      r[u] = buf_load16(rv, j < a.Nk ? static_cast<uint32_t>((((static_cast<int64_t>(b) * a.Nk + j) * a.Hkv + g) * D +
+                                                              8 * cch) * 2)
+                                     : kOutOfRange);
+    }
+  };
+  uint8_t *wv = va + wave * VB;
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float lsum = 0.0f;
+  u32x4 vr[NL];
+  if (nb > 0) load_v(0, vr);
+  // the rows' maxima over every range: the workgroup's threads share the
+  // 16 x nchunk range maxima (independent loads), then an LDS reduction
+  {
+    float mt = -INFINITY;
+    const float *cm = a.cmax + static_cast<int64_t>(bg) * a.nchunk * 16;
+    const int tid = static_cast<int>(threadIdx.x), row = tid & 15;
+#pragma unroll 4
+    for (int cc = tid >> 4; cc < a.nchunk; cc += 16) mt = fmaxf(mt, cm[cc * 16 + row]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    if (gq == 0) lred[wave][i] = mt;
+  }
+  __syncthreads();
+  const float m = fmaxf(fmaxf(lred[0][i], lred[1][i]), fmaxf(lred[2][i], lred[3][i]));
+  const float thr = m - a.haze;
+  const float mb = rok ? m * kLog2e : 0.0f;
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    if (t >= nb) break;
+    // block t from registers into the wavefront's region (the previous
+    // block's reads have completed: lgkmcnt(0) at the end of vsum_block)
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int f = 64 * u + lane, row = f / (D / 8), cch = f % (D / 8);
+      *reinterpret_cast<u32x4 *>(wv + row * 2 * D + 16 * (cch ^ swz<D>(row))) = vr[u];
+    }
+    if (t + 1 < nb) load_v(t + 1, vr);        // the next block streams in under this one's work
+    __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the block is in LDS
+    __builtin_amdgcn_wave_barrier();
+    vsum_block<D>(a, sl[t], kbw + 128 * t, rok, thr, mb, wv, lane, oacc, lsum);
+  }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+
+  // the wavefronts' sums through LDS (va reused: [4][16][D] fp32 = 4 V blocks)
+  __syncthreads();
+  float *osum = reinterpret_cast<float *>(va);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) osum[(wave * 16 + 4 * gq + v) * D + 16 * dt + i] = oacc[dt][v];
+  if (gq == 0) lred[wave][i] = lsum;
+  __syncthreads();
+  const int64_t pbase = (static_cast<int64_t>(bg) * a.nchunk + c) * 16;
+  for (int e = threadIdx.x; e < a.rows * D; e += 256) {
+    const int row = e / D, d = e - row * D;
+    const float sum = osum[row * D + d] + osum[(16 + row) * D + d] + osum[(32 + row) * D + d] + osum[(48 + row) * D + d];
+    st_dev(a.part + (pbase + row) * D + d, sum);
+  }
+  if (static_cast<int>(threadIdx.x) < a.rows)
+    st_dev(a.partl + pbase + threadIdx.x,
+           lred[0][threadIdx.x] + lred[1][threadIdx.x] + lred[2][threadIdx.x] + lred[3][threadIdx.x]);
+  drain_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_sh = __hip_atomic_fetch_add(a.cnt + bg, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+              static_cast<uint64_t>(a.nchunk);
+  __syncthreads();
+  if (!last_sh) return;
+  // the last range to arrive: o = sum over ranges (in range order) / l; a
+  // thread takes 4 dims of one row (16-byte loads), the device-scope loads
+  // issued in batches of kBatch ranges before their first use
+  constexpr int kBatch = 16;
+  const int64_t rbase = static_cast<int64_t>(bg) * a.nchunk * 16;
+  if (static_cast<int>(threadIdx.x) < a.rows) {
+    float l = 0.0f;
+    for (int c0 = 0; c0 < a.nchunk; c0 += kBatch) {
+      float pv[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) pv[j] = c0 + j < a.nchunk ? ld_dev(a.partl + rbase + (c0 + j) * 16 + threadIdx.x) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) l += pv[j];
+    }
+    lred[0][threadIdx.x] = l;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.rows * (D / 4); e += 256) {
+    const int row = e / (D / 4), d = 4 * (e - row * (D / 4));
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = 0; c0 < a.nchunk; c0 += kBatch) {
+      u32x4 pv[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        pv[j] = c0 + j < a.nchunk ? ld_dev16(a.part + (rbase + (c0 + j) * 16 + row) * D + d) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] += __uint_as_float(pv[j][q]);
+    }
+    const int qi = row / a.rep, h = g * a.rep + (row - qi * a.rep);
+    uint16_t *orow = a.o + ((static_cast<int64_t>(b) * a.Mq + qi) * a.Hq + h) * D + d;
+    const float inv = 1.0f / lred[0][row];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) orow[q] = f32_to_bf16(sum[q] * inv);
+  }
+}
+
+template <int D>
+hipError_t launch_split(const AttnArgs &a, hipStream_t s) {
+  const int grid = a.B * a.Hkv * a.nchunk;
+  hipError_t e = launch_kernel(reinterpret_cast<const void *>(kvbss_logits_kernel<D>), dim3(grid), dim3(256), 0, s, a);
+  if (e != hipSuccess) return e;
+  return launch_kernel(reinterpret_cast<const void *>(kvbss_vsum_kernel<D>), dim3(grid), dim3(256), 0, s, a);
+}
+
 }  // namespace
 
 hipError_t launch_kvbss_attention(const AttnArgs &a, hipStream_t s) {
+  const bool split = attn_split(a.rows, a.Nk);
   switch (a.D) {
-    case 64: return launch_d<64>(a, s);
-    case 128: return launch_d<128>(a, s);
-    case 256: return launch_d<256>(a, s);
+    case 64: return split ? launch_split<64>(a, s) : launch_d<64>(a, s);
+    case 128: return split ? launch_split<128>(a, s) : launch_d<128>(a, s);
+    case 256: return split ? launch_split<256>(a, s) : launch_d<256>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

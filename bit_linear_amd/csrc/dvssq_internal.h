@@ -648,10 +648,40 @@ struct AttnArgs {
   int rows;                    // Mq rep: (query, head) rows of one (sequence, KV head)
   int tiles;                   // workgroups per (sequence, KV head): ceil(rows / (16 attn_waves(D)))
   float scale, haze;
+  // split-key form (rows <= 16, two launches): workspace regions and the call's stamp
+  int nchunk;                  // key ranges of kAttnChunk keys per (sequence, KV head)
+  float *logits;               // fp32 [B Hkv][16][Nk], -inf where not visible
+  float *cmax;                 // fp32 [B Hkv][nchunk][16] row maxima of each range
+  float *part;                 // fp32 [B Hkv][nchunk][16][D] sum of exp(s - m) v of each range
+  float *partl;                // fp32 [B Hkv][nchunk][16] sum of exp(s - m) of each range
+  uint64_t *cnt;               // arrival counters [B Hkv], zeroed by the first launch
 };
 hipError_t launch_kvbss_attention(const AttnArgs &a, hipStream_t s);
 // wavefronts per attention workgroup (each takes 16 rows of the tile)
 constexpr int attn_waves(int) { return 4; }
+// split-key form: keys per range (one workgroup each), and when it is taken
+constexpr int kAttnChunk = 512;
+inline bool attn_split(int rows, int Nk) { return rows <= 16 && Nk > kAttnChunk; }
+struct AttnWs {
+  int64_t logits, cmax, part, partl, cnt, bytes;
+};
+inline AttnWs attn_ws_layout(int B, int Hkv, int Nk, int D) {
+  AttnWs w{};
+  const int64_t bg = static_cast<int64_t>(B) * Hkv, nchunk = (Nk + kAttnChunk - 1) / kAttnChunk;
+  int64_t cur = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = cur;
+    cur = (cur + bytes + 255) / 256 * 256;
+    return o;
+  };
+  w.logits = take(bg * 16 * Nk * 4);
+  w.cmax = take(bg * nchunk * 16 * 4);
+  w.part = take(bg * nchunk * 16 * D * 4);
+  w.partl = take(bg * nchunk * 16 * 4);
+  w.cnt = take(bg * 8);
+  w.bytes = cur;
+  return w;
+}
 
 // few-token decode (1 <= M <= kGemvMaxM): 32-row tiles on the int8 32x32x32 matrix cores
 constexpr int kGemvMaxM = 4;

@@ -319,7 +319,14 @@ int dvssq_stream_read(const void *buf, int64_t bytes, void *sink, void *stream);
  * >= 0; scale finite; haze >= 0 (not NaN); B Nk Hkv D and B Mq Hq D below 2^30
  * (DVSSQ_EUNSUPPORTED above).  Logits and sums in fp32 (the logits from bf16
  * products on the matrix cores), exp(s - m) rounded to bf16 for the product
- * with v, output rounded to bf16.  One kernel launch on `stream`; no workspace.
+ * with v, output rounded to bf16.  ws: device workspace of
+ * dvssq_kvbss_attention_ws_bytes bytes, 256-byte aligned, disjoint from q, k,
+ * v and o, no initialization needed, one call in flight per ws; may be null
+ * when that size is 0 (the shape runs one kernel launch).  A shape with
+ * Mq (Hq / Hkv) <= 16 query rows per KV head and more than 512 keys (a decode
+ * step over a long context) runs in two launches over ranges of 512 keys,
+ * with the ranges summed in a fixed order; every other shape in one launch.
+ * Kernels are launched on `stream`; the call does not synchronize.
  */
 typedef struct dvssq_attn_shape {
   int32_t B, Mq, Nk, Hq, Hkv, D;
@@ -328,8 +335,12 @@ typedef struct dvssq_attn_shape {
   float haze;           /* keys below the row maximum minus haze are dropped */
 } dvssq_attn_shape;
 
+/* Workspace bytes of dvssq_kvbss_attention for the shape (0 when it needs
+ * none), into *bytes.  Host-only; the same shape checks and errors. */
+int dvssq_kvbss_attention_ws_bytes(const dvssq_attn_shape *shape, int64_t *bytes);
+
 int dvssq_kvbss_attention(const dvssq_attn_shape *shape, const void *q, const void *k, const void *v, void *o,
-                          void *stream);
+                          void *ws, void *stream);
 
 /* Static text for a return code. */
 const char *dvssq_status_str(int status);

@@ -327,10 +327,10 @@ def test_kvbss_attention_error_paths():
         d.update(kw)
         return dv.AttnShape(**d)
 
-    def c(sh=None, q=X, k=BLOB, v=WS, o=O):
-        return f(C.byref(sh if sh is not None else shape()), q, k, v, o, None)
+    def c(sh=None, q=X, k=BLOB, v=WS, o=O, ws=None):
+        return f(C.byref(sh if sh is not None else shape()), q, k, v, o, ws, None)
 
-    assert f(None, X, BLOB, WS, O, None) == E
+    assert f(None, X, BLOB, WS, O, None, None) == E
     assert c(q=None) == E and c(k=None) == E and c(v=None) == E and c(o=None) == E
     assert c(shape(Mq=65)) == E                    # more queries than keys
     assert c(shape(Mq=0)) == E and c(shape(B=0)) == E
@@ -341,3 +341,28 @@ def test_kvbss_attention_error_paths():
     assert c(o=X + 64) == E                        # output overlaps q
     assert c(shape(D=96)) == dv.DVSSQ_EUNSUPPORTED
     assert c(shape(B=1, Nk=1 << 20, Hkv=4, D=256)) == dv.DVSSQ_EUNSUPPORTED
+    # a decode step over 4096 keys takes the two-launch form: it needs a workspace
+    WSA = 0x70000000
+    dec = shape(Mq=1, Nk=4096)
+    assert c(dec) == E and c(dec, ws=WSA + 64) == E                  # missing / misaligned
+    assert c(dec, ws=X) == E                                          # workspace overlaps q
+
+
+def test_kvbss_attention_ws_bytes():
+    f = dv.lib().dvssq_kvbss_attention_ws_bytes
+    n = C.c_int64(-1)
+
+    def shape(**kw):
+        d = dict(B=1, Mq=1, Nk=32768, Hq=16, Hkv=4, D=256, window=0, scale=0.06875, haze=12.0)
+        d.update(kw)
+        return dv.AttnShape(**d)
+
+    assert f(C.byref(shape()), C.byref(n)) == dv.DVSSQ_OK
+    # logits [4][16][32768] fp32 + range maxima, sums and counters: 64 ranges of 512 keys
+    assert n.value >= 4 * 16 * 32768 * 4 + 4 * 64 * 16 * 256 * 4 and n.value % 256 == 0
+    assert f(C.byref(shape(Mq=2048, Nk=2048)), C.byref(n)) == dv.DVSSQ_OK and n.value == 0   # one launch
+    assert f(C.byref(shape(Nk=512)), C.byref(n)) == dv.DVSSQ_OK and n.value == 0             # one range
+    assert f(C.byref(shape(Mq=5, Nk=4096)), C.byref(n)) == dv.DVSSQ_OK and n.value == 0      # 20 rows
+    assert f(C.byref(shape()), None) == dv.DVSSQ_EINVAL
+    assert f(None, C.byref(n)) == dv.DVSSQ_EINVAL
+    assert f(C.byref(shape(D=96)), C.byref(n)) == dv.DVSSQ_EUNSUPPORTED

@@ -42,7 +42,9 @@ def run(q, k, v, window=0, haze=oracle.KVBSS_HAZE, scale=None):
         scale = float(np.float32(oracle.KVBSS_TAU / math.sqrt(D)))
     sh = dv.AttnShape(B=B, Mq=Mq, Nk=Nk, Hq=Hq, Hkv=Hkv, D=D, window=window, scale=scale, haze=haze)
     o = torch.empty((B, Mq, Hq, D), dtype=torch.int16, device=DEV)
-    dv.kvbss_attention(sh, dev(q), dev(k), dev(v), o)
+    nws = dv.kvbss_attention_ws_bytes(sh)
+    ws = dv.device_buffer(nws, DEV).fill_(0x7F) if nws else None     # no initialization expected
+    dv.kvbss_attention(sh, dev(q), dev(k), dev(v), o, ws)
     torch.cuda.synchronize()
     return synth.bf16_bits_to_f64(o.cpu().numpy().view(np.uint16)), scale
 
@@ -122,6 +124,33 @@ def test_attention_repeat_is_bit_identical():
     np.testing.assert_array_equal(a, b)
 
 
+# the split-key form: at most 16 (query, head) rows per KV head and more than 512 keys
+SPLIT_CASES = [
+    # B, Mq, Nk, Hq, Hkv, D, window
+    (2, 1, 3000, 16, 4, 256, 0),     # decode, Spark heads, ragged last range
+    (1, 4, 1537, 16, 4, 256, 0),     # 16 rows: four queries of a group of four heads
+    (3, 1, 2048, 8, 1, 128, 0),      # 8 heads sharing one KV head
+    (1, 2, 1100, 4, 2, 64, 300),     # window: most ranges see no key of the rows
+    (1, 1, 513, 2, 2, 256, 0),       # one key past a range
+]
+
+
+@pytest.mark.parametrize("B,Mq,Nk,Hq,Hkv,D,window", SPLIT_CASES)
+def test_attention_split_parity(B, Mq, Nk, Hq, Hkv, D, window):
+    sh = dv.AttnShape(B=B, Mq=Mq, Nk=Nk, Hq=Hq, Hkv=Hkv, D=D, window=window, scale=0.1, haze=12.0)
+    assert dv.kvbss_attention_ws_bytes(sh) > 0           # the two-launch form
+    print(f"attention split B={B} Mq={Mq} Nk={Nk} Hq={Hq} Hkv={Hkv} D={D} window={window}", flush=True)
+    q, k, v = synth.attention_qkv(15, f"split{Mq}x{Nk}", B, Mq, Nk, Hq, Hkv, D)
+    check(q, k, v, window)
+
+
+def test_attention_split_repeat_is_bit_identical():
+    q, k, v = synth.attention_qkv(16, "srep", 2, 1, 2600, 16, 4, 256)
+    a, _ = run(q, k, v)
+    b, _ = run(q, k, v)
+    np.testing.assert_array_equal(a, b)
+
+
 def spark_rows(B, Mq, Hq, n=96, seed=2):
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(B * Mq * Hq, size=n, replace=False).tolist())
@@ -141,7 +170,8 @@ def test_attention_spark_prefill_2048_sampled(window):
 
 
 def test_attention_spark_decode_32k():
-    """One new token over a 32768-token context, every head (Spark full layer)."""
+    """One new token over a 32768-token context, every head (Spark full layer):
+    the split-key form the benchmark times."""
     B, Mq, Nk, Hq, Hkv, D = 1, 1, 32768, 16, 4, 256
     q, k, v = synth.attention_qkv(0, "spark_decode", B, Mq, Nk, Hq, Hkv, D)
     check(q, k, v)
