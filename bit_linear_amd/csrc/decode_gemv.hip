@@ -644,12 +644,7 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   int last = 0;
   if (lane == 0) {
     uint64_t *cnt = a.cnt + tile;
-    uint64_t old = ld_dev(cnt), nw;
-    do {
-      nw = (static_cast<uint32_t>(old >> 32) == a.stamp) ? old + 1 : ((static_cast<uint64_t>(a.stamp) << 32) | 1u);
-    } while (!__hip_atomic_compare_exchange_strong(cnt, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT));
-    last = static_cast<uint32_t>(nw) == static_cast<uint32_t>(a.S);
+    last = arrive_tagged(cnt, a.stamp) == static_cast<uint32_t>(a.S);
   }
   last = __shfl(last, 0, 64);
   if (!last || !row_ok || h != 0) return;

@@ -670,12 +670,7 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   int last = 0;
   if (lane == 0) {
     uint64_t *cnt = a.cntw + (T8 ? (a.n4 + kTile - 1) / kTile : 0) + tile;
-    uint64_t old = ld_dev(cnt), nw;
-    do {
-      nw = (static_cast<uint32_t>(old >> 32) == a.tag) ? old + 1 : ((static_cast<uint64_t>(a.tag) << 32) | 1u);
-    } while (!__hip_atomic_compare_exchange_strong(cnt, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT));
-    last = static_cast<uint32_t>(nw) == static_cast<uint32_t>(a.S);
+    last = arrive_tagged(cnt, a.tag) == static_cast<uint32_t>(a.S);
   }
   last = __shfl(last, 0, 64);
   if (!last) return;

@@ -263,6 +263,23 @@ __device__ __forceinline__ u32x4 ld_dev16(const void *p) {
   r[3] = static_cast<uint32_t>(hi >> 32);
   return r;
 }
+// Arrival on a tagged counter {stamp : 32, count : 32} that needs no
+// initialization; returns the count after this arrival.  The first arriver of
+// a call (the word still holds another stamp) installs {stamp, 1} by
+// compare-and-swap; every later arriver adds 1 with one fetch-add, so
+// arrivals that come together do not retry against each other.
+__device__ inline uint32_t arrive_tagged(uint64_t *cnt, uint32_t stamp) {
+  uint64_t old = ld_dev(cnt);
+  for (;;) {
+    if (static_cast<uint32_t>(old >> 32) == stamp)
+      return static_cast<uint32_t>(__hip_atomic_fetch_add(cnt, uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) +
+             1u;
+    if (__hip_atomic_compare_exchange_strong(cnt, &old, (static_cast<uint64_t>(stamp) << 32) | 1u, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      return 1u;
+    // old now holds the word another arriver wrote: its stamp is this call's
+  }
+}
 // wait until every store this thread issued has completed
 __device__ __forceinline__ void drain_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
