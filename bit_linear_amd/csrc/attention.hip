@@ -201,15 +201,15 @@ __global__ __launch_bounds__(64 * W, 8 / W) void kvbss_attention_kernel(AttnArgs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, gq = lane >> 4;
 
-  // Work rank: tiles of later queries see more keys.  The first half of the
-  // grid takes the ranks heaviest first, the second half lightest first, so
-  // that the two workgroups a compute unit receives (the dispatcher places
-  // the first half, then the second) carry about the same work together.
-  const int nseq = a.B * a.Hkv, total = nseq * a.tiles, half = (total + 1) / 2;
-  const int k = static_cast<int>(blockIdx.x);
-  const int rank = k < half ? k : total - 1 - (k - half);
-  const int tile = a.tiles - 1 - rank / nseq;
-  const int bg = rank - (rank / nseq) * nseq;
+  // Tiles of later queries see more keys.  Workgroup k takes (sequence, KV
+  // head) k mod nseq, so that with nseq dividing the 8 XCDs (or a multiple of
+  // them) each XCD's L2 serves one set of K and V; its tiles go heaviest first
+  // over the first half of the grid and lightest first over the second, so
+  // that the two workgroups a compute unit receives (the dispatcher places the
+  // first half, then the second) carry about the same work together.
+  const int nseq = a.B * a.Hkv, k = static_cast<int>(blockIdx.x);
+  const int bg = k % nseq, q = k / nseq, hq = (a.tiles + 1) / 2;
+  const int tile = q < hq ? a.tiles - 1 - q : q - hq;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int r0 = tile * kRowsPerWg;
   const int r1 = min(a.rows, r0 + kRowsPerWg) - 1;       // last row of the tile

@@ -109,6 +109,10 @@ QZ_CASES = [
     ("mlp_tiny_gu", 8, 2),
     ("spark_up", 8, 2),
     ("spark_down", 8, 2),         # K = 10240: the rotation row needs > 64 KB of LDS
+    ("spark_gateup", 8, 2),       # two segments of 10240 rows, r = 24
+    ("minicpm_gate", 8, 2),       # blocks of 2048
+    ("minicpm_down", 8, 2),       # K = 6144, three blocks of 2048
+    ("minicpm_gate_r32", 8, 2),   # r = 32
 ]
 
 
