@@ -527,7 +527,7 @@ __global__ __launch_bounds__(256, 1) void kvbss_vsum_kernel(AttnArgs a) {
   // the last range to arrive: o = sum over ranges (in range order) / l; a
   // thread takes 4 dims of one row (16-byte loads), the device-scope loads
   // issued in batches of kBatch ranges before their first use
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 32;
   const int64_t rbase = static_cast<int64_t>(bg) * a.nchunk * 16;
   if (static_cast<int>(threadIdx.x) < a.rows) {
     float l = 0.0f;
