@@ -61,27 +61,37 @@ __device__ __forceinline__ int swz(int k) {
   else return (2 * (k & 3)) ^ ((k >> 2) & 1);
 }
 
-// Buffer-to-LDS loads of key block [kb, kb + 32) of KV head g (K or V) into
-// dst; keys past the end of the sequence read zeros.  Each of the W
-// wavefronts issues D / (16 W) loads of 1 KB (lane l's 16 bytes land at byte
-// 16 l).
+// Buffer-to-LDS copies of key blocks: a lane's source offset inside a block
+// is fixed (row, swizzled chunk), so it is computed once (StageMap); a block
+// adds its scalar base (sequence, first key, KV head) as the buffer's scalar
+// offset (below 2^31: the host limits K and V to 2^30 elements), and keys
+// past the end of the sequence read zeros.  Each of the W wavefronts issues
+// D / (16 W) copies of 1 KB (lane l's 16 bytes land at byte 16 l).
 template <int D, int W>
-__device__ __forceinline__ void stage(const AttnArgs &a, __amdgpu_buffer_rsrc_t rs, int b, int g, int kb, uint8_t *dst,
-                                      int wave, int lane) {
-  constexpr int PER = D / (16 * W);
-  static_assert(PER >= 1, "one 1 KB load per wavefront at least");
+struct StageMap {
+  static constexpr int PER = D / (16 * W);
+  static_assert(PER >= 1, "one 1 KB copy per wavefront at least");
+  uint32_t voff[PER];   // byte offset of the lane's 16 bytes from the block's first key row
+  int row[PER];         // the key row (inside the block) they come from
+  __device__ __forceinline__ StageMap(const AttnArgs &a, int wave, int lane) {
 #pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int o = 1024 * (wave * PER + t) + 16 * lane;     // LDS byte of this lane
-    const int row = o / (2 * D), c = (o % (2 * D)) / 16;
-    const int j = kb + row;
-    const uint32_t off =
-        j < a.Nk ? static_cast<uint32_t>((((static_cast<int64_t>(b) * a.Nk + j) * a.Hkv + g) * D + 8 * (c ^ swz<D>(row))) * 2)
-                 : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(dst + 1024 * (wave * PER + t)),
-                                             16, off, 0, 0, 0);
+    for (int t = 0; t < PER; ++t) {
+      const int o = 1024 * (wave * PER + t) + 16 * lane;
+      row[t] = o / (2 * D);
+      const int c = (o % (2 * D)) / 16;
+      voff[t] = static_cast<uint32_t>((row[t] * a.Hkv * D + 8 * (c ^ swz<D>(row[t]))) * 2);
+    }
   }
-}
+  __device__ __forceinline__ void stage(const AttnArgs &a, __amdgpu_buffer_rsrc_t rs, int b, int g, int kb,
+                                        uint8_t *dst, int wave) const {
+    const uint32_t base = static_cast<uint32_t>((((static_cast<int64_t>(b) * a.Nk + kb) * a.Hkv + g) * D) * 2);
+    const int lim = a.Nk - kb;                 // rows of the block inside the sequence
+#pragma unroll
+    for (int t = 0; t < PER; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(dst + 1024 * (wave * PER + t)),
+                                               16, row[t] < lim ? voff[t] : kOutOfRange, static_cast<int>(base), 0, 0);
+  }
+};
 
 // S^T tiles of the wavefront's 16 rows against the 32 keys of a K block:
 // s[nt][v] = S[row l % 16][key 16 nt + 4 (l / 16) + v], unscaled.  Every
@@ -122,29 +132,36 @@ struct RowState {
 // staged into knxt meanwhile.  kcur and knxt are distinct LDS arrays, so the
 // compiler sees that the reads of kcur do not wait for the copy into knxt.
 template <int D, int W>
-__device__ __forceinline__ void max_block(const AttnArgs &a, __amdgpu_buffer_rsrc_t rk, int b, int g, int kb,
-                                          bool more, const uint8_t *kcur, uint8_t *knxt, const u32x4 (&qa)[D / 32],
-                                          const RowState &rs, int wave, int lane, float &mx) {
+__device__ __forceinline__ void max_block(const AttnArgs &a, const StageMap<D, W> &sm, __amdgpu_buffer_rsrc_t rk, int b, int g, int kb,
+                                          bool more, bool full, const uint8_t *kcur, uint8_t *knxt,
+                                          const u32x4 (&qa)[D / 32], const RowState &rs, int wave, int lane, float &mx) {
   const int gq = lane >> 4;
   __builtin_amdgcn_s_waitcnt(kVm0);
   __syncthreads();                           // block t in LDS; block t - 1 no longer read
-  if (more) stage<D, W>(a, rk, b, g, kb + kKeys, knxt, wave, lane);
+  if (more) sm.stage(a, rk, b, g, kb + kKeys, knxt, wave);
   f32x4 s[2];
   logits_t<D>(qa, kcur, lane, s);
+  if (full) {                                // every key of the block visible to every row
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = kb + 16 * nt + 4 * gq + v;
-      if (j <= rs.pos && j >= rs.jlo) mx = fmaxf(mx, s[nt][v] * a.scale);
-    }
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[nt][v] * a.scale);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = kb + 16 * nt + 4 * gq + v;
+        if (j <= rs.pos && j >= rs.jlo) mx = fmaxf(mx, s[nt][v] * a.scale);
+      }
+  }
 }
 
 // Pass 2 on block t: O += P V and l += sum P over the kept keys, with the
 // next block's K and V staged into knxt / vnxt meanwhile.
 template <int D, int W>
-__device__ __forceinline__ void sum_block(const AttnArgs &a, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          int b, int g, int kb, bool more, const uint8_t *kcur, const uint8_t *vcur,
+__device__ __forceinline__ void sum_block(const AttnArgs &a, const StageMap<D, W> &sm, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          int b, int g, int kb, bool more, bool full, const uint8_t *kcur, const uint8_t *vcur,
                                           uint8_t *knxt, uint8_t *vnxt, const u32x4 (&qa)[D / 32], const RowState &rs,
                                           float thr, float mb, int wave, int lane, f32x4 (&oacc)[D / 16], float &lsum) {
   const int i = lane & 15, gq = lane >> 4;
@@ -152,8 +169,8 @@ __device__ __forceinline__ void sum_block(const AttnArgs &a, __amdgpu_buffer_rsr
   __builtin_amdgcn_s_waitcnt(kVm0);
   __syncthreads();
   if (more) {
-    stage<D, W>(a, rk, b, g, kb + kKeys, knxt, wave, lane);
-    stage<D, W>(a, rv, b, g, kb + kKeys, vnxt, wave, lane);
+    sm.stage(a, rk, b, g, kb + kKeys, knxt, wave);
+    sm.stage(a, rv, b, g, kb + kKeys, vnxt, wave);
   }
   f32x4 s[2];
   logits_t<D>(qa, kcur, lane, s);
@@ -172,17 +189,31 @@ __device__ __forceinline__ void sum_block(const AttnArgs &a, __amdgpu_buffer_rsr
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     vop[dt] = u32x4{l2[0], l2[1], h2[0], h2[1]};
   }
+  // thr is +inf on rows past the end, so they keep no key
   float p[2][4];
+  if (full) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float sv = s[nt][v] * a.scale;
+        p[nt][v] = sv < thr ? 0.0f : __builtin_amdgcn_exp2f(sv * kLog2e - mb);   // argument in [-17.4, 0]
+      }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = kb + 16 * nt + 4 * gq + v;
+        const float sv = s[nt][v] * a.scale;
+        const bool keep = j <= rs.pos && j >= rs.jlo && !(sv < thr);
+        p[nt][v] = keep ? __builtin_amdgcn_exp2f(sv * kLog2e - mb) : 0.0f;
+      }
+  }
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = kb + 16 * nt + 4 * gq + v;
-      const float sv = s[nt][v] * a.scale;
-      const bool keep = rs.rok && j <= rs.pos && j >= rs.jlo && !(sv < thr);
-      p[nt][v] = keep ? __builtin_amdgcn_exp2f(sv * kLog2e - mb) : 0.0f;   // argument in [-17.4, 0]
-      lsum += p[nt][v];
-    }
+    for (int v = 0; v < 4; ++v) lsum += p[nt][v];
   u32x4 pa;
   pa[0] = pack_bf16x2(p[0][0], p[0][1]);
   pa[1] = pack_bf16x2(p[0][2], p[0][3]);
@@ -218,6 +249,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void kvbss_attention_kernel(AttnArgs
   const int klo = a.window > 0 ? max(0, pmin - a.window + 1) : 0;
   const int kb0 = klo & ~(kKeys - 1);
   const int nblk = (pmax - kb0) / kKeys + 1;
+  // blocks [tf0, tf1) are visible in full to every row of the tile
+  const int tf0 = a.window > 0 ? (max(0, pmax - a.window + 1) - kb0 + kKeys - 1) / kKeys : 0;
+  const int tf1 = (pmin + 1 - kb0) / kKeys;
 
   const uint32_t kvbytes = static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.Nk * a.Hkv * D * 2);
   const auto rk = make_rsrc(a.k, kvbytes);
@@ -241,15 +275,16 @@ __global__ __launch_bounds__(64 * W, 8 / W) void kvbss_attention_kernel(AttnArgs
 
   // ---- pass 1: the row maximum of the scaled logits over the visible keys
   float mx = -INFINITY;
-  stage<D, W>(a, rk, b, g, kb0, k0buf, wave, lane);
+  const StageMap<D, W> sm(a, wave, lane);
+  sm.stage(a, rk, b, g, kb0, k0buf, wave);
   for (int t = 0; t < nblk; t += 2) {
-    max_block<D, W>(a, rk, b, g, kb0 + t * kKeys, t + 1 < nblk, k0buf, k1buf, qa, rs, wave, lane, mx);
+    max_block<D, W>(a, sm, rk, b, g, kb0 + t * kKeys, t + 1 < nblk, t >= tf0 && t < tf1, k0buf, k1buf, qa, rs, wave, lane, mx);
     if (t + 1 < nblk)
-      max_block<D, W>(a, rk, b, g, kb0 + (t + 1) * kKeys, t + 2 < nblk, k1buf, k0buf, qa, rs, wave, lane, mx);
+      max_block<D, W>(a, sm, rk, b, g, kb0 + (t + 1) * kKeys, t + 2 < nblk, t + 1 >= tf0 && t + 1 < tf1, k1buf, k0buf, qa, rs, wave, lane, mx);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float thr = mx - a.haze;             // keys below are dropped
+  const float thr = rs.rok ? mx - a.haze : INFINITY;    // keys below are dropped
   const float mb = rs.rok ? mx * kLog2e : 0.0f;
 
   // ---- pass 2: O = sum exp(s - m) v over the kept keys, l = sum exp(s - m)
@@ -258,14 +293,14 @@ __global__ __launch_bounds__(64 * W, 8 / W) void kvbss_attention_kernel(AttnArgs
   for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float lsum = 0.0f;
   __syncthreads();                           // pass 1's last block no longer read
-  stage<D, W>(a, rk, b, g, kb0, k0buf, wave, lane);
-  stage<D, W>(a, rv, b, g, kb0, v0buf, wave, lane);
+  sm.stage(a, rk, b, g, kb0, k0buf, wave);
+  sm.stage(a, rv, b, g, kb0, v0buf, wave);
   for (int t = 0; t < nblk; t += 2) {
-    sum_block<D, W>(a, rk, rv, b, g, kb0 + t * kKeys, t + 1 < nblk, k0buf, v0buf, k1buf, v1buf, qa, rs, thr, mb, wave,
-                 lane, oacc, lsum);
+    sum_block<D, W>(a, sm, rk, rv, b, g, kb0 + t * kKeys, t + 1 < nblk, t >= tf0 && t < tf1, k0buf, v0buf, k1buf, v1buf, qa, rs, thr, mb,
+                    wave, lane, oacc, lsum);
     if (t + 1 < nblk)
-      sum_block<D, W>(a, rk, rv, b, g, kb0 + (t + 1) * kKeys, t + 2 < nblk, k1buf, v1buf, k0buf, v0buf, qa, rs, thr, mb,
-                   wave, lane, oacc, lsum);
+      sum_block<D, W>(a, sm, rk, rv, b, g, kb0 + (t + 1) * kKeys, t + 2 < nblk, t + 1 >= tf0 && t + 1 < tf1, k1buf, v1buf, k0buf, v0buf, qa, rs, thr,
+                      mb, wave, lane, oacc, lsum);
   }
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
