@@ -217,9 +217,10 @@ __device__ void sum_t(const DecodeArgs &a, int t0, int nt, int u0, int nu, float
 
 // Copy of the producers' planes (rows 0 .. M-1, inputs k0 .. k0 + KW - 1),
 // 8 x group sums and unit scales into LDS by the lanes t0, t0 + nt, ... of the
-// workgroup; 16-byte chunks, read with device-scope loads.
+// workgroup; 16-byte chunks, read with device-scope loads.  Chunk c of row m
+// goes to chunk index c Mp + m of the LDS planes (Mp rows per chunk column).
 template <bool T8>
-__device__ void copy_planes(const DecodeArgs &a, int t0, int nt, int k0, int KW, int ngrp, int u0, int nu,
+__device__ void copy_planes(const DecodeArgs &a, int t0, int nt, int k0, int KW, int ngrp, int u0, int nu, int Mp,
                             int8_t *xs1, int8_t *xs2, int *x8, float *esc) {
   constexpr int kBatch = 4;
   const int M = a.M;
@@ -241,8 +242,8 @@ __device__ void copy_planes(const DecodeArgs &a, int t0, int nt, int k0, int KW,
       const int e = e0 + j * nt;
       if (e < nch) {
         const int m = static_cast<int>((static_cast<float>(e) + 0.5f) * inv), c = e - m * cpr;
-        *reinterpret_cast<u32x4 *>(xs1 + m * KW + 16 * c) = v1[j];
-        *reinterpret_cast<u32x4 *>(xs2 + m * KW + 16 * c) = v2[j];
+        *reinterpret_cast<u32x4 *>(xs1 + (c * Mp + m) * 16) = v1[j];
+        *reinterpret_cast<u32x4 *>(xs2 + (c * Mp + m) * 16) = v2[j];
       }
     }
   }
@@ -360,9 +361,12 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
   const int nitem = M * nu;                             // (row, unit) items to rotate
 
   // LDS: int8 planes, 8 x group sums, unit scales, partial tiles, U rows, columns, INT8 scales, t
+  // planes: 16-byte chunk c (inputs 16 c .. 16 c + 15 of the K-range) of token
+  // m at chunk index c MT + m, so that the 16 tokens of an operand read sit in
+  // 16 consecutive chunks
   int8_t *xs1 = reinterpret_cast<int8_t *>(smem);
-  int8_t *xs2 = xs1 + M * KW;
-  int *x8 = reinterpret_cast<int *>(xs2 + M * KW);                   // [ngrp][4]
+  int8_t *xs2 = xs1 + MT * KW;
+  int *x8 = reinterpret_cast<int *>(xs2 + MT * KW);                  // [ngrp][4]
   float *esc = reinterpret_cast<float *>(x8 + ngrp * kTab);          // [nu][4]
   float *red = esc + nu * kTab;                                      // [kWaves][kRed][64]
   u32x4 *ush = reinterpret_cast<u32x4 *>(red + kWaves * kRed * 64);  // U rows wbase .. wbase + 16 RT - 1
@@ -454,8 +458,8 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int kk = u * P + 256 * c + 16 * n + 4 * q;
-      *reinterpret_cast<uint32_t *>(xs1 + m * KW + kk) = p1[c];
-      *reinterpret_cast<uint32_t *>(xs2 + m * KW + kk) = p2[c];
+      *reinterpret_cast<uint32_t *>(xs1 + ((kk >> 4) * MT + m) * 16 + (kk & 15)) = p1[c];
+      *reinterpret_cast<uint32_t *>(xs2 + ((kk >> 4) * MT + m) * 16 + (kk & 15)) = p2[c];
       if (!T8 && (lane & 0x33) == 0) x8[(kk / kGroup) * kTab + m] = gsum[c];
     }
     if (lane == 0) esc[u * kTab + m] = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
@@ -465,7 +469,7 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
     // have seen their flags (barrier P), copy this K-range's planes, group
     // sums and unit scales into LDS
     __syncthreads();   // (P)
-    copy_planes<T8>(a, wave * 64 + lane, NCW * 64, k0, KW, ngrp, u0, nu, xs1, xs2, x8, esc);
+    copy_planes<T8>(a, wave * 64 + lane, NCW * 64, k0, KW, ngrp, u0, nu, MT, xs1, xs2, x8, esc);
     sum_t(a, wave * 64 + lane, NCW * 64, u0, nu, ts);
   } else {
     if (wave < nitem)
@@ -501,8 +505,8 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int mA = MT == 1 ? 0 : min(16 * t + n, M - 1);
-      pa1[t] = xs1 + mA * KW + 16 * q;
-      pa2[t] = xs2 + mA * KW + 16 * q;
+      pa1[t] = xs1 + (q * MT + mA) * 16;
+      pa2[t] = xs2 + (q * MT + mA) * 16;
     }
     auto bop = [&](int i) -> u32x4 {
       u32x4 b;
@@ -532,8 +536,8 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
       const u32x4 b = bop(0);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        d1[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1[t] + 64 * gs), b, zi);
-        d2[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2[t] + 64 * gs), b, cinit(gs, t));
+        d1[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1[t] + 64 * MT * gs), b, zi);
+        d2[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2[t] + 64 * MT * gs), b, cinit(gs, t));
       }
     }
 #pragma unroll
@@ -544,8 +548,8 @@ __device__ void consume(const DecodeArgs &a, int cidx, uint8_t *smem) {
         const u32x4 b = bop(i + 1 < MAXG ? i + 1 : i);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          e1[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1[t] + 64 * (g + 1)), b, zi);
-          e2[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2[t] + 64 * (g + 1)), b, cinit(g + 1, t));
+          e1[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa1[t] + 64 * MT * (g + 1)), b, zi);
+          e2[t] = mfma_i8(*reinterpret_cast<const u32x4 *>(pa2[t] + 64 * MT * (g + 1)), b, cinit(g + 1, t));
         }
       } else {
 #pragma unroll
@@ -712,7 +716,8 @@ size_t producer_lds(int unit) {
 
 size_t consumer_lds(int M, int unit, int KW, int nsr_pad) {
   const size_t nu = KW / unit, ngrp = KW / kGroup;
-  return static_cast<size_t>(2) * M * KW + ngrp * kTab * 4 + nu * kTab * 4 + static_cast<size_t>(kWaves) * kRed * 64 * 4 +
+  const size_t mt = M <= 1 ? 1 : M <= 4 ? 4 : M <= 16 ? 16 : 32;   // token rows of the plane layout
+  return static_cast<size_t>(2) * mt * KW + ngrp * kTab * 4 + nu * kTab * 4 + static_cast<size_t>(kWaves) * kRed * 64 * 4 +
          static_cast<size_t>(kUVec) * 64 * 16 + 2 * kMaxRT * kTile * 4 +
          static_cast<size_t>(M) * nsr_pad * 4 + 16;
 }
