@@ -72,7 +72,7 @@ __device__ __forceinline__ int plane_pos(int j) { return (j & 4) ? 16 + ((j >> 3
 // --------------------------------------------------------------------------- producer
 // Partial t of rotation unit u for the M rows: t[m][i] = sum_{k in u} x_rot[m][k] V[i][k].
 // The loads of x and of the first V k-steps go out together at the start.
-template <int MT, int C>
+template <int MT, int C, bool GT>
 __device__ __forceinline__ void gemv_produce(const GemvArgs &a, int u, uint8_t *smem) {
   constexpr int P = 256 * C;
   constexpr int LDB = P + 8;            // bf16 x_rot row in LDS
@@ -87,7 +87,7 @@ __device__ __forceinline__ void gemv_produce(const GemvArgs &a, int u, uint8_t *
   float *tred = reinterpret_cast<float *>(smem + 16 * LDB * 2);       // [W][NI][4][64]
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   const auto rv = make_rsrc(a.V, static_cast<uint32_t>(a.nsr) * a.K * 2);
-  const int xrow = a.gated ? 2 * a.K : a.K;            // inputs per row of x
+  const int xrow = GT ? 2 * a.K : a.K;            // inputs per row of x
   const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * xrow * 2);
 
   // x rows wave, wave + W (M <= 4 <= 2 W) (gated: the gate and the up
@@ -102,7 +102,7 @@ __device__ __forceinline__ void gemv_produce(const GemvArgs &a, int u, uint8_t *
       xu[j][c] = u32x2{0u, 0u};
     }
   }
-  if (a.gated)
+  if (GT)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int m = wave + j * W;
@@ -134,7 +134,7 @@ __device__ __forceinline__ void gemv_produce(const GemvArgs &a, int u, uint8_t *
   for (int j = 0; j < 2; ++j) {
     const int m = wave + j * W;
     if (m < M) {
-      if (a.gated) {
+      if (GT) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
           xw[j][c][0] = geglu_bf16x2(xw[j][c][0], xu[j][c][0]);
@@ -284,9 +284,107 @@ struct GemvLds {
   }
 };
 
+// Items (token m, unit u) of the K-range -> their 15-bit planes, 8 x group
+// sums and unit scales in LDS.  NI independent items (1 or 2) go through each
+// phase together, so that their dependent chains (matrix-core rotation,
+// wave-wide max, group sums) interleave.
+template <int C, bool T8, int NI>
+__device__ __forceinline__ void put_items(const GemvArgs &a, int lane, int8_t *pl1, int8_t *pl2, int *x8, float *esc,
+                                          int XP, const int *ms, const int *us, const u32x2 (*xw)[C]) {
+  constexpr int P = 256 * C;
+  const int n = lane & 15, q = lane >> 4;
+  float y[NI][C][4];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) rotate_x_item<C>(a.rotate, a.block, a.hscale, xw[i], y[i]);
+  uint32_t p1[NI][C], p2[NI][C], eb[NI];
+  int gsum[NI][C];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) eb[i] = quantize_fast<C>(y[i], p1[i], p2[i], gsum[i], lane);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int m = ms[i], u = us[i];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int kk = u * P + 256 * c + 16 * n + 4 * q;   // first of the lane's 4 inputs (range-local)
+      const int pos = T8 ? kk : (kk & ~31) + plane_pos(kk & 31);
+      *reinterpret_cast<uint32_t *>(pl1 + m * XP + pos) = p1[i][c];
+      *reinterpret_cast<uint32_t *>(pl2 + m * XP + pos) = p2[i][c];
+      if (!T8 && (lane & 0x33) == 0) x8[(kk >> 6) * kTokPad + m] = gsum[i][c];
+    }
+    if (lane == 0) esc[u * kTokPad + m] = __uint_as_float(eb[i]);
+  }
+}
+
+// x of item (m, u) from an LDS copy (gated: h = geglu(gate, up) formed here;
+// the up values sit uofs inputs after the gate values)
+template <int C, bool GT>
+__device__ __forceinline__ void fetch_item(const uint16_t *src, int e, int uofs, u32x2 (&xw)[C]) {
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    xw[c] = *reinterpret_cast<const u32x2 *>(src + e + 256 * c);
+    if (GT) {
+      const u32x2 uv = *reinterpret_cast<const u32x2 *>(src + uofs + e + 256 * c);
+      xw[c][0] = geglu_bf16x2(xw[c][0], uv[0]);
+      xw[c][1] = geglu_bf16x2(xw[c][1], uv[1]);
+    }
+  }
+}
+
+// Items it0, it0 + step, ... (< M nu) of the K-range, from the copy of x in LDS
+// ([M][KW], flattened), two at a time.
+template <int MT, int C, bool T8, bool GT>
+__device__ __forceinline__ void rotate_range(const GemvArgs &a, const GemvLds<MT> &sm, int lane, int it0, int step,
+                                             int uofs) {
+  constexpr int P = 256 * C;
+  const int n = lane & 15, q = lane >> 4;
+  const int M = a.M, KW = a.KW, nit = M * a.nu_w;
+  int it = it0;
+  for (; it + step < nit; it += 2 * step) {
+    int ms[2], us[2];
+    u32x2 xw[2][C];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = it + i * step;
+      ms[i] = e % M;
+      us[i] = e / M;
+      fetch_item<C, GT>(sm.xs, ms[i] * KW + us[i] * P + 16 * n + 4 * q, uofs, xw[i]);
+    }
+    put_items<C, T8, 2>(a, lane, sm.pl1, sm.pl2, sm.x8, sm.esc, sm.XP, ms, us, xw);
+  }
+  if (it < nit) {
+    int ms[1] = {it % M}, us[1] = {it / M};
+    u32x2 xw[1][C];
+    fetch_item<C, GT>(sm.xs, ms[0] * KW + us[0] * P + 16 * n + 4 * q, uofs, xw[0]);
+    put_items<C, T8, 1>(a, lane, sm.pl1, sm.pl2, sm.x8, sm.esc, sm.XP, ms, us, xw);
+  }
+}
+
+// The workgroup's copy of x of the K-range into LDS ([M][KW] flattened, 1 KB
+// per wavefront instruction, lane l's 16 bytes at byte 16 l; gated: the gate
+// values, then the up values): chunks c0, c0 + cstep, ...  Returns the offset
+// (in inputs) of the up values.
+template <int MT, bool GT>
+__device__ __forceinline__ int copy_x_range(const GemvArgs &a, const GemvLds<MT> &sm, int lane, int k0, int c0,
+                                            int cstep) {
+  const int M = a.M, K = a.K, span = 2 * a.KW;
+  const int nch = (M * span + 1023) >> 10;
+  const int xrow = GT ? 2 * K : K;
+  const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * xrow * 2);
+  uint8_t *dst = reinterpret_cast<uint8_t *>(sm.xs);
+  for (int h2 = 0; h2 < (GT ? 2 : 1); ++h2)
+    for (int c = c0; c < nch; c += cstep) {
+      const int f = c * 1024 + lane * 16;
+      const int m = f / span, kb = f - m * span;
+      const uint32_t off = m < M ? static_cast<uint32_t>(m * 2 * xrow + 2 * (h2 * K + k0) + kb) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void *)(dst + (h2 * nch + c) * 1024), 16, off, 0, 0, 0);
+    }
+  return GT ? nch * 512 : 0;
+}
+
 // Spare wavefront of a consumer workgroup (wavefront W): loads the tile's U
 // rows, output columns and INT8 scales, waits for the producers' t of the
-// range's units (stamped words, bounded wait per word), sums them in unit
+// range's units (stamped words, a bounded number of reloads), sums them in unit
 // order and forms the low-rank term of each (row, token), in parallel with the
 // compute wavefronts' main loop.
 template <int MT>
@@ -318,44 +416,40 @@ __device__ __forceinline__ void gemv_spare(const GemvArgs &a, int cidx, uint8_t 
     bare_barrier();   // (2) planes in LDS
   }
   // t[m][i] = sum over the range's units of their partial t, in unit order.
-  // First every unit's word (token 0, i = 0) is polled, one unit per lane, so
-  // that one round trip serves all units (the words of a unit are stored
-  // together); the per-word waits below then rarely spin.
+  // Each lane loads the words of its (token, i) for a batch of units at once
+  // and the batch is reloaded whole until every word carries this call's
+  // stamp: these loads return only after the weight loads issued before them
+  // on this compute unit, so each retry costs one such round trip, not one
+  // per word.
   bool late = false;
   const int64_t ustr = static_cast<int64_t>(kTokPad) * nsp;
-  for (int spins = 0;; ++spins) {
-    bool mine = true;
-    for (int j = lane; j < nu; j += 64)
-      mine = mine && static_cast<uint32_t>(ld_dev(a.tp + static_cast<int64_t>(u0 + j) * ustr) >> 32) == a.stamp;
-    if (__builtin_amdgcn_ballot_w64(!mine) == 0 || spins >= a.spin_limit) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  for (int e = lane; e < M * nsp; e += 64) {
+  const uint64_t fresh_word = static_cast<uint64_t>(a.stamp) << 32;
+  for (int e0 = 0; e0 < M * nsp; e0 += 64) {
+    const int e = e0 + lane;
     const int m = e / nsp, i = e - m * nsp;
+    const bool act = e < M * nsp && i < a.nsr;
+    const uint64_t *src = a.tp + (static_cast<int64_t>(u0) * kTokPad + m) * nsp + i;
     float s = 0.0f;
-    if (i < a.nsr) {
-      const uint64_t *src = a.tp + (static_cast<int64_t>(u0) * kTokPad + m) * nsp + i;
-      for (int u = 0; u < nu; u += kLoadBatch) {
-        uint64_t v[kLoadBatch];
+    for (int u = 0; u < nu; u += kLoadBatch) {
+      uint64_t v[kLoadBatch];
+      for (int spins = 0;; ++spins) {
 #pragma unroll
-        for (int j = 0; j < kLoadBatch; ++j) v[j] = u + j < nu ? ld_dev(src + (u + j) * ustr) : 0ull;
+        for (int j = 0; j < kLoadBatch; ++j) v[j] = act && u + j < nu ? ld_dev(src + (u + j) * ustr) : fresh_word;
+        bool fresh = true;
 #pragma unroll
-        for (int j = 0; j < kLoadBatch; ++j) {
-          if (u + j >= nu) continue;
-          int spins = 0;
-          while (static_cast<uint32_t>(v[j] >> 32) != a.stamp) {
-            if (++spins > a.spin_limit) {
-              late = true;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            v[j] = ld_dev(src + (u + j) * ustr);
-          }
-          s += __uint_as_float(static_cast<uint32_t>(v[j]));
+        for (int j = 0; j < kLoadBatch; ++j) fresh = fresh && static_cast<uint32_t>(v[j] >> 32) == a.stamp;
+        if (__builtin_amdgcn_ballot_w64(!fresh) == 0) break;
+        if (spins >= a.spin_limit) {
+          late = late || !fresh;
+          break;
         }
+        __builtin_amdgcn_s_sleep(1);
       }
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j)
+        if (act && u + j < nu) s += __uint_as_float(static_cast<uint32_t>(v[j]));
     }
-    sm.ts[e] = s;
+    if (e < M * nsp) sm.ts[e] = s;
   }
   if (__builtin_amdgcn_ballot_w64(late) != 0 && lane == 0) *sm.tout = 1;
   __builtin_amdgcn_s_waitcnt(kLgkm0);
@@ -398,7 +492,7 @@ __device__ __forceinline__ void gemv_spare(const GemvArgs &a, int cidx, uint8_t 
 // MT: largest M (1 or 4); C: 256-blocks per rotation unit; G: most groups per
 // compute wavefront (its load registers); T8: INT8 tier.  The compute
 // wavefronts 0 .. W-1 of a consumer workgroup (wavefront W is gemv_spare).
-template <int MT, int C, int G, bool T8>
+template <int MT, int C, int G, bool T8, bool GT>
 __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_t *smem) {
   constexpr int P = 256 * C;
   constexpr int GPU = P / kGroup;       // groups per rotation unit
@@ -431,52 +525,33 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   float *s8s = sm.s8s;
   int *tout = sm.tout;
 
-  // Item (token m, unit u) -> its 15-bit planes, 8 x group sums and unit
-  // scale in LDS.
-  auto put_item = [&](int m, int u, const u32x2 (&xw)[C]) {
-    const int n = lane & 15, q = lane >> 4;
-    float y[C][4];
-    rotate_x_item<C>(a.rotate, a.block, a.hscale, xw, y);
-    uint32_t p1[C], p2[C];
-    int gsum[C];
-    const uint32_t eb = quantize_fast<C>(y, p1, p2, gsum, lane);
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int kk = u * P + 256 * c + 16 * n + 4 * q;   // first of the lane's 4 inputs (range-local)
-      const int pos = T8 ? kk : (kk & ~31) + plane_pos(kk & 31);
-      *reinterpret_cast<uint32_t *>(pl1 + m * XP + pos) = p1[c];
-      *reinterpret_cast<uint32_t *>(pl2 + m * XP + pos) = p2[c];
-      if (!T8 && (lane & 0x33) == 0) x8[(kk >> 6) * kTokPad + m] = gsum[c];
-    }
-    if (lane == 0) esc[u * kTokPad + m] = __uint_as_float(eb);
-  };
-
   // ---- 1. activations first, straight into LDS (1 KB per wavefront
   // instruction, lane l's 16 bytes at byte 16 l; 16 | 2 KW, so a lane's bytes
-  // never straddle rows).  Local path (the wavefront's groups are whole
-  // rotation units): each wavefront copies the rows of its own units into
-  // its own slab [M][lnu P].  Shared path: the workgroup copies x of the
-  // K-range, flattened [M][KW].
+  // never straddle rows).  Local path (the wavefront's groups are whole rotation units): each
+  // wavefront copies the rows of its own units into its own slab [M][lnu P].
+  // Shared path: the workgroup copies x of the K-range, flattened [M][KW].
   const int lu0 = gw0 / GPU, lnu = ng / GPU;
   const int n = lane & 15, q = lane >> 4;
   const int LW = lnu * P;                               // local path: inputs of the slab's rows
   uint16_t *slab = xs + wave * (sm.xslab >> 1);         // local path: this wavefront's slab
-  const int span = a.local_rot ? 2 * LW : 2 * KW;        // bytes of one row of the copy
-  const int nch = (M * span + 1023) >> 10;               // 1 KB chunks of the copy
-  const int uofs = a.gated ? nch * 512 : 0;              // gated: the up values, inputs after the gate values
-  {
-    const int xrow = a.gated ? 2 * K : K;                // inputs per row of x
+  int uofs = 0;                                         // gated: the up values, inputs after the gate values
+  if (a.local_rot) {
+    const int span = 2 * LW, nch = (M * span + 1023) >> 10;
+    uofs = GT ? nch * 512 : 0;
+    const int xrow = GT ? 2 * K : K;
     const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * xrow * 2);
-    const int kbase = a.local_rot ? k0 + lu0 * P : k0;    // first input of the copy
-    uint8_t *dst = reinterpret_cast<uint8_t *>(a.local_rot ? slab : xs);
-    for (int h2 = 0; h2 < (a.gated ? 2 : 1); ++h2)
-      for (int c = a.local_rot ? 0 : wave; c < nch; c += a.local_rot ? 1 : W) {
+    const int kbase = k0 + lu0 * P;
+    uint8_t *dst = reinterpret_cast<uint8_t *>(slab);
+    for (int h2 = 0; h2 < (GT ? 2 : 1); ++h2)
+      for (int c = 0; c < nch; ++c) {
         const int f = c * 1024 + lane * 16;             // flattened byte
         const int m = f / span, kb = f - m * span;
         const uint32_t off = m < M ? static_cast<uint32_t>(m * 2 * xrow + 2 * (h2 * K + kbase) + kb) : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rx, (__attribute__((address_space(3))) void *)(dst + (h2 * nch + c) * 1024), 16, off, 0, 0, 0);
       }
+  } else {
+    uofs = copy_x_range<MT, GT>(a, sm, lane, k0, wave, W);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -511,40 +586,31 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   // other wavefront reads them); shared path, the range's items round-robin
   // after every wavefront's copy has landed
   if (a.local_rot) {
-    for (int it = 0; it < M * lnu; ++it) {
-      const int m = it % M, ul = it / M;
-      u32x2 xw[C];
+    const int nit = M * lnu;
+    int it = 0;
+    for (; it + 2 <= nit; it += 2) {
+      int ms[2], us[2];
+      u32x2 xw[2][C];
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int e = m * LW + ul * P + 256 * c + 16 * n + 4 * q;
-        xw[c] = *reinterpret_cast<const u32x2 *>(slab + e);
-        if (a.gated) {
-          const u32x2 uv = *reinterpret_cast<const u32x2 *>(slab + uofs + e);
-          xw[c][0] = geglu_bf16x2(xw[c][0], uv[0]);
-          xw[c][1] = geglu_bf16x2(xw[c][1], uv[1]);
-        }
+      for (int i = 0; i < 2; ++i) {
+        ms[i] = (it + i) % M;
+        const int ul = (it + i) / M;
+        us[i] = lu0 + ul;
+        fetch_item<C, GT>(slab, ms[i] * LW + ul * P + 16 * n + 4 * q, uofs, xw[i]);
       }
-      put_item(m, lu0 + ul, xw);
+      put_items<C, T8, 2>(a, lane, pl1, pl2, x8, esc, XP, ms, us, xw);
+    }
+    if (it < nit) {
+      int ms[1] = {it % M}, us[1] = {lu0 + it / M};
+      u32x2 xw[1][C];
+      fetch_item<C, GT>(slab, ms[0] * LW + (it / M) * P + 16 * n + 4 * q, uofs, xw[0]);
+      put_items<C, T8, 1>(a, lane, pl1, pl2, x8, esc, XP, ms, us, xw);
     }
     __builtin_amdgcn_s_waitcnt(kLgkm0);
     __builtin_amdgcn_wave_barrier();
   } else {
     bare_barrier();   // (1)
-    for (int it = wave; it < M * nu; it += W) {
-      const int m = it % M, u = it / M;
-      u32x2 xw[C];
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int e = m * KW + u * P + 256 * c + 16 * n + 4 * q;
-        xw[c] = *reinterpret_cast<const u32x2 *>(xs + e);
-        if (a.gated) {
-          const u32x2 uv = *reinterpret_cast<const u32x2 *>(xs + uofs + e);
-          xw[c][0] = geglu_bf16x2(xw[c][0], uv[0]);
-          xw[c][1] = geglu_bf16x2(xw[c][1], uv[1]);
-        }
-      }
-      put_item(m, u, xw);
-    }
+    rotate_range<MT, C, T8, GT>(a, sm, lane, wave, W, uofs);
     __builtin_amdgcn_s_waitcnt(kLgkm0);
     bare_barrier();   // (2)
   }
@@ -666,18 +732,18 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   }
 }
 
-template <int MT, int C, int G>
+template <int MT, int C, int G, bool GT>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int b = blockIdx.x;
   if (b < a.nprod) {
-    gemv_produce<MT, C>(a, b, smem);
+    gemv_produce<MT, C, GT>(a, b, smem);
     return;
   }
   const int c = b - a.nprod;   // consumer index = tile * S + range
   if (static_cast<int>(threadIdx.x >> 6) == a.W) gemv_spare<MT>(a, c, smem);
-  else if (c < a.t4 * a.S) gemv_consume<MT, C, G, false>(a, c, smem);
-  else gemv_consume<MT, C, G, true>(a, c, smem);
+  else if (c < a.t4 * a.S) gemv_consume<MT, C, G, false, GT>(a, c, smem);
+  else gemv_consume<MT, C, G, true, GT>(a, c, smem);
 }
 
 size_t producer_lds(int unit, int W, int nsp) {
@@ -692,16 +758,23 @@ size_t consumer_lds(int MT, int M, int KW, int nu, int W, int GPW, int nsp, bool
          (static_cast<size_t>(W) + 1) * NV * 64 * 4 + static_cast<size_t>(MT) * nsp * 4 + 2 * kRows * 4 + 16;
 }
 
-template <int MT, int C, int G>
-hipError_t launch_t(const GemvArgs &a, size_t lds, hipStream_t s) {
+template <int MT, int C, int G, bool GT>
+hipError_t launch_gt(const GemvArgs &a, size_t lds, hipStream_t s) {
   if (lds > 65536) {
     static std::atomic<uint64_t> done{0};
-    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(gemv_kernel<MT, C, G>), 160 * 1024, done);
+    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(gemv_kernel<MT, C, G, GT>), 160 * 1024, done);
     if (e != hipSuccess) return e;
   }
   const int grid = a.nprod + (a.t4 + a.t8) * a.S;
-  return launch_kernel(reinterpret_cast<const void *>(gemv_kernel<MT, C, G>), dim3(grid), dim3(64 * (a.W + 1)), lds, s,
-                       a);
+  return launch_kernel(reinterpret_cast<const void *>(gemv_kernel<MT, C, G, GT>), dim3(grid), dim3(64 * (a.W + 1)),
+                       lds, s, a);
+}
+
+// the gated input (h formed from the gate+up output as it loads) is its own
+// instantiation, so that the plain kernel carries none of its code
+template <int MT, int C, int G>
+hipError_t launch_t(const GemvArgs &a, size_t lds, hipStream_t s) {
+  return a.gated ? launch_gt<MT, C, G, true>(a, lds, s) : launch_gt<MT, C, G, false>(a, lds, s);
 }
 
 template <int MT, int C>
