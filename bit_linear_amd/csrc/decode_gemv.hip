@@ -52,6 +52,10 @@ __device__ __forceinline__ i32x16 mfma32_i8(u32x4 a, u32x4 b, i32x16 c) {
                                                0);
 }
 
+// it / M for 0 <= it < 2048 and 1 <= M <= 32, with rM = ceil(2^16 / M)
+// (a multiply instead of a division)
+__device__ __forceinline__ int div_m(int it, uint32_t rM) { return static_cast<int>((static_cast<uint32_t>(it) * rM) >> 16); }
+
 // s_waitcnt with vmcnt <= n (n < 64) and the other counters free
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 constexpr int kLgkm0 = 0xC07F;    // lgkmcnt(0), vmcnt and expcnt free
@@ -81,7 +85,7 @@ __device__ __forceinline__ void gemv_produce(const GemvArgs &a, int u, uint8_t *
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int W = static_cast<int>(blockDim.x >> 6);   // every wavefront of the block (>= 2)
   const int n = lane & 15, q = lane >> 4;
-  const int M = a.M, k0 = u * P;
+  const int M = MT == 1 ? 1 : a.M, k0 = u * P;   // MT = 1: one token
   const int nsp = a.nsr_pad, NI = nsp / 16;
   uint16_t *xb = reinterpret_cast<uint16_t *>(smem);                  // [16][LDB], rows >= M zero
   float *tred = reinterpret_cast<float *>(smem + 16 * LDB * 2);       // [W][NI][4][64]
@@ -337,7 +341,8 @@ __device__ __forceinline__ void rotate_range(const GemvArgs &a, const GemvLds<MT
                                              int uofs) {
   constexpr int P = 256 * C;
   const int n = lane & 15, q = lane >> 4;
-  const int M = a.M, KW = a.KW, nit = M * a.nu_w;
+  const int M = MT == 1 ? 1 : a.M, KW = a.KW, nit = M * a.nu_w;
+  const uint32_t rM = (65536u + M - 1) / M;
   int it = it0;
   for (; it + step < nit; it += 2 * step) {
     int ms[2], us[2];
@@ -345,14 +350,15 @@ __device__ __forceinline__ void rotate_range(const GemvArgs &a, const GemvLds<MT
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int e = it + i * step;
-      ms[i] = e % M;
-      us[i] = e / M;
+      us[i] = div_m(e, rM);
+      ms[i] = e - us[i] * M;
       fetch_item<C, GT>(sm.xs, ms[i] * KW + us[i] * P + 16 * n + 4 * q, uofs, xw[i]);
     }
     put_items<C, T8, 2>(a, lane, sm.pl1, sm.pl2, sm.x8, sm.esc, sm.XP, ms, us, xw);
   }
   if (it < nit) {
-    int ms[1] = {it % M}, us[1] = {it / M};
+    int us[1] = {div_m(it, rM)};
+    int ms[1] = {it - us[0] * M};
     u32x2 xw[1][C];
     fetch_item<C, GT>(sm.xs, ms[0] * KW + us[0] * P + 16 * n + 4 * q, uofs, xw[0]);
     put_items<C, T8, 1>(a, lane, sm.pl1, sm.pl2, sm.x8, sm.esc, sm.XP, ms, us, xw);
@@ -366,7 +372,7 @@ __device__ __forceinline__ void rotate_range(const GemvArgs &a, const GemvLds<MT
 template <int MT, bool GT>
 __device__ __forceinline__ int copy_x_range(const GemvArgs &a, const GemvLds<MT> &sm, int lane, int k0, int c0,
                                             int cstep) {
-  const int M = a.M, K = a.K, span = 2 * a.KW;
+  const int M = MT == 1 ? 1 : a.M, K = a.K, span = 2 * a.KW;
   const int nch = (M * span + 1023) >> 10;
   const int xrow = GT ? 2 * K : K;
   const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * xrow * 2);
@@ -398,7 +404,7 @@ __device__ __forceinline__ void gemv_spare(const GemvArgs &a, int cidx, uint8_t 
   const int row0 = (T8 ? tile - a.t4 : tile) * kRows;
   const int nrow = min(kRows, rows - row0);
   const int prow = row0 + min(r, nrow - 1), pk = (T8 ? a.n4 : 0) + prow;
-  const int M = a.M, KGw = a.KW >> 6, nu = a.nu_w, u0 = sp * nu, nsp = a.nsr_pad;
+  const int M = MT == 1 ? 1 : a.M, KGw = a.KW >> 6, nu = a.nu_w, u0 = sp * nu, nsp = a.nsr_pad;
   float *x8f = reinterpret_cast<float *>(sm.x8);
   u32x4 uv[8];
   const auto ru = make_rsrc(a.U, static_cast<uint32_t>(a.N) * a.r * 2);
@@ -505,7 +511,8 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   const int rows = T8 ? a.n8 : a.n4;
   const int row0 = (T8 ? tile - a.t4 : tile) * kRows;    // first row of the tile inside the tier
   const int nrow = min(kRows, rows - row0);
-  const int M = a.M, K = a.K, KW = a.KW, k0 = sp * KW;
+  const int M = MT == 1 ? 1 : a.M, K = a.K, KW = a.KW, k0 = sp * KW;
+  const uint32_t rM = (65536u + M - 1) / M;   // div_m
   const int KG = K >> 6, KGw = KW >> 6, gk0 = k0 >> 6;   // groups: whole K, this range, first of the range
   const int nu = a.nu_w, u0 = sp * nu;
   const int GPW = a.GPW, gw0 = wave * GPW;              // this wavefront's first group inside the range
@@ -593,17 +600,18 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
       u32x2 xw[2][C];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        ms[i] = (it + i) % M;
-        const int ul = (it + i) / M;
+        const int ul = div_m(it + i, rM);
+        ms[i] = it + i - ul * M;
         us[i] = lu0 + ul;
         fetch_item<C, GT>(slab, ms[i] * LW + ul * P + 16 * n + 4 * q, uofs, xw[i]);
       }
       put_items<C, T8, 2>(a, lane, pl1, pl2, x8, esc, XP, ms, us, xw);
     }
     if (it < nit) {
-      int ms[1] = {it % M}, us[1] = {lu0 + it / M};
+      const int ul = div_m(it, rM);
+      int ms[1] = {it - ul * M}, us[1] = {lu0 + ul};
       u32x2 xw[1][C];
-      fetch_item<C, GT>(slab, ms[0] * LW + (it / M) * P + 16 * n + 4 * q, uofs, xw[0]);
+      fetch_item<C, GT>(slab, ms[0] * LW + ul * P + 16 * n + 4 * q, uofs, xw[0]);
       put_items<C, T8, 1>(a, lane, pl1, pl2, x8, esc, XP, ms, us, xw);
     }
     __builtin_amdgcn_s_waitcnt(kLgkm0);

@@ -173,7 +173,7 @@ __device__ __forceinline__ f32x4 mfma16_bf16(u32x2 a, u32x2 b, f32x4 c) {
 
 // bf16 entry (a, b) of the 16x16 block-diagonal matrix with Sylvester blocks H_R
 __device__ __forceinline__ uint32_t sylvester_bf16(int a, int b, int R) {
-  if ((a / R) != (b / R)) return 0u;
+  if ((a ^ b) & ~(R - 1)) return 0u;   // different blocks (R a power of two)
   return (__popc(a & b & (R - 1)) & 1) ? 0xBF80u : 0x3F80u;
 }
 
