@@ -262,7 +262,6 @@ static int gemv_launch(const dvssq_layout &L, const WsLayout &W, const GemvPlan 
   g.t4 = (L.n_int4 + 31) / 32;
   g.t8 = (L.n_int8 + 31) / 32;
   g.nprod = g.nunit;
-  g.local_rot = gp.local_rot;
   g.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
   g.publish = (flags & DVSSQ_TEST_NO_PUBLISH) ? 0 : 1;
   g.spin_limit = (flags & DVSSQ_TEST_NO_PUBLISH) ? kTestSpinLimit : kSpinLimit;

@@ -10,10 +10,11 @@
 // 16-byte loads, one INT4 group (32 bytes of a row) per pair of lanes (two
 // 16-byte loads of a row per INT8 group), the operand layout of the int8
 // matrix core v_mfma_i32_32x32x32_i8: lane (r, h) holds row r, bytes 16 h ..
-// 16 h + 15 of the group.  Before any weight load, the workgroup copies the
-// activations of its K-range straight into LDS (buffer loads to LDS); after
-// them, the wavefronts rotate and quantize the (token, rotation unit) items
-// while the weights stream in: each item of x_rot becomes a 15-bit integer
+// 16 h + 15 of the group.  A wavefront's groups are whole rotation units:
+// before any weight load it copies the activations of its units straight
+// into LDS (buffer loads to LDS); after them, it rotates and quantizes its
+// (token, rotation unit) items while the weights stream in (two items at a
+// time, so that their dependent chains interleave): each item of x_rot becomes a 15-bit integer
 // X = 256 x1 + x2 with a power-of-two scale 2^e, stored as two int8 planes.
 // Per group, four matrix-core instructions (the low and the high nibbles of
 // the codes, times each plane) sum exactly in int32:
@@ -260,7 +261,7 @@ __device__ __forceinline__ uint32_t quantize_fast(const float (&y)[C][4], uint32
 template <int MT>
 struct GemvLds {
   static constexpr int NV = MT == 1 ? 1 : 4;   // result values per lane that can hold a token (lanes h = 0)
-  int XP, xbytes, xslab;   // xslab: bytes of one wavefront's slab (local path)
+  int XP, xbytes, xslab;   // xslab: bytes of one wavefront's slab of x
   uint16_t *xs;
   int8_t *pl1, *pl2;
   int *x8;
@@ -273,7 +274,7 @@ struct GemvLds {
     XP = KW + 16;
     const int gx = a.gated ? 2 : 1;    // gated: the gate values, then the up values
     xslab = gx * ((a.M * a.GPW * kGroup * 2 + 1023) & ~1023);
-    xbytes = max(gx * ((a.M * KW * 2 + 1023) & ~1023), a.W * xslab);
+    xbytes = a.W * xslab;
     xs = reinterpret_cast<uint16_t *>(smem);
     pl1 = reinterpret_cast<int8_t *>(smem + xbytes);
     pl2 = pl1 + MT * XP;
@@ -334,60 +335,6 @@ __device__ __forceinline__ void fetch_item(const uint16_t *src, int e, int uofs,
   }
 }
 
-// Items it0, it0 + step, ... (< M nu) of the K-range, from the copy of x in LDS
-// ([M][KW], flattened), two at a time.
-template <int MT, int C, bool T8, bool GT>
-__device__ __forceinline__ void rotate_range(const GemvArgs &a, const GemvLds<MT> &sm, int lane, int it0, int step,
-                                             int uofs) {
-  constexpr int P = 256 * C;
-  const int n = lane & 15, q = lane >> 4;
-  const int M = MT == 1 ? 1 : a.M, KW = a.KW, nit = M * a.nu_w;
-  const uint32_t rM = (65536u + M - 1) / M;
-  int it = it0;
-  for (; it + step < nit; it += 2 * step) {
-    int ms[2], us[2];
-    u32x2 xw[2][C];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = it + i * step;
-      us[i] = div_m(e, rM);
-      ms[i] = e - us[i] * M;
-      fetch_item<C, GT>(sm.xs, ms[i] * KW + us[i] * P + 16 * n + 4 * q, uofs, xw[i]);
-    }
-    put_items<C, T8, 2>(a, lane, sm.pl1, sm.pl2, sm.x8, sm.esc, sm.XP, ms, us, xw);
-  }
-  if (it < nit) {
-    int us[1] = {div_m(it, rM)};
-    int ms[1] = {it - us[0] * M};
-    u32x2 xw[1][C];
-    fetch_item<C, GT>(sm.xs, ms[0] * KW + us[0] * P + 16 * n + 4 * q, uofs, xw[0]);
-    put_items<C, T8, 1>(a, lane, sm.pl1, sm.pl2, sm.x8, sm.esc, sm.XP, ms, us, xw);
-  }
-}
-
-// The workgroup's copy of x of the K-range into LDS ([M][KW] flattened, 1 KB
-// per wavefront instruction, lane l's 16 bytes at byte 16 l; gated: the gate
-// values, then the up values): chunks c0, c0 + cstep, ...  Returns the offset
-// (in inputs) of the up values.
-template <int MT, bool GT>
-__device__ __forceinline__ int copy_x_range(const GemvArgs &a, const GemvLds<MT> &sm, int lane, int k0, int c0,
-                                            int cstep) {
-  const int M = MT == 1 ? 1 : a.M, K = a.K, span = 2 * a.KW;
-  const int nch = (M * span + 1023) >> 10;
-  const int xrow = GT ? 2 * K : K;
-  const auto rx = make_rsrc(a.x, static_cast<uint32_t>(M) * xrow * 2);
-  uint8_t *dst = reinterpret_cast<uint8_t *>(sm.xs);
-  for (int h2 = 0; h2 < (GT ? 2 : 1); ++h2)
-    for (int c = c0; c < nch; c += cstep) {
-      const int f = c * 1024 + lane * 16;
-      const int m = f / span, kb = f - m * span;
-      const uint32_t off = m < M ? static_cast<uint32_t>(m * 2 * xrow + 2 * (h2 * K + k0) + kb) : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (__attribute__((address_space(3))) void *)(dst + (h2 * nch + c) * 1024), 16, off, 0, 0, 0);
-    }
-  return GT ? nch * 512 : 0;
-}
-
 // Spare wavefront of a consumer workgroup (wavefront W): loads the tile's U
 // rows, output columns and INT8 scales, waits for the producers' t of the
 // range's units (stamped words, a bounded number of reloads), sums them in unit
@@ -405,7 +352,6 @@ __device__ __forceinline__ void gemv_spare(const GemvArgs &a, int cidx, uint8_t 
   const int nrow = min(kRows, rows - row0);
   const int prow = row0 + min(r, nrow - 1), pk = (T8 ? a.n4 : 0) + prow;
   const int M = MT == 1 ? 1 : a.M, KGw = a.KW >> 6, nu = a.nu_w, u0 = sp * nu, nsp = a.nsr_pad;
-  float *x8f = reinterpret_cast<float *>(sm.x8);
   u32x4 uv[8];
   const auto ru = make_rsrc(a.U, static_cast<uint32_t>(a.N) * a.r * 2);
   const uint32_t ob = static_cast<uint32_t>(pk) * a.r * 2;
@@ -413,14 +359,8 @@ __device__ __forceinline__ void gemv_spare(const GemvArgs &a, int cidx, uint8_t 
   for (int j = 0; j < 8; ++j) uv[j] = buf_load16(ru, 8 * j < a.r ? ob + 16 * j : kOutOfRange);
   const uint32_t colv = a.idx[pk];
   const float s8v = T8 ? a.s8[prow] : 1.0f;
-  if (!a.local_rot)
-    for (int e = lane; e < (KGw + nu) * kTokPad; e += 64) x8f[e] = 0.0f;   // x8 and esc start at zero
   if (lane == 0) *sm.tout = 0;
   __builtin_amdgcn_s_waitcnt(kLgkm0);
-  if (!a.local_rot) {
-    bare_barrier();   // (1) x in LDS
-    bare_barrier();   // (2) planes in LDS
-  }
   // t[m][i] = sum over the range's units of their partial t, in unit order.
   // Each lane loads the words of its (token, i) for a batch of units at once
   // and the batch is reloaded whole until every word carries this call's
@@ -532,17 +472,16 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   float *s8s = sm.s8s;
   int *tout = sm.tout;
 
-  // ---- 1. activations first, straight into LDS (1 KB per wavefront
-  // instruction, lane l's 16 bytes at byte 16 l; 16 | 2 KW, so a lane's bytes
-  // never straddle rows).  Local path (the wavefront's groups are whole rotation units): each
-  // wavefront copies the rows of its own units into its own slab [M][lnu P].
-  // Shared path: the workgroup copies x of the K-range, flattened [M][KW].
+  // ---- 1. activations first, straight into LDS: each wavefront copies the
+  // rows of its own rotation units (its groups are whole units) into its own
+  // slab [M][lnu P] (1 KB per wavefront instruction, lane l's 16 bytes at
+  // byte 16 l; 16 | 2 lnu P, so a lane's bytes never straddle rows)
   const int lu0 = gw0 / GPU, lnu = ng / GPU;
   const int n = lane & 15, q = lane >> 4;
-  const int LW = lnu * P;                               // local path: inputs of the slab's rows
-  uint16_t *slab = xs + wave * (sm.xslab >> 1);         // local path: this wavefront's slab
+  const int LW = lnu * P;                               // inputs of the slab's rows
+  uint16_t *slab = xs + wave * (sm.xslab >> 1);         // this wavefront's slab
   int uofs = 0;                                         // gated: the up values, inputs after the gate values
-  if (a.local_rot) {
+  {
     const int span = 2 * LW, nch = (M * span + 1023) >> 10;
     uofs = GT ? nch * 512 : 0;
     const int xrow = GT ? 2 * K : K;
@@ -557,8 +496,6 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rx, (__attribute__((address_space(3))) void *)(dst + (h2 * nch + c) * 1024), 16, off, 0, 0, 0);
       }
-  } else {
-    uofs = copy_x_range<MT, GT>(a, sm, lane, k0, wave, W);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -589,39 +526,31 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   // the activations of this wavefront have landed
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterX));
 
-  // ---- 3. rotate and quantize: local path, this wavefront's own items (no
-  // other wavefront reads them); shared path, the range's items round-robin
-  // after every wavefront's copy has landed
-  if (a.local_rot) {
-    const int nit = M * lnu;
-    int it = 0;
-    for (; it + 2 <= nit; it += 2) {
-      int ms[2], us[2];
-      u32x2 xw[2][C];
+  // ---- 3. rotate and quantize this wavefront's own items (no other
+  // wavefront reads them), two at a time
+  const int nit = M * lnu;
+  int it = 0;
+  for (; it + 2 <= nit; it += 2) {
+    int ms[2], us[2];
+    u32x2 xw[2][C];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ul = div_m(it + i, rM);
-        ms[i] = it + i - ul * M;
-        us[i] = lu0 + ul;
-        fetch_item<C, GT>(slab, ms[i] * LW + ul * P + 16 * n + 4 * q, uofs, xw[i]);
-      }
-      put_items<C, T8, 2>(a, lane, pl1, pl2, x8, esc, XP, ms, us, xw);
+    for (int i = 0; i < 2; ++i) {
+      const int ul = div_m(it + i, rM);
+      ms[i] = it + i - ul * M;
+      us[i] = lu0 + ul;
+      fetch_item<C, GT>(slab, ms[i] * LW + ul * P + 16 * n + 4 * q, uofs, xw[i]);
     }
-    if (it < nit) {
-      const int ul = div_m(it, rM);
-      int ms[1] = {it - ul * M}, us[1] = {lu0 + ul};
-      u32x2 xw[1][C];
-      fetch_item<C, GT>(slab, ms[0] * LW + ul * P + 16 * n + 4 * q, uofs, xw[0]);
-      put_items<C, T8, 1>(a, lane, pl1, pl2, x8, esc, XP, ms, us, xw);
-    }
-    __builtin_amdgcn_s_waitcnt(kLgkm0);
-    __builtin_amdgcn_wave_barrier();
-  } else {
-    bare_barrier();   // (1)
-    rotate_range<MT, C, T8, GT>(a, sm, lane, wave, W, uofs);
-    __builtin_amdgcn_s_waitcnt(kLgkm0);
-    bare_barrier();   // (2)
+    put_items<C, T8, 2>(a, lane, pl1, pl2, x8, esc, XP, ms, us, xw);
   }
+  if (it < nit) {
+    const int ul = div_m(it, rM);
+    int ms[1] = {it - ul * M}, us[1] = {lu0 + ul};
+    u32x2 xw[1][C];
+    fetch_item<C, GT>(slab, ms[0] * LW + ul * P + 16 * n + 4 * q, uofs, xw[0]);
+    put_items<C, T8, 1>(a, lane, pl1, pl2, x8, esc, XP, ms, us, xw);
+  }
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_wave_barrier();
 
   // ---- 4. main loop: four int8 matrix-core instructions per group
   float acc[NV];
@@ -761,7 +690,7 @@ size_t producer_lds(int unit, int W, int nsp) {
 size_t consumer_lds(int MT, int M, int KW, int nu, int W, int GPW, int nsp, bool gated) {
   const size_t NV = MT == 1 ? 1 : 4, gx = gated ? 2 : 1;
   const size_t xslab = gx * ((static_cast<size_t>(M) * GPW * kGroup * 2 + 1023) & ~size_t(1023));
-  const size_t xbytes = std::max(gx * ((static_cast<size_t>(M) * KW * 2 + 1023) & ~size_t(1023)), W * xslab);
+  const size_t xbytes = W * xslab;
   return xbytes + 2 * static_cast<size_t>(MT) * (KW + 16) + static_cast<size_t>(KW / kGroup + nu) * kTokPad * 4 +
          (static_cast<size_t>(W) + 1) * NV * 64 * 4 + static_cast<size_t>(MT) * nsp * 4 + 2 * kRows * 4 + 16;
 }

@@ -723,7 +723,6 @@ struct GemvArgs {
   int W, GPW;          // wavefronts per workgroup, groups of 64 per wavefront (even)
   int t4, t8;          // 32-row tiles of each tier
   int nprod;           // producer workgroups (one per rotation unit)
-  int local_rot;       // 1: each compute wavefront rotates the units of its own groups
   int rotate, publish, spin_limit;
   int gated;           // 1: the input row m is h = geglu(x[m][0 .. K), x[m][K .. 2K)), formed as it loads
   float hscale;        // 1/sqrt(block)
