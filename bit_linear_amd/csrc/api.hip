@@ -259,6 +259,7 @@ static int gemv_launch(const dvssq_layout &L, const WsLayout &W, const GemvPlan 
   g.nu_w = g.nunit / gp.S;
   g.W = gp.W;
   g.GPW = gp.GPW;
+  g.lut_units = gp.lut_units;
   g.t4 = (L.n_int4 + 31) / 32;
   g.t8 = (L.n_int8 + 31) / 32;
   g.nprod = g.nunit;

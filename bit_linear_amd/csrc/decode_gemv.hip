@@ -455,8 +455,13 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   const uint32_t rM = (65536u + M - 1) / M;   // div_m
   const int KG = K >> 6, KGw = KW >> 6, gk0 = k0 >> 6;   // groups: whole K, this range, first of the range
   const int nu = a.nu_w, u0 = sp * nu;
-  const int GPW = a.GPW, gw0 = wave * GPW;              // this wavefront's first group inside the range
-  const int ng = max(0, min(GPW, KGw - gw0));
+  // this wavefront's rotation units of the range (lut_units: 4 bits per
+  // wavefront, in wavefront order); its first group inside the range, its groups
+  int ustart = 0;
+  for (int j = 0; j < wave; ++j) ustart += static_cast<int>((a.lut_units >> (4 * j)) & 15u);
+  const int ucnt = static_cast<int>((a.lut_units >> (4 * wave)) & 15u);
+  const int gw0 = ustart * GPU;
+  const int ng = max(0, min(ucnt * GPU, KGw - gw0));
   const int nsp = a.nsr_pad;
   const bool row_ok = r < nrow;
   const int prow = row0 + min(r, nrow - 1);                // row inside the tier
@@ -476,7 +481,7 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
   // rows of its own rotation units (its groups are whole units) into its own
   // slab [M][lnu P] (1 KB per wavefront instruction, lane l's 16 bytes at
   // byte 16 l; 16 | 2 lnu P, so a lane's bytes never straddle rows)
-  const int lu0 = gw0 / GPU, lnu = ng / GPU;
+  const int lu0 = ustart, lnu = ng / GPU;
   const int n = lane & 15, q = lane >> 4;
   const int LW = lnu * P;                               // inputs of the slab's rows
   uint16_t *slab = xs + wave * (sm.xslab >> 1);         // this wavefront's slab
@@ -733,6 +738,40 @@ hipError_t launch_m(const GemvArgs &a, size_t lds, hipStream_t s) {
 
 }  // namespace
 
+// One more compute wavefront where the even split puts two of them on one
+// SIMD: the wavefronts of a workgroup sit on the four SIMDs in turn
+// (wavefront w on SIMD w mod 4, the spare one on SIMD W mod 4), and two
+// compute wavefronts on one SIMD share its issue slots, so with W = 5 the
+// pair on SIMD 0 finishes its rotation and main loop well after the others.
+// With W + 1 wavefronts of at most upw units each, the units go one by one
+// to the wavefront whose SIMD carries the fewest so far (the spare counted as
+// half a unit); taken if the busiest SIMD then carries fewer units.
+bool spread_units(int nu, int upw, GemvPlan *p) {
+  const int W = p->W, W1 = W + 1;
+  if (W1 + 1 > 8 || nu > W1 * upw) return false;   // 64 (W1 + 1) threads within the launch bound
+  auto busiest = [](const double (&l)[4]) { return std::max(std::max(l[0], l[1]), std::max(l[2], l[3])); };
+  double even[4] = {0.0, 0.0, 0.0, 0.0}, load[4] = {0.0, 0.0, 0.0, 0.0};
+  even[W % 4] += 0.5;
+  for (int w = 0; w < W; ++w) even[w % 4] += static_cast<double>((p->lut_units >> (4 * w)) & 15u);
+  load[W1 % 4] += 0.5;
+  int cnt[8] = {0};
+  for (int u = 0; u < nu; ++u) {
+    int best = -1;
+    for (int w = 0; w < W1; ++w) {
+      if (cnt[w] >= upw) continue;
+      if (best < 0 || load[w % 4] < load[best % 4] - 1e-9) best = w;
+    }
+    ++cnt[best];
+    load[best % 4] += 1.0;
+  }
+  if (busiest(load) >= busiest(even) - 1e-9) return false;
+  uint64_t lut = 0;
+  for (int w = 0; w < W1; ++w) lut |= static_cast<uint64_t>(cnt[w]) << (4 * w);
+  p->W = W1;
+  p->lut_units = lut;
+  return true;
+}
+
 // Plan of the few-token decode: S equal K-ranges (each a whole number of
 // rotation units), the smallest S that gives every compute unit a workgroup
 // (or the largest feasible), and W compute wavefronts per workgroup (plus the
@@ -777,6 +816,16 @@ bool plan_gemv(const dvssq_layout &L, int M, int cus, bool gated, GemvPlan *p) {
     // each wavefront rotates its own units when its groups are whole units (at most two)
     const int gpu = unit / kGroup;
     p->local_rot = (gpw % gpu == 0 && gpw <= 2 * gpu) ? 1 : 0;
+    p->lut_units = 0;
+    for (int w = 0; w < W; ++w)   // gpw / gpu units each, the last wavefront the rest
+      p->lut_units |= static_cast<uint64_t>(std::min(gpw / gpu, nu - w * (gpw / gpu))) << (4 * w);
+    if (p->local_rot) {
+      const GemvPlan even = *p;
+      if (!spread_units(nu, gpw / gpu, p) ||
+          std::max(consumer_lds(MT, M, L.K / S, nu, p->W, p->GPW, nsp, gated), producer_lds(unit, p->W + 1, nsp)) >
+              160 * 1024)
+        *p = even;
+    }
     found = true;
     if (tiles * S >= cus) break;
   }

@@ -720,7 +720,8 @@ struct GemvArgs {
   uint32_t stamp;      // nonzero 32-bit stamp of this call
   int N, K, r, n_seg, n4, n8, M, block, unit, nunit, nsr, nsr_pad;
   int S, KW, nu_w;     // K-ranges, inputs and rotation units per range
-  int W, GPW;          // wavefronts per workgroup, groups of 64 per wavefront (even)
+  int W, GPW;          // wavefronts per workgroup, most groups of 64 of a wavefront (even)
+  uint64_t lut_units;  // rotation units of the range per compute wavefront, 4 bits each (in wavefront order)
   int t4, t8;          // 32-row tiles of each tier
   int nprod;           // producer workgroups (one per rotation unit)
   int rotate, publish, spin_limit;
@@ -729,6 +730,7 @@ struct GemvArgs {
 };
 struct GemvPlan {
   int S, W, GPW, local_rot;
+  uint64_t lut_units;   // rotation units of each compute wavefront, 4 bits each
 };
 bool plan_gemv(const dvssq_layout &L, int M, int cus, bool gated, GemvPlan *plan);
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);
