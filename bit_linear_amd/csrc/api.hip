@@ -263,6 +263,12 @@ static int gemv_launch(const dvssq_layout &L, const WsLayout &W, const GemvPlan 
   g.t4 = (L.n_int4 + 31) / 32;
   g.t8 = (L.n_int8 + 31) / 32;
   g.nprod = g.nunit;
+  {
+    // with up to two blocks per compute unit, those beyond one per unit share
+    // units with the first ones: let those be INT4 consumers on both sides
+    const int grid = g.nprod + (g.t4 + g.t8) * g.S, cus = compute_units();
+    g.lead4 = grid <= cus || grid > 2 * cus ? -1 : std::min(grid - cus, g.t4 * g.S);
+  }
   g.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
   g.publish = (flags & DVSSQ_TEST_NO_PUBLISH) ? 0 : 1;
   g.spin_limit = (flags & DVSSQ_TEST_NO_PUBLISH) ? kTestSpinLimit : kSpinLimit;

@@ -677,12 +677,32 @@ __device__ __forceinline__ void gemv_consume(const GemvArgs &a, int cidx, uint8_
 template <int MT, int C, int G, bool GT>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
+  // Block b runs on compute unit b mod (compute units) while every block of
+  // the grid is resident at once, so with cus < G <= 2 cus blocks the first
+  // G - cus positions share a unit with the last ones.  Roles by position
+  // (lead4 >= 0): INT4 consumers 0 .. lead4 - 1 (they share with INT4
+  // consumers at the end), then the INT8 consumers (twice an INT4 tile's
+  // bytes) and the producers, each on a unit of its own, then the other INT4
+  // consumers.  lead4 < 0: producers, INT4, INT8.
   const int b = blockIdx.x;
-  if (b < a.nprod) {
-    gemv_produce<MT, C, GT>(a, b, smem);
+  const int n8c = a.t8 * a.S, lead = a.lead4;
+  int c;   // consumer index = tile * S + range
+  if (lead < 0) {
+    if (b < a.nprod) {
+      gemv_produce<MT, C, GT>(a, b, smem);
+      return;
+    }
+    c = b - a.nprod;
+  } else if (b < lead) {
+    c = b;
+  } else if (b < lead + n8c) {
+    c = a.t4 * a.S + (b - lead);
+  } else if (b < lead + n8c + a.nprod) {
+    gemv_produce<MT, C, GT>(a, b - lead - n8c, smem);
     return;
+  } else {
+    c = b - n8c - a.nprod;
   }
-  const int c = b - a.nprod;   // consumer index = tile * S + range
   if (static_cast<int>(threadIdx.x >> 6) == a.W) gemv_spare<MT>(a, c, smem);
   else if (c < a.t4 * a.S) gemv_consume<MT, C, G, false, GT>(a, c, smem);
   else gemv_consume<MT, C, G, true, GT>(a, c, smem);

@@ -724,6 +724,7 @@ struct GemvArgs {
   uint64_t lut_units;  // rotation units of the range per compute wavefront, 4 bits each (in wavefront order)
   int t4, t8;          // 32-row tiles of each tier
   int nprod;           // producer workgroups (one per rotation unit)
+  int lead4;           // INT4 consumers placed before the INT8 consumers and the producers (< 0: producers first)
   int rotate, publish, spin_limit;
   int gated;           // 1: the input row m is h = geglu(x[m][0 .. K), x[m][K .. 2K)), formed as it loads
   float hscale;        // 1/sqrt(block)
