@@ -265,9 +265,11 @@ static int gemv_launch(const dvssq_layout &L, const WsLayout &W, const GemvPlan 
   g.nprod = g.nunit;
   {
     // with up to two blocks per compute unit, those beyond one per unit share
-    // units with the first ones: let those be INT4 consumers on both sides
+    // units with the first ones: let those be INT4 consumers on both sides;
+    // larger grids: the INT8 consumers and the producers first, so that none
+    // of them waits for a later round
     const int grid = g.nprod + (g.t4 + g.t8) * g.S, cus = compute_units();
-    g.lead4 = grid <= cus || grid > 2 * cus ? -1 : std::min(grid - cus, g.t4 * g.S);
+    g.lead4 = grid <= cus ? -1 : grid > 2 * cus ? 0 : std::min(grid - cus, g.t4 * g.S);
   }
   g.rotate = (flags & DVSSQ_X_ROTATED) ? 0 : 1;
   g.publish = (flags & DVSSQ_TEST_NO_PUBLISH) ? 0 : 1;

@@ -683,7 +683,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
   // (lead4 >= 0): INT4 consumers 0 .. lead4 - 1 (they share with INT4
   // consumers at the end), then the INT8 consumers (twice an INT4 tile's
   // bytes) and the producers, each on a unit of its own, then the other INT4
-  // consumers.  lead4 < 0: producers, INT4, INT8.
+  // consumers (lead4 = 0 for larger grids: INT8 and producers first).
+  // lead4 < 0 (a grid of one round): producers, INT4, INT8.
   const int b = blockIdx.x;
   const int n8c = a.t8 * a.S, lead = a.lead4;
   int c;   // consumer index = tile * S + range
