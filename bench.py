@@ -366,8 +366,8 @@ def quantize_table(dv, torch, layers, steps=3):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs the layer on a "
-              "single GPU; its multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the layer runs on a single GPU; "
+              "how it would shard over several is described in the design notes, not run.", file=sys.stderr)
         sys.exit(2)
     import torch
 
